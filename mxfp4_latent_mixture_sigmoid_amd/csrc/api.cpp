@@ -1,0 +1,496 @@
+// api.cpp -- the C ABI declared in include/mxmoe.h: validation, packed-buffer and workspace
+// layouts, and the launch sequence of moe_route / moe_forward on the caller's stream.
+#include "kernels.hpp"
+#include "mxmoe.h"
+
+#include <climits>
+#include <cstdlib>
+#include <new>
+#include <vector>
+
+using namespace mxmoe;
+
+struct moe_handle {
+    moe_config cfg;
+    int Hin;             // width of x and of the router's input
+    int E_pad;           // router rows padded to 16
+    uint8_t *packed;
+    int64_t off_router, off_xside, off_outside, off_gateup, off_down;
+    int64_t gateup_stride, down_stride;   // packed bytes per expert
+    // profiling hook state
+    bool prof = false;
+    int prof_max = 0;
+    std::vector<int> prof_kid;
+    std::vector<hipEvent_t> prof_ev;      // start/stop pairs
+};
+
+namespace {
+
+constexpr int64_t ALIGN = 256;
+constexpr int BM_GEMM1 = 16;   // rows per tile of the gate/up product
+constexpr int BM_GEMM2 = 16;   // rows per tile of the down product
+
+int64_t align_up(int64_t v) { return (v + ALIGN - 1) / ALIGN * ALIGN; }
+
+bool valid_config(const moe_config *c)
+{
+    if (!c)
+        return false;
+    if (c->act != MOE_ACT_SILU_GLU || (c->has_latent_proj != 0 && c->has_latent_proj != 1))
+        return false;
+    if (c->latent <= 0 || c->latent % 128 || c->inter <= 0 || c->inter % 128)
+        return false;
+    if (c->n_experts < 1 || c->n_experts > 1024 || c->top_k < 1 || c->top_k > 32 || c->top_k > c->n_experts)
+        return false;
+    if (c->n_shared < 0 || c->n_shared > 8)
+        return false;
+    if (c->has_latent_proj) {
+        if (c->hidden <= 0 || c->hidden % 128)
+            return false;
+        if (c->n_shared > 0 && (c->shared_inter <= 0 || c->shared_inter % 32))
+            return false;
+    } else if (c->n_shared != 0) {
+        return false;
+    }
+    // keep every index below 2^31 at T = 0 (sizes are re-checked per call with T)
+    const int64_t gateup = (int64_t)c->n_experts * mx_packed_bytes(2 * (int64_t)c->inter, c->latent);
+    return gateup > 0;
+}
+
+struct PackedLayout {
+    int64_t router, xside, outside, gateup, down, total, gateup_stride, down_stride;
+};
+
+PackedLayout packed_layout(const moe_config *c)
+{
+    PackedLayout L{};
+    const int64_t Hin = c->has_latent_proj ? c->hidden : c->latent;
+    const int64_t E_pad = (c->n_experts + 15) / 16 * 16;
+    const int64_t Lt = c->latent, H = c->hidden, S = c->n_shared, Is = c->shared_inter, I = c->inter;
+    int64_t off = 0;
+    L.router = off;
+    off = align_up(off + bf16_packed_bytes(E_pad, Hin));
+    L.xside = off;
+    if (c->has_latent_proj)
+        off = align_up(off + bf16_packed_bytes(Lt + 2 * S * Is, H));
+    L.outside = off;
+    if (c->has_latent_proj)
+        off = align_up(off + bf16_packed_bytes(H, Lt + S * Is));
+    L.gateup_stride = mx_packed_bytes(2 * I, Lt);
+    L.down_stride = mx_packed_bytes(Lt, I);
+    L.gateup = off;
+    off = align_up(off + c->n_experts * L.gateup_stride);
+    L.down = off;
+    off = align_up(off + c->n_experts * L.down_stride);
+    L.total = off;
+    return L;
+}
+
+struct WsLayout {
+    int64_t logits, hist, tiles1, tiles2, z, acat, h, y, total;
+    int64_t max_tiles1, max_tiles2;
+};
+
+int64_t max_tiles(int64_t T, int64_t K, int64_t E, int bm)
+{
+    const int64_t P = T * K;
+    return (P + bm - 1) / bm + (P < E ? P : E);
+}
+
+WsLayout ws_layout(const moe_config *c, int64_t T)
+{
+    WsLayout L{};
+    const int64_t E = c->n_experts, K = c->top_k, Lt = c->latent, I = c->inter;
+    const int64_t S = c->n_shared, Is = c->shared_inter;
+    const int64_t nb = (T + PERM_TOKENS_PER_BLOCK - 1) / PERM_TOKENS_PER_BLOCK;
+    L.max_tiles1 = max_tiles(T, K, E, BM_GEMM1);
+    L.max_tiles2 = max_tiles(T, K, E, BM_GEMM2);
+    int64_t off = 0;
+    L.logits = off;
+    off = align_up(off + T * E * 4);
+    L.hist = off;
+    off = align_up(off + E * nb * 4);
+    L.tiles1 = off;
+    off = align_up(off + (TILE_HEADER_INTS + 4 * L.max_tiles1) * 4);
+    L.tiles2 = off;
+    off = align_up(off + (TILE_HEADER_INTS + 4 * L.max_tiles2) * 4);
+    L.z = off;
+    if (c->has_latent_proj)
+        off = align_up(off + T * Lt * 2);
+    L.acat = off;
+    if (c->has_latent_proj)
+        off = align_up(off + T * (Lt + S * Is) * 2);
+    L.h = off;
+    off = align_up(off + T * K * I * 2);
+    L.y = off;
+    off = align_up(off + T * K * Lt * 2);
+    L.total = off;
+    return L;
+}
+
+// Largest element index any kernel forms from a 32-bit product must stay below 2^31.
+bool sizes_fit_int32(const moe_config *c, int64_t T)
+{
+    const int64_t P = T * c->top_k;
+    return P < INT_MAX && T * c->n_experts < INT_MAX;
+}
+
+bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+void prof_mark(moe_handle *h, int kid, hipStream_t st, bool start)
+{
+    if (!h->prof)
+        return;
+    if (start) {
+        if ((int)h->prof_kid.size() >= h->prof_max)
+            return;
+        hipEvent_t a = nullptr, b = nullptr;
+        if (hipEventCreate(&a) != hipSuccess)
+            return;
+        if (hipEventCreate(&b) != hipSuccess) {
+            (void)hipEventDestroy(a);
+            return;
+        }
+        h->prof_kid.push_back(kid);
+        h->prof_ev.push_back(a);
+        h->prof_ev.push_back(b);
+        (void)hipEventRecord(a, st);
+    } else if (!h->prof_kid.empty() && h->prof_kid.back() == kid && h->prof_ev.size() == 2 * h->prof_kid.size()) {
+        (void)hipEventRecord(h->prof_ev.back(), st);
+    }
+}
+
+// Launch `expr` (one or more kernels on `st`), bracketed by profiling events when enabled.
+#define MOE_LAUNCH(kid, expr)                                                                                 \
+    do {                                                                                                      \
+        prof_mark(h, (kid), st, true);                                                                        \
+        hipError_t _e = (expr);                                                                               \
+        prof_mark(h, (kid), st, false);                                                                       \
+        if (_e != hipSuccess)                                                                                 \
+            return MOE_ERR_HIP;                                                                               \
+    } while (0)
+
+
+} // namespace
+
+extern "C" {
+
+const char *moe_strerror(moe_status s)
+{
+    switch (s) {
+    case MOE_OK:
+        return "success";
+    case MOE_ERR_INVALID_ARG:
+        return "invalid argument (config, shape, pointer or size)";
+    case MOE_ERR_UNSUPPORTED:
+        return "unsupported request";
+    case MOE_ERR_BUFFER_TOO_SMALL:
+        return "packed buffer or workspace too small";
+    case MOE_ERR_HIP:
+        return "HIP launch or runtime error";
+    }
+    return "unknown status";
+}
+
+moe_status moe_query(const moe_config *cfg, int32_t T_max, size_t *packed_bytes, size_t *workspace_bytes)
+{
+    if (!valid_config(cfg) || T_max < 0 || !sizes_fit_int32(cfg, T_max))
+        return MOE_ERR_INVALID_ARG;
+    if (packed_bytes)
+        *packed_bytes = (size_t)packed_layout(cfg).total;
+    if (workspace_bytes)
+        *workspace_bytes = (size_t)ws_layout(cfg, T_max).total;
+    return MOE_OK;
+}
+
+moe_status moe_query_workspace_layout(const moe_config *cfg, int32_t T, size_t *offsets)
+{
+    if (!valid_config(cfg) || T < 0 || !sizes_fit_int32(cfg, T) || !offsets)
+        return MOE_ERR_INVALID_ARG;
+    const WsLayout W = ws_layout(cfg, T);
+    const int64_t v[9] = {W.logits, W.hist, W.tiles1, W.tiles2, W.z, W.acat, W.h, W.y, W.total};
+    for (int i = 0; i < 9; i++)
+        offsets[i] = (size_t)v[i];
+    return MOE_OK;
+}
+
+moe_status moe_create(const moe_config *cfg, const moe_weights *w, void *packed, size_t packed_bytes, void *stream,
+                      moe_handle **out)
+{
+    if (!out)
+        return MOE_ERR_INVALID_ARG;
+    *out = nullptr;
+    if (!valid_config(cfg) || !w || !packed || !aligned(packed, ALIGN))
+        return MOE_ERR_INVALID_ARG;
+    const bool lat = cfg->has_latent_proj != 0, sh = lat && cfg->n_shared > 0;
+    const void *need[] = {w->w_router, w->gate_codes, w->gate_scales, w->up_codes, w->up_scales, w->down_codes,
+                          w->down_scales};
+    for (const void *p : need)
+        if (!p)
+            return MOE_ERR_INVALID_ARG;
+    if (!aligned(w->w_router, 16) || !aligned(w->gate_codes, 4) || !aligned(w->up_codes, 4) ||
+        !aligned(w->down_codes, 4))
+        return MOE_ERR_INVALID_ARG;
+    if (lat && (!w->w_down || !w->w_up || !aligned(w->w_down, 16) || !aligned(w->w_up, 16)))
+        return MOE_ERR_INVALID_ARG;
+    if (sh && (!w->sh_gate || !w->sh_up || !w->sh_down || !aligned(w->sh_gate, 16) || !aligned(w->sh_up, 16) ||
+               !aligned(w->sh_down, 16)))
+        return MOE_ERR_INVALID_ARG;
+    const PackedLayout L = packed_layout(cfg);
+    if (packed_bytes < (size_t)L.total)
+        return MOE_ERR_BUFFER_TOO_SMALL;
+
+    moe_handle *h = new (std::nothrow) moe_handle;
+    if (!h)
+        return MOE_ERR_UNSUPPORTED;
+    h->cfg = *cfg;
+    h->Hin = lat ? cfg->hidden : cfg->latent;
+    h->E_pad = (cfg->n_experts + 15) / 16 * 16;
+    h->packed = static_cast<uint8_t *>(packed);
+    h->off_router = L.router;
+    h->off_xside = L.xside;
+    h->off_outside = L.outside;
+    h->off_gateup = L.gateup;
+    h->off_down = L.down;
+    h->gateup_stride = L.gateup_stride;
+    h->down_stride = L.down_stride;
+
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int64_t E = cfg->n_experts, Lt = cfg->latent, H = cfg->hidden, I = cfg->inter;
+    const int64_t S = sh ? cfg->n_shared : 0, Is = sh ? cfg->shared_inter : 0;
+    hipError_t e = launch_pack_router(h->packed + L.router, static_cast<const uint16_t *>(w->w_router), E, h->E_pad,
+                                      h->Hin, st);
+    if (e == hipSuccess && lat)
+        e = launch_pack_xside(h->packed + L.xside, static_cast<const uint16_t *>(w->w_down),
+                              static_cast<const uint16_t *>(w->sh_gate), static_cast<const uint16_t *>(w->sh_up), Lt,
+                              H, S, Is, st);
+    if (e == hipSuccess && lat)
+        e = launch_pack_outside(h->packed + L.outside, static_cast<const uint16_t *>(w->w_up),
+                                static_cast<const uint16_t *>(w->sh_down), Lt, H, S, Is, st);
+    if (e == hipSuccess)
+        e = launch_pack_gateup(h->packed + L.gateup, static_cast<const uint8_t *>(w->gate_codes),
+                               static_cast<const uint8_t *>(w->gate_scales), static_cast<const uint8_t *>(w->up_codes),
+                               static_cast<const uint8_t *>(w->up_scales), E, I, Lt, st);
+    if (e == hipSuccess)
+        e = launch_pack_down(h->packed + L.down, static_cast<const uint8_t *>(w->down_codes),
+                             static_cast<const uint8_t *>(w->down_scales), E, I, Lt, st);
+    if (e != hipSuccess) {
+        delete h;
+        return MOE_ERR_HIP;
+    }
+    *out = h;
+    return MOE_OK;
+}
+
+static void prof_clear(moe_handle *h)
+{
+    for (hipEvent_t e : h->prof_ev)
+        (void)hipEventDestroy(e);
+    h->prof_ev.clear();
+    h->prof_kid.clear();
+    h->prof = false;
+}
+
+moe_status moe_profile_begin(moe_handle *h, int32_t max_launches)
+{
+    if (!h || max_launches <= 0)
+        return MOE_ERR_INVALID_ARG;
+    prof_clear(h);
+    h->prof = true;
+    h->prof_max = max_launches;
+    try {
+        h->prof_kid.reserve(max_launches);
+        h->prof_ev.reserve(2 * (size_t)max_launches);
+    } catch (...) {
+        h->prof = false;
+        return MOE_ERR_UNSUPPORTED;
+    }
+    return MOE_OK;
+}
+
+moe_status moe_profile_end(moe_handle *h, int32_t *kernel_ids, float *ms, int32_t *n)
+{
+    if (!h || !n || *n < 0 || (*n > 0 && (!kernel_ids || !ms)))
+        return MOE_ERR_INVALID_ARG;
+    moe_status st = MOE_OK;
+    const int cap = *n;
+    int w = 0;
+    for (size_t i = 0; i < h->prof_kid.size() && w < cap; i++) {
+        float t = 0.f;
+        if (hipEventSynchronize(h->prof_ev[2 * i + 1]) != hipSuccess ||
+            hipEventElapsedTime(&t, h->prof_ev[2 * i], h->prof_ev[2 * i + 1]) != hipSuccess) {
+            st = MOE_ERR_HIP;
+            break;
+        }
+        kernel_ids[w] = h->prof_kid[i];
+        ms[w] = t;
+        w++;
+    }
+    *n = w;
+    prof_clear(h);
+    return st;
+}
+
+void moe_destroy(moe_handle *h)
+{
+    if (!h)
+        return;
+    prof_clear(h);
+    delete h;
+}
+
+moe_status moe_route(moe_handle *h, const void *x, int32_t T, const float *logit_bias, const float *logits_in,
+                     float *logits_out, const moe_routing *r, void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (!h || T < 0 || !r)
+        return MOE_ERR_INVALID_ARG;
+    const moe_config *c = &h->cfg;
+    if (!sizes_fit_int32(c, T))
+        return MOE_ERR_INVALID_ARG;
+    if (T == 0)
+        return MOE_OK;
+    if (logits_in ? (x || logit_bias || logits_out) : !x)
+        return MOE_ERR_INVALID_ARG;
+    if (!r->topk_ids || !r->topk_w || !r->counts || !r->offsets || !r->sorted_pairs || !r->inv)
+        return MOE_ERR_INVALID_ARG;
+    if (x && !aligned(x, 16))
+        return MOE_ERR_INVALID_ARG;
+    const WsLayout W = ws_layout(c, T);
+    if (!workspace || !aligned(workspace, ALIGN))
+        return MOE_ERR_INVALID_ARG;
+    if (workspace_bytes < (size_t)W.total)
+        return MOE_ERR_BUFFER_TOO_SMALL;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    uint8_t *ws = static_cast<uint8_t *>(workspace);
+    const int E = c->n_experts, K = c->top_k;
+
+    const float *logits = logits_in;
+    if (!logits_in) {
+        float *lg = logits_out ? logits_out : reinterpret_cast<float *>(ws + W.logits);
+        GemmArgs g{};
+        g.A = static_cast<const uint16_t *>(x);
+        g.lda = h->Hin;
+        g.B = h->packed + h->off_router;
+        g.M = T;
+        g.N = h->E_pad;
+        g.K = h->Hin;
+        g.split = INT_MAX;
+        g.lo = OutDesc{OUT_F32, lg, E, 0, E, logit_bias};
+        MOE_LAUNCH(MOE_KERNEL_ROUTER, launch_gemm_dense(g, GEMM_SKINNY_N16, st));
+        logits = lg;
+    }
+    MOE_LAUNCH(MOE_KERNEL_TOPK, launch_topk(logits, T, E, K, r->topk_ids, r->topk_w, st));
+    MOE_LAUNCH(MOE_KERNEL_PERMUTE, launch_permute(r->topk_ids, T, K, E, reinterpret_cast<int32_t *>(ws + W.hist), r->counts, r->offsets,
+                           r->sorted_pairs, r->inv, st));
+    return MOE_OK;
+}
+
+moe_status moe_forward(moe_handle *h, const void *x, int32_t T, const moe_routing *r, void *out, void *workspace,
+                       size_t workspace_bytes, void *stream)
+{
+    if (!h || T < 0 || !r)
+        return MOE_ERR_INVALID_ARG;
+    const moe_config *c = &h->cfg;
+    if (!sizes_fit_int32(c, T))
+        return MOE_ERR_INVALID_ARG;
+    if (T == 0)
+        return MOE_OK;
+    if (!x || !out || !aligned(x, 16) || !aligned(out, 16) || x == out)
+        return MOE_ERR_INVALID_ARG;
+    if (!r->topk_w || !r->offsets || !r->sorted_pairs || !r->inv)
+        return MOE_ERR_INVALID_ARG;
+    const WsLayout W = ws_layout(c, T);
+    if (!workspace || !aligned(workspace, ALIGN))
+        return MOE_ERR_INVALID_ARG;
+    if (workspace_bytes < (size_t)W.total)
+        return MOE_ERR_BUFFER_TOO_SMALL;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    uint8_t *ws = static_cast<uint8_t *>(workspace);
+    const bool lat = c->has_latent_proj != 0;
+    const int E = c->n_experts, K = c->top_k, Lt = c->latent, I = c->inter, H = c->hidden;
+    const int S = lat ? c->n_shared : 0, Is = S ? c->shared_inter : 0;
+    const int ldcat = Lt + S * Is;
+    uint16_t *Z = reinterpret_cast<uint16_t *>(ws + W.z);
+    uint16_t *Acat = reinterpret_cast<uint16_t *>(ws + W.acat);
+    uint16_t *Hb = reinterpret_cast<uint16_t *>(ws + W.h);
+    uint16_t *Yb = reinterpret_cast<uint16_t *>(ws + W.y);
+    int32_t *tiles1 = reinterpret_cast<int32_t *>(ws + W.tiles1);
+    int32_t *tiles2 = reinterpret_cast<int32_t *>(ws + W.tiles2);
+
+    if (lat) {   // z = bf16(x W_down^T) and h_s = bf16(silu(x Wg_s^T) (x Wu_s^T)) in one pass over x
+        GemmArgs g{};
+        g.A = static_cast<const uint16_t *>(x);
+        g.lda = H;
+        g.B = h->packed + h->off_xside;
+        g.M = T;
+        g.N = Lt + 2 * S * Is;
+        g.K = H;
+        g.split = Lt;
+        g.lo = OutDesc{OUT_BF16, Z, Lt, 0, Lt, nullptr};
+        g.hi = OutDesc{OUT_GLU, Acat + Lt, ldcat, Lt, INT_MAX, nullptr};
+        MOE_LAUNCH(MOE_KERNEL_XSIDE, launch_gemm_dense(g, GEMM_SKINNY_N32, st));
+    }
+    MOE_LAUNCH(MOE_KERNEL_TILEMAP, launch_tilemap(r->offsets, E, BM_GEMM1, tiles1, BM_GEMM2, tiles2, st));
+    {   // h = bf16(silu(z Wg_e^T) (z Wu_e^T)) for every pair, rows in expert-sorted order
+        GemmArgs g{};
+        g.A = lat ? Z : static_cast<const uint16_t *>(x);
+        g.lda = Lt;
+        g.a_index = r->sorted_pairs;
+        g.a_div = K;
+        g.B = h->packed + h->off_gateup;
+        g.b_stride = h->gateup_stride;
+        g.N = 2 * I;
+        g.K = Lt;
+        g.tiles = tiles1;
+        g.split = INT_MAX;
+        g.lo = OutDesc{OUT_GLU, Hb, I, 0, INT_MAX, nullptr};
+        MOE_LAUNCH(MOE_KERNEL_GATEUP, launch_gemm_grouped(g, GEMM_MX_GLU_M16, (int)W.max_tiles1, st));
+    }
+    {   // y = bf16(h Wd_e^T), unweighted, expert-sorted rows
+        GemmArgs g{};
+        g.A = Hb;
+        g.lda = I;
+        g.B = h->packed + h->off_down;
+        g.b_stride = h->down_stride;
+        g.N = Lt;
+        g.K = I;
+        g.tiles = tiles2;
+        g.split = INT_MAX;
+        g.lo = OutDesc{OUT_BF16, Yb, Lt, 0, Lt, nullptr};
+        MOE_LAUNCH(MOE_KERNEL_DOWN, launch_gemm_grouped(g, GEMM_MX_M16_N64, (int)W.max_tiles2, st));
+    }
+    // zc = bf16(sum_j w_j y_j) in slot order: into the first Lt columns of [zc | h_s], or the output
+    MOE_LAUNCH(MOE_KERNEL_COMBINE, launch_combine(Yb, Lt, r->inv, r->topk_w, T, K, lat ? Acat : static_cast<uint16_t *>(out),
+                           lat ? ldcat : Lt, st));
+    if (lat) {   // out = bf16([zc | h_s] [W_up | Wd_s]^T)
+        GemmArgs g{};
+        g.A = Acat;
+        g.lda = ldcat;
+        g.B = h->packed + h->off_outside;
+        g.M = T;
+        g.N = H;
+        g.K = ldcat;
+        g.split = INT_MAX;
+        g.lo = OutDesc{OUT_BF16, out, H, 0, H, nullptr};
+        MOE_LAUNCH(MOE_KERNEL_OUT, launch_gemm_dense(g, GEMM_SKINNY_N16, st));
+    }
+    return MOE_OK;
+}
+
+moe_status moe_unpack_expert(moe_handle *h, int32_t e, int32_t which, void *out, void *stream)
+{
+    if (!h || !out || e < 0 || e >= h->cfg.n_experts || which < 0 || which > 2 || !aligned(out, 16))
+        return MOE_ERR_INVALID_ARG;
+    const moe_config *c = &h->cfg;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    uint16_t *o = static_cast<uint16_t *>(out);
+    if (which < 2)
+        return hip_status(launch_unpack_mx(h->packed + h->off_gateup + e * h->gateup_stride, 2 * (int64_t)c->inter,
+                                           c->latent, 1, which, o, st));
+    return hip_status(
+        launch_unpack_mx(h->packed + h->off_down + e * h->down_stride, c->latent, c->inter, 0, 0, o, st));
+}
+
+} // extern "C"

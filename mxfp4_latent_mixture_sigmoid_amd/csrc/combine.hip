@@ -1,0 +1,110 @@
+// combine.hip -- the tile list of the grouped expert GEMMs and the fixed-order gate-weighted
+// combine of the expert outputs.
+#include "kernels.hpp"
+
+namespace mxmoe {
+
+// One workgroup (blockDim = 1024 >= E). Expert e with n_e rows gets ceil(n_e / bm) tiles of at
+// most bm consecutive rows of the expert-sorted order; tiles are listed expert by expert.
+// Layout: tiles[0] = tile count, then from element 4 one int4 (expert, row begin, row end, 0).
+__device__ void write_tiles(const int32_t *offsets, int E, int bm, int32_t *tiles, int *sh)
+{
+    const int e = threadIdx.x;
+    const int beg = e < E ? offsets[e] : 0;
+    const int n = e < E ? offsets[e + 1] - beg : 0;
+    const int c = (n + bm - 1) / bm;
+    int total;
+    const int base = [&] {
+        // exclusive scan of c over the workgroup
+        const int lane = threadIdx.x & (WAVE - 1), wid = threadIdx.x / WAVE;
+        const int nw = (blockDim.x + WAVE - 1) / WAVE;
+        int inc = c;
+#pragma unroll
+        for (int o = 1; o < WAVE; o <<= 1) {
+            const int t = __shfl_up(inc, o);
+            if (lane >= o)
+                inc += t;
+        }
+        if (lane == WAVE - 1)
+            sh[wid] = inc;
+        __syncthreads();
+        if (wid == 0) {
+            int x = lane < nw ? sh[lane] : 0;
+#pragma unroll
+            for (int o = 1; o < WAVE; o <<= 1) {
+                const int t = __shfl_up(x, o);
+                if (lane >= o)
+                    x += t;
+            }
+            if (lane < nw)
+                sh[lane] = x;
+        }
+        __syncthreads();
+        const int b = wid ? sh[wid - 1] : 0;
+        total = sh[nw - 1];
+        __syncthreads();
+        return b + inc - c;
+    }();
+    int4 *out = reinterpret_cast<int4 *>(tiles + TILE_HEADER_INTS);
+    for (int j = 0; j < c; j++)
+        out[base + j] = int4{e, beg + j * bm, min(beg + (j + 1) * bm, beg + n), 0};
+    if (threadIdx.x == 0)
+        tiles[0] = total;
+}
+
+__global__ __launch_bounds__(1024) void tilemap_kernel(const int32_t *__restrict__ offsets, int E, int bm1,
+                                                       int32_t *__restrict__ tiles1, int bm2,
+                                                       int32_t *__restrict__ tiles2)
+{
+    __shared__ int sh[16];
+    write_tiles(offsets, E, bm1, tiles1, sh);
+    if (bm2 > 0)
+        write_tiles(offsets, E, bm2, tiles2, sh);
+}
+
+hipError_t launch_tilemap(const int32_t *offsets, int E, int bm1, int32_t *tiles1, int bm2, int32_t *tiles2,
+                          hipStream_t st)
+{
+    if (E > 1024)
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL(tilemap_kernel, dim3(1), dim3(1024), 0, st, offsets, E, bm1, tiles1, bm2, tiles2);
+    return hipGetLastError();
+}
+
+// zc[t, c] = bf16(sum over slots j = 0..K-1, in order, of w[t, j] * Y[inv[t K + j], c]).
+// Each thread owns 8 consecutive columns of one token (16-byte loads and store); FP32 sums.
+__global__ __launch_bounds__(64) void combine_kernel(const uint16_t *__restrict__ Y, int Lt,
+                                                     const int32_t *__restrict__ inv, const float *__restrict__ w,
+                                                     int K, uint16_t *__restrict__ out, int64_t ldo)
+{
+    const int t = blockIdx.x;
+    const int c8 = blockIdx.y * 64 + threadIdx.x;
+    if (c8 * 8 >= Lt)
+        return;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < K; j++) {
+        const int64_t r = inv[(int64_t)t * K + j];
+        const float wj = w[(int64_t)t * K + j];
+        const u32x4_t y = load16(Y + r * Lt + c8 * 8);
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            acc[2 * i] += wj * bf16_bits_to_f32(y[i] & 0xFFFFu);
+            acc[2 * i + 1] += wj * bf16_bits_to_f32(y[i] >> 16);
+        }
+    }
+    u32x4_t o;
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+        o[i] = pack_bf16x2(acc[2 * i], acc[2 * i + 1]);
+    *reinterpret_cast<u32x4_t *>(out + (int64_t)t * ldo + c8 * 8) = o;
+}
+
+hipError_t launch_combine(const uint16_t *Y, int Lt, const int32_t *inv, const float *w, int T, int K,
+                          uint16_t *out, int64_t ldo, hipStream_t st)
+{
+    const dim3 grid(T, (Lt / 8 + 63) / 64);
+    hipLaunchKernelGGL(combine_kernel, grid, dim3(64), 0, st, Y, Lt, inv, w, K, out, ldo);
+    return hipGetLastError();
+}
+
+} // namespace mxmoe

@@ -1,0 +1,106 @@
+// common.hpp -- device types, packed-layout constants and small helpers shared by the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+namespace mxmoe {
+
+constexpr int WAVE = 64;
+
+// ---------------------------------------------------------------------------------------------
+// Packed weight layouts.
+//
+// Every packed matrix B [N, K] (N output rows, K the reduction axis) is cut into blocks of 16 rows;
+// within a row block the K axis is cut into steps. A block is laid out so that lane l of a wave
+// reads bytes [16 l, 16 l + 16) and receives exactly its operand of the 16x16x32 BF16 matrix-core
+// instruction: row (l % 16), inputs 8 (l / 16) .. 8 (l / 16) + 7 of each 32-wide input slice.
+// Blocks are stored row-block major: block (nb, kb) at index nb * (K / step) + kb.
+//
+//  BF16 blocks: 16 rows x 32 inputs, 1024 bytes; lane l holds row l%16, inputs 8(l/16)..+7.
+//  MX blocks:   16 rows x 128 inputs = four 32-input slices, 1024 code bytes + 64 scale bytes.
+//               Lane l's 16 code bytes are four 4-byte words; word j holds the 8 E2M1 codes of
+//               row l%16, inputs 32 j + 8 (l/16) .. +7 (low nibble first). Scale byte
+//               1024 + 4 n + j is the E8M0 scale of row n for slice j, so lane l reads one
+//               dword at 1024 + 4 (l % 16).
+// ---------------------------------------------------------------------------------------------
+constexpr int BF16_BLOCK_BYTES = 1024;
+constexpr int BF16_STEP = 32;
+constexpr int MX_CODE_BYTES = 1024;
+constexpr int MX_BLOCK_BYTES = 1088;
+constexpr int MX_STEP = 128;
+
+__host__ __device__ inline int64_t bf16_packed_bytes(int64_t N, int64_t K) { return N * K * 2; }
+__host__ __device__ inline int64_t mx_packed_bytes(int64_t N, int64_t K)
+{
+    return (N / 16) * (K / MX_STEP) * MX_BLOCK_BYTES;
+}
+
+// ---------------------------------------------------------------------------------------------
+// Number formats.
+// ---------------------------------------------------------------------------------------------
+__device__ inline float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// float -> BF16 bits, round to nearest even (NaN kept quiet).
+__device__ inline uint32_t f32_to_bf16_bits(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u)
+        return ((u >> 16) | 0x40u) & 0xFFFFu;
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+__device__ inline uint32_t pack_bf16x2(float lo, float hi)
+{
+    return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+// E8M0 byte -> the float 2^(e-127) used as the conversion scale (255 -> NaN).
+__device__ inline float e8m0_to_f32(uint32_t e)
+{
+    uint32_t bits = (e == 0u) ? 0x00400000u : (e == 255u ? 0x7FC00000u : (e << 23));
+    return __uint_as_float(bits);
+}
+
+// Eight E2M1 codes (one dword, element 2i in the low nibble of byte i) times one E8M0 scale,
+// converted to eight BF16 values with gfx950's scaled FP4 -> BF16 conversion (two values per
+// instruction, the byte chosen by the instruction's selector).
+__device__ inline bf16x8_t mx_dequant8(uint32_t codes, float scale)
+{
+    union {
+        bf16x2_t h[4];
+        bf16x8_t v;
+    } r;
+    r.h[0] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 0);
+    r.h[1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 1);
+    r.h[2] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 2);
+    r.h[3] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 3);
+    return r.v;
+}
+
+__device__ inline bf16x8_t as_bf16x8(u32x4_t v)
+{
+    union {
+        u32x4_t u;
+        bf16x8_t b;
+    } r;
+    r.u = v;
+    return r.b;
+}
+
+__device__ inline f32x4_t mfma16(bf16x8_t a, bf16x8_t b, f32x4_t c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ inline float silu_f32(float g) { return g / (1.0f + expf(-g)); }
+
+__device__ inline u32x4_t load16(const void *p) { return *reinterpret_cast<const u32x4_t *>(p); }
+
+} // namespace mxmoe

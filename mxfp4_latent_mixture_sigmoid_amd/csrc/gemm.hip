@@ -1,0 +1,204 @@
+// gemm.hip -- BF16 matrix-core GEMMs C = A . B^T for the layer's dense and grouped products.
+//
+// A is a row-major BF16 activation matrix, optionally gathered row by row; B is a packed weight
+// matrix (BF16 or MXFP4, see common.hpp) streamed from HBM in fragment order so that every
+// 16-byte lane load is exactly one matrix-core operand and a wave's load covers 1 KiB of
+// contiguous memory. MXFP4 codes are converted to BF16 in registers with their E8M0 scale
+// (gfx950's scaled FP4 conversion) right before the 16x16x32 BF16 instruction; accumulation is
+// FP32. The waves of a workgroup split the K axis; their partial tiles are summed in LDS in a
+// fixed order, so the result does not depend on timing. The epilogue writes FP32 logits (+bias),
+// BF16, or the GLU h = bf16(silu(gate) * up) from gate/up column pairs.
+#include "kernels.hpp"
+
+namespace mxmoe {
+
+template <int MT, int NT, int WK, bool MX>
+__global__ __launch_bounds__(WAVE *WK) void gemm_kernel(const GemmArgs g)
+{
+    constexpr int BM = 16 * MT, BN = 16 * NT;
+    constexpr int STEP = MX ? MX_STEP : BF16_STEP;
+    __shared__ float red[WK * BM * BN];
+
+    const int lane = threadIdx.x & (WAVE - 1);
+    const int wv = threadIdx.x / WAVE;
+
+    int group = 0, m0, m1;
+    if (g.tiles) {
+        if ((int)blockIdx.x >= g.tiles[0])
+            return;
+        const int4 t = reinterpret_cast<const int4 *>(g.tiles + 4)[blockIdx.x];
+        group = t.x;
+        m0 = t.y;
+        m1 = t.z;
+    } else {
+        m0 = blockIdx.x * BM;
+        m1 = min(g.M, m0 + BM);
+    }
+    const int n0 = blockIdx.y * BN;
+
+    // Activation rows of this lane for each 16-row fragment (gathered when a_index is set).
+    const uint16_t *arow[MT];
+    bool aval[MT];
+#pragma unroll
+    for (int mf = 0; mf < MT; mf++) {
+        const int r = m0 + mf * 16 + (lane & 15);
+        aval[mf] = r < m1;
+        int64_t row = 0;
+        if (aval[mf])
+            row = g.a_index ? (int64_t)(g.a_index[r] / g.a_div) : (int64_t)r;
+        arow[mf] = g.A + row * g.lda + 8 * (lane >> 4);
+    }
+
+    const int nsteps = g.K / STEP;
+    const int s0 = (wv * nsteps) / WK, s1 = ((wv + 1) * nsteps) / WK;
+    const uint8_t *Bg = g.B + (int64_t)group * g.b_stride;
+
+    f32x4_t acc[MT][NT];
+#pragma unroll
+    for (int mf = 0; mf < MT; mf++)
+#pragma unroll
+        for (int nf = 0; nf < NT; nf++)
+            acc[mf][nf] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    const u32x4_t zero4 = {0u, 0u, 0u, 0u};
+    if constexpr (MX) {
+#pragma unroll 2
+        for (int s = s0; s < s1; s++) {
+            u32x4_t codes[NT];
+            uint32_t sc[NT];
+#pragma unroll
+            for (int nf = 0; nf < NT; nf++) {
+                const uint8_t *blk = Bg + ((int64_t)(n0 / 16 + nf) * nsteps + s) * MX_BLOCK_BYTES;
+                codes[nf] = load16(blk + lane * 16);
+                sc[nf] = *reinterpret_cast<const uint32_t *>(blk + MX_CODE_BYTES + 4 * (lane & 15));
+            }
+            u32x4_t a[MT][4];
+#pragma unroll
+            for (int mf = 0; mf < MT; mf++)
+#pragma unroll
+                for (int j = 0; j < 4; j++)
+                    a[mf][j] = aval[mf] ? load16(arow[mf] + s * STEP + 32 * j) : zero4;
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                bf16x8_t b[NT];
+#pragma unroll
+                for (int nf = 0; nf < NT; nf++)
+                    b[nf] = mx_dequant8(codes[nf][j], e8m0_to_f32((sc[nf] >> (8 * j)) & 0xFFu));
+#pragma unroll
+                for (int mf = 0; mf < MT; mf++)
+#pragma unroll
+                    for (int nf = 0; nf < NT; nf++)
+                        acc[mf][nf] = mfma16(as_bf16x8(a[mf][j]), b[nf], acc[mf][nf]);
+            }
+        }
+    } else {
+#pragma unroll 4
+        for (int s = s0; s < s1; s++) {
+            u32x4_t b[NT];
+#pragma unroll
+            for (int nf = 0; nf < NT; nf++)
+                b[nf] = load16(Bg + ((int64_t)(n0 / 16 + nf) * nsteps + s) * BF16_BLOCK_BYTES + lane * 16);
+#pragma unroll
+            for (int mf = 0; mf < MT; mf++) {
+                const u32x4_t a = aval[mf] ? load16(arow[mf] + s * STEP) : zero4;
+#pragma unroll
+                for (int nf = 0; nf < NT; nf++)
+                    acc[mf][nf] = mfma16(as_bf16x8(a), as_bf16x8(b[nf]), acc[mf][nf]);
+            }
+        }
+    }
+
+    // Partial tiles to LDS: lane l holds rows 4 (l/16) + i, column l % 16 of each fragment.
+#pragma unroll
+    for (int mf = 0; mf < MT; mf++)
+#pragma unroll
+        for (int nf = 0; nf < NT; nf++)
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const int row = mf * 16 + 4 * (lane >> 4) + i, col = nf * 16 + (lane & 15);
+                red[(wv * BM + row) * BN + col] = acc[mf][nf][i];
+            }
+    __syncthreads();
+
+    const OutDesc d = (n0 < g.split) ? g.lo : g.hi;
+    const int nthr = WAVE * WK;
+    if (d.kind == OUT_GLU) {
+        // Column pairs: within each 32 columns, 16 gate columns then the 16 matching up columns.
+        constexpr int BO = BN / 2;
+        for (int idx = threadIdx.x; idx < BM * BO; idx += nthr) {
+            const int row = idx / BO, oc = idx % BO;
+            const int r = m0 + row;
+            if (r >= m1)
+                continue;
+            const int gc = (oc / 16) * 32 + (oc % 16), uc = gc + 16;
+            float gs = 0.f, us = 0.f;
+#pragma unroll
+            for (int w = 0; w < WK; w++) {
+                gs += red[(w * BM + row) * BN + gc];
+                us += red[(w * BM + row) * BN + uc];
+            }
+            const float h = silu_f32(gs) * us;
+            uint16_t *o = reinterpret_cast<uint16_t *>(d.ptr);
+            o[(int64_t)r * d.ld + (n0 - d.col0) / 2 + oc] = (uint16_t)f32_to_bf16_bits(h);
+        }
+    } else {
+        for (int idx = threadIdx.x; idx < BM * BN; idx += nthr) {
+            const int row = idx / BN, col = idx % BN;
+            const int r = m0 + row, n = n0 + col;
+            if (r >= m1 || n >= d.n_valid)
+                continue;
+            float v = 0.f;
+#pragma unroll
+            for (int w = 0; w < WK; w++)
+                v += red[(w * BM + row) * BN + col];
+            if (d.kind == OUT_F32) {
+                if (d.bias)
+                    v += d.bias[n];
+                reinterpret_cast<float *>(d.ptr)[(int64_t)r * d.ld + (n - d.col0)] = v;
+            } else {
+                reinterpret_cast<uint16_t *>(d.ptr)[(int64_t)r * d.ld + (n - d.col0)] =
+                    (uint16_t)f32_to_bf16_bits(v);
+            }
+        }
+    }
+}
+
+template <int MT, int NT, int WK, bool MX>
+static hipError_t launch(const GemmArgs &g, int grid_m, hipStream_t st)
+{
+    constexpr int BN = 16 * NT;
+    if (g.N % BN != 0 || g.K % (MX ? MX_STEP : BF16_STEP) != 0)
+        return hipErrorInvalidValue;
+    if (grid_m <= 0)
+        return hipSuccess;
+    hipLaunchKernelGGL((gemm_kernel<MT, NT, WK, MX>), dim3(grid_m, g.N / BN), dim3(WAVE * WK), 0, st, g);
+    return hipGetLastError();
+}
+
+// Dense products (row count M known on the host).
+hipError_t launch_gemm_dense(const GemmArgs &g, GemmShape shape, hipStream_t st)
+{
+    switch (shape) {
+    case GEMM_SKINNY_N16:
+        return launch<4, 1, 8, false>(g, (g.M + 63) / 64, st);
+    case GEMM_SKINNY_N32:
+        return launch<4, 2, 8, false>(g, (g.M + 63) / 64, st);
+    default:
+        return hipErrorInvalidValue;
+    }
+}
+
+// Grouped MXFP4 products over the tile list (upper bound `max_tiles` workgroup rows).
+hipError_t launch_gemm_grouped(const GemmArgs &g, GemmShape shape, int max_tiles, hipStream_t st)
+{
+    switch (shape) {
+    case GEMM_MX_GLU_M16:
+        return launch<1, 2, 4, true>(g, max_tiles, st);
+    case GEMM_MX_M16_N64:
+        return launch<1, 4, 1, true>(g, max_tiles, st);
+    default:
+        return hipErrorInvalidValue;
+    }
+}
+
+} // namespace mxmoe

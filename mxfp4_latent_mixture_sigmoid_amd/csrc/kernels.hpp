@@ -1,0 +1,71 @@
+// kernels.hpp -- launch interfaces of the device kernels (internal to the library).
+#pragma once
+
+#include "common.hpp"
+
+namespace mxmoe {
+
+enum OutKind { OUT_F32 = 0, OUT_BF16 = 1, OUT_GLU = 2 };
+
+// Where the GEMM epilogue writes columns [col0, ...) of the logical product.
+struct OutDesc {
+    int kind;            // OutKind
+    void *ptr;           // FP32 or BF16 row-major output
+    int64_t ld;          // output row stride in elements
+    int col0;            // first logical column this descriptor covers
+    int n_valid;         // logical columns >= n_valid are not written (FP32 / BF16)
+    const float *bias;   // FP32 only: added per logical column (nullable)
+};
+
+struct GemmArgs {
+    const uint16_t *A;       // BF16 activations, row-major
+    int64_t lda;             // row stride of A in elements
+    const int32_t *a_index;  // nullable: product row r reads A row a_index[r] / a_div
+    int a_div;
+    const uint8_t *B;        // packed weights (group 0)
+    int64_t b_stride;        // bytes between consecutive groups' packed weights
+    int M, N, K;             // M: dense row count (ignored with a tile list)
+    const int32_t *tiles;    // nullable: [0] = tile count, from element 4: int4 (group, m0, m1, -)
+    int split;               // logical columns < split use `lo`, the rest `hi`
+    OutDesc lo, hi;
+};
+
+enum GemmShape {
+    GEMM_SKINNY_N16 = 0,     // dense, 64 rows x 16 columns per workgroup, K split over 8 waves
+    GEMM_SKINNY_N32 = 1,     // dense, 64 rows x 32 columns (one GLU pair), K over 8 waves
+    GEMM_MX_GLU_M16 = 2,     // grouped MXFP4, 16 rows x (16 gate + 16 up), K over 4 waves
+    GEMM_MX_M16_N64 = 3,     // grouped MXFP4, 16 rows x 64 columns, one wave
+};
+
+constexpr int TILE_HEADER_INTS = 4;
+
+hipError_t launch_gemm_dense(const GemmArgs &g, GemmShape shape, hipStream_t st);
+hipError_t launch_gemm_grouped(const GemmArgs &g, GemmShape shape, int max_tiles, hipStream_t st);
+
+// Packing (moe_create) and unpacking (test hook).
+hipError_t launch_pack_router(uint8_t *dst, const uint16_t *w, int64_t E, int64_t E_pad, int64_t Hin,
+                              hipStream_t st);
+hipError_t launch_pack_xside(uint8_t *dst, const uint16_t *wdn, const uint16_t *sg, const uint16_t *su,
+                             int64_t Lt, int64_t H, int64_t S, int64_t Is, hipStream_t st);
+hipError_t launch_pack_outside(uint8_t *dst, const uint16_t *wup, const uint16_t *sd, int64_t Lt,
+                               int64_t H, int64_t S, int64_t Is, hipStream_t st);
+hipError_t launch_pack_gateup(uint8_t *dst, const uint8_t *gc, const uint8_t *gs, const uint8_t *uc,
+                              const uint8_t *us, int64_t E, int64_t I, int64_t Lt, hipStream_t st);
+hipError_t launch_pack_down(uint8_t *dst, const uint8_t *dc, const uint8_t *ds, int64_t E, int64_t I,
+                            int64_t Lt, hipStream_t st);
+hipError_t launch_unpack_mx(const uint8_t *packed_expert, int64_t N, int64_t K, int interleave,
+                            int which_half, uint16_t *out, hipStream_t st);
+
+// Routing.
+constexpr int PERM_TOKENS_PER_BLOCK = 32;
+hipError_t launch_topk(const float *logits, int T, int E, int K, int32_t *ids, float *w, hipStream_t st);
+hipError_t launch_permute(const int32_t *ids, int T, int K, int E, int32_t *hist, int32_t *counts,
+                          int32_t *offsets, int32_t *sorted_pairs, int32_t *inv, hipStream_t st);
+
+// Forward helpers.
+hipError_t launch_tilemap(const int32_t *offsets, int E, int bm1, int32_t *tiles1, int bm2, int32_t *tiles2,
+                          hipStream_t st);
+hipError_t launch_combine(const uint16_t *Y, int Lt, const int32_t *inv, const float *w, int T, int K,
+                          uint16_t *out, int64_t ldo, hipStream_t st);
+
+} // namespace mxmoe

@@ -1,0 +1,78 @@
+"""MoELayer: owns the packed weights, workspace and routing buffers of one layer on one GPU and
+calls the C ABI (torch provides device memory and the stream; all arithmetic runs in HIP)."""
+from __future__ import annotations
+
+import torch
+
+from . import abi
+
+
+class MoELayer:
+    """One MXFP4 latent-MoE layer on the current GPU.
+
+    ``weights`` maps the canonical weight names of ``abi.WEIGHT_FIELDS`` to device tensors
+    (BF16 bit patterns as int16/bfloat16, MXFP4 codes/scales as uint8); they are only read while
+    the packing kernels run and may be dropped after the first synchronisation.
+    """
+
+    def __init__(self, hidden, latent, n_experts, top_k, inter, n_shared, shared_inter,
+                 has_latent_proj, weights: dict, T_max: int, device="cuda", stream=None):
+        self.cfg = abi.make_config(hidden, latent, n_experts, top_k, inter, n_shared, shared_inter,
+                                   has_latent_proj)
+        self.E, self.K, self.Lt = n_experts, top_k, latent
+        self.H = hidden if has_latent_proj else latent
+        self.T_max = T_max
+        packed_bytes, ws_bytes = abi.query(self.cfg, T_max)
+        self.device = torch.device(device)
+        self.packed = torch.empty(packed_bytes, dtype=torch.uint8, device=self.device)
+        self.workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=self.device)
+        self.handle = abi.create(self.cfg, weights, self.packed, stream)
+
+    def alloc_routing(self, T: int) -> dict:
+        d, P = self.device, max(T * self.K, 1)
+        i32 = dict(dtype=torch.int32, device=d)
+        return dict(topk_ids=torch.empty(max(T, 1), self.K, **i32),
+                    topk_w=torch.empty(max(T, 1), self.K, dtype=torch.float32, device=d),
+                    counts=torch.empty(self.E, **i32), offsets=torch.empty(self.E + 1, **i32),
+                    sorted_pairs=torch.empty(P, **i32), inv=torch.empty(P, **i32))
+
+    def _check_T(self, T):
+        if T > self.T_max:
+            raise ValueError(f"T={T} exceeds T_max={self.T_max}")
+
+    def route(self, x, T, routing, logit_bias=None, logits_in=None, logits_out=None, stream=None):
+        self._check_T(T)
+        abi.route(self.handle, x, T, routing, self.workspace, logit_bias, logits_in, logits_out, stream)
+
+    def forward(self, x, T, routing, out=None, stream=None):
+        self._check_T(T)
+        if out is None:
+            out = torch.empty(max(T, 1), self.H, dtype=torch.bfloat16, device=self.device)
+        abi.forward(self.handle, x, T, routing, out, self.workspace, stream)
+        return out
+
+    def unpack_expert(self, e: int, which: int, stream=None):
+        rows, cols = (self.cfg.inter, self.Lt) if which < 2 else (self.Lt, self.cfg.inter)
+        out = torch.empty(rows, cols, dtype=torch.bfloat16, device=self.device)
+        abi.unpack_expert(self.handle, e, which, out, stream)
+        return out
+
+    def workspace_view(self, T: int, region: str, shape, dtype):
+        """Tensor view of a workspace region (test hook)."""
+        off = abi.workspace_layout(self.cfg, T)[region]
+        n = 1
+        for s in shape:
+            n *= s
+        nbytes = n * torch.empty(0, dtype=dtype).element_size()
+        return self.workspace[off:off + nbytes].view(dtype).view(*shape)
+
+    def close(self):
+        if self.handle:
+            abi.destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -58,6 +58,7 @@ def lib():
             "or_output": (None, [P, I64, I64, P, I64, P, P]),
             "or_experts": (None, [P, I64, I64, P, I64, I64, P, P, P, P, P, P, P, P]),
             "or_combine": (None, [P, P, I64, I64, I64, P]),
+            "or_num_threads": (ctypes.c_int, []),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -86,6 +87,10 @@ def f64_to_bf16(v) -> np.ndarray:
     v = np.asarray(v, dtype=np.float64)
     f = np.vectorize(lambda s: lib().or_double_to_bf16(float(s)), otypes=[np.uint16])
     return f(v) if v.size else np.zeros(v.shape, np.uint16)
+
+
+def num_threads() -> int:
+    return int(lib().or_num_threads())
 
 
 def e2m1(code: int) -> float:

@@ -1,0 +1,86 @@
+"""Host-side checks of the C ABI: the library loads, exports every entry point the header
+declares, sizes its buffers as documented and rejects bad arguments before touching the GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from mxfp4_latent_mixture_sigmoid_amd import abi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _built():
+    if not os.path.exists(abi.LIB_PATH):
+        from mxfp4_latent_mixture_sigmoid_amd import build
+        build.build()
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "mxmoe.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_function():
+    names = header_functions()
+    assert {"moe_query", "moe_create", "moe_route", "moe_forward", "moe_destroy", "moe_strerror"} <= set(names)
+    L = ctypes.CDLL(abi.LIB_PATH)
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(abi.SIGNATURES), "binding and header disagree"
+
+
+def _cfg(**kw):
+    base = dict(hidden=7168, latent=3584, n_experts=896, top_k=16, inter=384, n_shared=2,
+                shared_inter=384, has_latent_proj=1)
+    base.update(kw)
+    return abi.make_config(**base)
+
+
+def test_packed_size_matches_layout():
+    pb, wb = abi.query(_cfg(), 64)
+    E, H, Lt, I, S, Is = 896, 7168, 3584, 384, 2, 384
+    mx = lambda n, k: (n // 16) * (k // 128) * 1088        # noqa: E731
+    expect = E * H * 2 + (Lt + 2 * S * Is) * H * 2 + H * (Lt + S * Is) * 2 + E * (mx(2 * I, Lt) + mx(Lt, I))
+    assert expect <= pb < expect + 5 * 256
+    # one expert's MXFP4 bytes: three 3584 x 384 matrices at 4.25 bits per value
+    assert mx(2 * I, Lt) + mx(Lt, I) == 3 * 3584 * 384 * 17 // 32
+    lay = abi.workspace_layout(_cfg(), 64)
+    assert lay["total"] == wb and all(lay[k] % 256 == 0 for k in lay)
+    assert lay["y"] + 64 * 16 * Lt * 2 <= lay["total"]
+
+
+@pytest.mark.parametrize("kw", [dict(latent=3500), dict(inter=100), dict(top_k=0), dict(top_k=33),
+                                dict(n_experts=1025), dict(top_k=9, n_experts=8),
+                                dict(has_latent_proj=0, n_shared=1), dict(hidden=7000),
+                                dict(shared_inter=30), dict(n_shared=-1)])
+def test_query_rejects_bad_configs(kw):
+    c = _cfg(**kw)
+    pb = ctypes.c_size_t(0)
+    assert abi.lib().moe_query(ctypes.byref(c), 64, ctypes.byref(pb), None) == abi.Status.INVALID_ARG
+
+
+def test_query_rejects_negative_tokens_and_reports_strings():
+    c = _cfg()
+    assert abi.lib().moe_query(ctypes.byref(c), -1, None, None) == abi.Status.INVALID_ARG
+    for s in abi.Status:
+        assert abi.lib().moe_strerror(int(s))
+    assert abi.lib().moe_strerror(-99) == b"unknown status"
+
+
+def test_create_route_forward_reject_null_arguments_without_gpu_work():
+    L = abi.lib()
+    c = _cfg()
+    w = abi.MoeWeights()
+    h = ctypes.c_void_p()
+    assert L.moe_create(ctypes.byref(c), ctypes.byref(w), None, 0, None, ctypes.byref(h)) == abi.Status.INVALID_ARG
+    assert L.moe_create(ctypes.byref(c), ctypes.byref(w), 256, 1 << 40, None, ctypes.byref(h)) == \
+        abi.Status.INVALID_ARG
+    r = abi.MoeRouting()
+    assert L.moe_route(None, None, 4, None, None, None, ctypes.byref(r), None, 0, None) == abi.Status.INVALID_ARG
+    assert L.moe_forward(None, None, 4, ctypes.byref(r), None, None, 0, None) == abi.Status.INVALID_ARG
+    assert L.moe_unpack_expert(None, 0, 0, None, None) == abi.Status.INVALID_ARG
+    L.moe_destroy(None)

@@ -1,0 +1,155 @@
+"""GPU parity: the HIP path (through the C ABI) against the FP64 CPU oracle.
+
+Routing ids and the expert grouping must match bit for bit (the oracle selects on the GPU's own
+FP32 logits); every floating-point tensor (logits, z, h, y, zc, h_s, out) must satisfy
+max|err| <= 2e-2 rms(ref) and mean|err| <= 2e-3 rms(ref); gate weights match to 1e-6 relative.
+"""
+from dataclasses import replace
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle as O
+from tests import gpu_helpers as G
+from workload import SHAPES, LayerShape, make_inputs, sample_tokens, tie_tokens
+
+pytestmark = pytest.mark.gpu
+
+MID = LayerShape("mid", 200, 1024, 512, 64, 8, 256, 2, 128, True, "uniform", 0.0, 7)
+MID_ZIPF = LayerShape("mid_zipf", 300, 1024, 512, 96, 6, 256, 1, 256, True, "zipf", 0.0, 8)
+NOLAT = LayerShape("nolat", 77, 512, 512, 32, 4, 256, 0, 0, False, "uniform", 0.0, 9)
+SMALL_SHAPES = {s.name: s for s in (SHAPES["tiny"], MID, MID_ZIPF, NOLAT)}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    G.ensure_built()
+    yield
+
+
+_cache = {}
+
+
+def _setup(name):
+    if name not in _cache:
+        shape = SMALL_SHAPES[name]
+        G.log(f"[setup] {name}: T={shape.T} E={shape.E} K={shape.K}")
+        inp = make_inputs(shape)
+        layer = G.make_layer(shape, inp, T_max=shape.T)
+        _cache[name] = (shape, inp, layer)
+    return _cache[name]
+
+
+@pytest.mark.parametrize("name", list(SMALL_SHAPES))
+def test_unpack_bit_exact(name):
+    shape, inp, layer = _setup(name)
+    for e in sorted({0, shape.E // 2, shape.E - 1}):
+        for which, (c, s) in enumerate((("gate_codes", "gate_scales"), ("up_codes", "up_scales"),
+                                        ("down_codes", "down_scales"))):
+            got = G.host_bf16(layer.unpack_expert(e, which))
+            ref = O.f64_to_bf16(O.dequant(inp[c][e], inp[s][e]))
+            assert np.array_equal(got, ref), (name, e, which)
+
+
+def test_unpack_scale_range_bit_exact():
+    # Every E8M0 byte whose products stay in BF16's normal range converts exactly.
+    shape = replace(SHAPES["tiny"], E=2, name="scales")
+    inp = make_inputs(shape)
+    rng = np.random.default_rng(1)
+    for m in ("gate", "up", "down"):
+        inp[m + "_scales"] = rng.integers(2, 253, inp[m + "_scales"].shape).astype(np.uint8)
+    layer = G.make_layer(shape, inp, T_max=1)
+    for which, (c, s) in enumerate((("gate_codes", "gate_scales"), ("up_codes", "up_scales"),
+                                    ("down_codes", "down_scales"))):
+        got = G.host_bf16(layer.unpack_expert(1, which))
+        ref = O.f64_to_bf16(O.dequant(inp[c][1], inp[s][1]))
+        assert np.array_equal(got, ref)
+
+
+@pytest.mark.parametrize("name", list(SMALL_SHAPES))
+def test_forward_parity(name):
+    shape, inp, layer = _setup(name)
+    G.log(f"[forward] {name}")
+    run = G.GpuRun(layer, shape, inp)
+    G.check_forward(shape, inp, run)
+    if shape.routing == "zipf":
+        assert np.sum(run.counts == 0) > 0, "skewed routing should leave experts empty"
+
+
+@pytest.mark.parametrize("name", ["tiny", "mid"])
+def test_deterministic_and_token_permutation_invariant(name):
+    shape, inp, layer = _setup(name)
+    a = G.GpuRun(layer, shape, inp)
+    b = G.GpuRun(layer, shape, inp)
+    ra, rb = a.rows(), b.rows()
+    assert np.array_equal(ra["out"], rb["out"]) and np.array_equal(a.ids, b.ids)
+    assert np.array_equal(ra["y"], rb["y"]) and np.array_equal(ra["h"], rb["h"])
+    perm = np.random.default_rng(3).permutation(shape.T)
+    c = G.GpuRun(layer, shape, dict(inp, x=inp["x"][perm]))
+    assert np.array_equal(c.ids, a.ids[perm])
+    assert np.array_equal(c.rows()["out"], ra["out"][perm])
+
+
+@pytest.mark.parametrize("T", [1, 2, 15, 17, 33])
+def test_ragged_token_counts(T):
+    shape, inp, layer = _setup("mid")
+    sub = dict(inp, x=inp["x"][:T])
+    run = G.GpuRun(layer, shape, sub)
+    G.check_forward(replace(shape, T=T), sub, run)
+
+
+def test_zero_tokens_is_noop():
+    shape, inp, layer = _setup("tiny")
+    r = layer.alloc_routing(1)
+    r["counts"].fill_(-7)
+    layer.route(G.dev(inp["x"]), 0, r)
+    out = torch.full((1, shape.H), 3.0, dtype=torch.bfloat16, device="cuda")
+    layer.forward(G.dev(inp["x"]), 0, r, out=out)
+    torch.cuda.synchronize()
+    assert int(r["counts"][0]) == -7 and float(out[0, 0]) == 3.0
+
+
+@pytest.mark.parametrize("E,K", [(16, 16), (48, 1), (8, 8)])
+def test_degenerate_topk(E, K):
+    shape = replace(MID, name=f"deg{E}_{K}", T=40, E=E, K=K, seed=11)
+    inp = make_inputs(shape)
+    layer = G.make_layer(shape, inp, T_max=shape.T)
+    run = G.GpuRun(layer, shape, inp)
+    G.check_forward(shape, inp, run)
+    if K == E:
+        assert np.all(np.sort(run.ids, 1) == np.arange(E))
+    if K == 1:
+        assert np.all(run.w == 1.0)
+
+
+def test_planted_ties_select_lower_index():
+    shape, inp, layer = _setup("mid")
+    run = G.GpuRun(layer, shape, inp)
+    lg = run.logits.copy()
+    toks = np.arange(0, shape.T, 7)
+    order = O.select(lg[toks].astype(np.float64), shape.K + 1)
+    e_k, e_k1 = order[:, shape.K - 1], order[:, shape.K]
+    lg[toks, e_k1] = lg[toks, e_k]
+    tied = G.GpuRun(layer, shape, dict(inp), logits_in=lg)
+    lo = np.minimum(e_k, e_k1)
+    hi = np.maximum(e_k, e_k1)
+    assert all(lo[i] in tied.ids[t] and hi[i] not in tied.ids[t] for i, t in enumerate(toks))
+    G.check_forward(shape, inp, tied, oracle_logits_in=lg)
+
+
+def test_bad_arguments_raise():
+    from mxfp4_latent_mixture_sigmoid_amd import abi
+    shape, inp, layer = _setup("tiny")
+    r = layer.alloc_routing(shape.T)
+    x = G.dev(inp["x"])
+    with pytest.raises(abi.MoEError) as ei:       # logits_in together with x
+        abi.route(layer.handle, x, shape.T, r, layer.workspace, logits_in=torch.zeros(1, device="cuda"))
+    assert ei.value.status == abi.Status.INVALID_ARG
+    with pytest.raises(abi.MoEError) as ei:       # workspace too small
+        abi.route(layer.handle, x, shape.T, r, layer.workspace[:256])
+    assert ei.value.status == abi.Status.BUFFER_TOO_SMALL
+    with pytest.raises(abi.MoEError):             # output aliases input
+        abi.forward(layer.handle, x, shape.T, r, x, layer.workspace)

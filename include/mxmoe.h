@@ -104,8 +104,8 @@ moe_status moe_query(const moe_config *cfg, int32_t T_max, size_t *packed_bytes,
 
 /* Test hook: byte offsets inside the workspace for T tokens, in this order: FP32 logits [T,E],
  * per-block expert histogram, the two expert tile lists, z [T,Lt], [zc | h_s] [T, Lt + S Is],
- * h [T K, I] and y [T K, Lt] (expert-sorted rows, BF16), then the total size. `offsets` is a host
- * array of 9 entries. Host-only. */
+ * h [T K, I] and y [T K, Lt] (expert-sorted rows, BF16), FP32 split-K partials, then the total
+ * size. `offsets` is a host array of 10 entries. Host-only. */
 moe_status moe_query_workspace_layout(const moe_config *cfg, int32_t T, size_t *offsets);
 
 /* Validate the config and weights, then enqueue the packing of every weight into `packed`
@@ -147,7 +147,9 @@ typedef enum {
     MOE_KERNEL_GATEUP = 5,   /* routed gate/up product with the GLU                 */
     MOE_KERNEL_DOWN = 6,     /* routed down product                                 */
     MOE_KERNEL_COMBINE = 7,  /* gate-weighted combine                               */
-    MOE_KERNEL_OUT = 8       /* up-projection + shared down-projection              */
+    MOE_KERNEL_OUT = 8,      /* up-projection + shared down-projection              */
+    MOE_KERNEL_XSIDE_EPI = 9,/* few-token x-side partial sums, GLU and tile lists   */
+    MOE_KERNEL_OUT_EPI = 10  /* few-token output partial sums                       */
 } moe_kernel;
 
 /* Profiling hook (benchmarks, tests): after moe_profile_begin, every kernel launch of moe_route

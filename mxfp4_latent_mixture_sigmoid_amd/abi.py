@@ -118,7 +118,7 @@ def query(cfg: MoeConfig, T_max: int):
     return pb.value, wb.value
 
 
-WS_REGIONS = ("logits", "hist", "tiles1", "tiles2", "z", "acat", "h", "y", "total")
+WS_REGIONS = ("logits", "hist", "tiles1", "tiles2", "z", "acat", "h", "y", "partials", "total")
 
 
 def workspace_layout(cfg: MoeConfig, T: int) -> dict:
@@ -156,7 +156,8 @@ def unpack_expert(h, e: int, which: int, out, stream=None) -> None:
     check(lib().moe_unpack_expert(h, e, which, ptr(out), stream_handle(stream)), "moe_unpack_expert")
 
 
-KERNELS = ("router", "topk", "permute", "xside", "tilemap", "gateup", "down", "combine", "out")
+KERNELS = ("router", "topk", "permute", "xside", "tilemap", "gateup", "down", "combine", "out", "xside_epi",
+           "out_epi")
 
 
 def profile_begin(h, max_launches: int) -> None:

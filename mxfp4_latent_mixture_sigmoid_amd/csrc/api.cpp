@@ -6,6 +6,7 @@
 #include <climits>
 #include <cstdlib>
 #include <new>
+#include <algorithm>
 #include <vector>
 
 using namespace mxmoe;
@@ -29,6 +30,7 @@ namespace {
 constexpr int64_t ALIGN = 256;
 constexpr int BM_GEMM1 = 16;   // rows per tile of the gate/up product
 constexpr int BM_GEMM2 = 16;   // rows per tile of the down product
+constexpr int SKINNY_STEPS = 16; // 32-wide K steps per split of the few-token dense products
 
 int64_t align_up(int64_t v) { return (v + ALIGN - 1) / ALIGN * ALIGN; }
 
@@ -87,7 +89,7 @@ PackedLayout packed_layout(const moe_config *c)
 }
 
 struct WsLayout {
-    int64_t logits, hist, tiles1, tiles2, z, acat, h, y, total;
+    int64_t logits, hist, tiles1, tiles2, z, acat, h, y, partials, total;
     int64_t max_tiles1, max_tiles2;
 };
 
@@ -124,6 +126,18 @@ WsLayout ws_layout(const moe_config *c, int64_t T)
     off = align_up(off + T * K * I * 2);
     L.y = off;
     off = align_up(off + T * K * Lt * 2);
+    L.partials = off;
+    if (T <= SKINNY_MAX_M) {   // split-K partial tiles of the few-token dense products
+        const int64_t Hin = c->has_latent_proj ? c->hidden : c->latent, E_pad = (E + 15) / 16 * 16;
+        const int64_t R = SKINNY_MAX_M;   // partial tiles keep 64 rows whatever T is
+        int64_t p = skinny_splits((int)Hin, SKINNY_STEPS) * R * E_pad;
+        if (c->has_latent_proj) {
+            const int64_t H = c->hidden;
+            p = std::max(p, (int64_t)skinny_splits((int)H, SKINNY_STEPS) * R * (Lt + 2 * S * Is));
+            p = std::max(p, (int64_t)skinny_splits((int)(Lt + S * Is), SKINNY_STEPS) * R * H);
+        }
+        off = align_up(off + p * 4);
+    }
     L.total = off;
     return L;
 }
@@ -210,8 +224,8 @@ moe_status moe_query_workspace_layout(const moe_config *cfg, int32_t T, size_t *
     if (!valid_config(cfg) || T < 0 || !sizes_fit_int32(cfg, T) || !offsets)
         return MOE_ERR_INVALID_ARG;
     const WsLayout W = ws_layout(cfg, T);
-    const int64_t v[9] = {W.logits, W.hist, W.tiles1, W.tiles2, W.z, W.acat, W.h, W.y, W.total};
-    for (int i = 0; i < 9; i++)
+    const int64_t v[10] = {W.logits, W.hist, W.tiles1, W.tiles2, W.z, W.acat, W.h, W.y, W.partials, W.total};
+    for (int i = 0; i < 10; i++)
         offsets[i] = (size_t)v[i];
     return MOE_OK;
 }
@@ -366,8 +380,29 @@ moe_status moe_route(moe_handle *h, const void *x, int32_t T, const float *logit
     uint8_t *ws = static_cast<uint8_t *>(workspace);
     const int E = c->n_experts, K = c->top_k;
 
-    const float *logits = logits_in;
-    if (!logits_in) {
+    float *partials = reinterpret_cast<float *>(ws + W.partials);
+    TopkArgs ta{};
+    ta.T = T;
+    ta.E = E;
+    ta.K = K;
+    ta.ids = r->topk_ids;
+    ta.w = r->topk_w;
+    ta.splits = 1;
+    ta.ld = E;
+    if (logits_in) {
+        ta.src = logits_in;
+    } else if (T <= SKINNY_MAX_M) {   // few tokens: split-K partials, summed (+bias) by the top-K kernel
+        const int64_t pstride = (int64_t)(h->E_pad / 16) * SKINNY_TILE_FLOATS;
+        SkinnyArgs g{static_cast<const uint16_t *>(x), h->Hin, T, h->packed + h->off_router, h->E_pad, h->Hin,
+                     partials, pstride};
+        MOE_LAUNCH(MOE_KERNEL_ROUTER, launch_skinny(g, 4, SKINNY_STEPS, st));
+        ta.src = partials;
+        ta.partials = 1;
+        ta.split_stride = pstride;
+        ta.splits = skinny_splits(h->Hin, SKINNY_STEPS);
+        ta.bias = logit_bias;
+        ta.logits_out = logits_out;
+    } else {
         float *lg = logits_out ? logits_out : reinterpret_cast<float *>(ws + W.logits);
         GemmArgs g{};
         g.A = static_cast<const uint16_t *>(x);
@@ -379,11 +414,15 @@ moe_status moe_route(moe_handle *h, const void *x, int32_t T, const float *logit
         g.split = INT_MAX;
         g.lo = OutDesc{OUT_F32, lg, E, 0, E, logit_bias};
         MOE_LAUNCH(MOE_KERNEL_ROUTER, launch_gemm_dense(g, GEMM_SKINNY_N16, st));
-        logits = lg;
+        ta.src = lg;
     }
-    MOE_LAUNCH(MOE_KERNEL_TOPK, launch_topk(logits, T, E, K, r->topk_ids, r->topk_w, st));
-    MOE_LAUNCH(MOE_KERNEL_PERMUTE, launch_permute(r->topk_ids, T, K, E, reinterpret_cast<int32_t *>(ws + W.hist), r->counts, r->offsets,
-                           r->sorted_pairs, r->inv, st));
+    MOE_LAUNCH(MOE_KERNEL_TOPK, launch_topk(ta, st));
+    if (T <= PERM_SMALL_MAX_T)
+        MOE_LAUNCH(MOE_KERNEL_PERMUTE, launch_permute_small(r->topk_ids, T, K, E, r->counts, r->offsets,
+                                                            r->sorted_pairs, r->inv, st));
+    else
+        MOE_LAUNCH(MOE_KERNEL_PERMUTE, launch_permute(r->topk_ids, T, K, E, reinterpret_cast<int32_t *>(ws + W.hist),
+                                                      r->counts, r->offsets, r->sorted_pairs, r->inv, st));
     return MOE_OK;
 }
 
@@ -419,20 +458,31 @@ moe_status moe_forward(moe_handle *h, const void *x, int32_t T, const moe_routin
     int32_t *tiles1 = reinterpret_cast<int32_t *>(ws + W.tiles1);
     int32_t *tiles2 = reinterpret_cast<int32_t *>(ws + W.tiles2);
 
-    if (lat) {   // z = bf16(x W_down^T) and h_s = bf16(silu(x Wg_s^T) (x Wu_s^T)) in one pass over x
-        GemmArgs g{};
-        g.A = static_cast<const uint16_t *>(x);
-        g.lda = H;
-        g.B = h->packed + h->off_xside;
-        g.M = T;
-        g.N = Lt + 2 * S * Is;
-        g.K = H;
-        g.split = Lt;
-        g.lo = OutDesc{OUT_BF16, Z, Lt, 0, Lt, nullptr};
-        g.hi = OutDesc{OUT_GLU, Acat + Lt, ldcat, Lt, INT_MAX, nullptr};
-        MOE_LAUNCH(MOE_KERNEL_XSIDE, launch_gemm_dense(g, GEMM_SKINNY_N32, st));
+    float *partials = reinterpret_cast<float *>(ws + W.partials);
+    const int Nx = Lt + 2 * S * Is;
+    if (lat && T <= SKINNY_MAX_M) {   // z and h_s from split-K partials; the epilogue also builds the tile lists
+        const int64_t pstride = (int64_t)(Nx / 16) * SKINNY_TILE_FLOATS;
+        SkinnyArgs g{static_cast<const uint16_t *>(x), H, T, h->packed + h->off_xside, Nx, H, partials, pstride};
+        MOE_LAUNCH(MOE_KERNEL_XSIDE, launch_skinny_persist(g, 8, 18, st));
+        XsideEpiArgs ea{partials, pstride, skinny_splits(H, SKINNY_STEPS), T, Nx, Lt, 2 * S * Is, Z, Acat, ldcat,
+                        r->offsets, E, BM_GEMM1, BM_GEMM2, tiles1, tiles2};
+        MOE_LAUNCH(MOE_KERNEL_XSIDE_EPI, launch_xside_epilogue(ea, st));
+    } else {
+        if (lat) {   // z = bf16(x W_down^T) and h_s = bf16(silu(x Wg_s^T) (x Wu_s^T)) in one pass over x
+            GemmArgs g{};
+            g.A = static_cast<const uint16_t *>(x);
+            g.lda = H;
+            g.B = h->packed + h->off_xside;
+            g.M = T;
+            g.N = Nx;
+            g.K = H;
+            g.split = Lt;
+            g.lo = OutDesc{OUT_BF16, Z, Lt, 0, Lt, nullptr};
+            g.hi = OutDesc{OUT_GLU, Acat + Lt, ldcat, Lt, INT_MAX, nullptr};
+            MOE_LAUNCH(MOE_KERNEL_XSIDE, launch_gemm_dense(g, GEMM_SKINNY_N32, st));
+        }
+        MOE_LAUNCH(MOE_KERNEL_TILEMAP, launch_tilemap(r->offsets, E, BM_GEMM1, tiles1, BM_GEMM2, tiles2, st));
     }
-    MOE_LAUNCH(MOE_KERNEL_TILEMAP, launch_tilemap(r->offsets, E, BM_GEMM1, tiles1, BM_GEMM2, tiles2, st));
     {   // h = bf16(silu(z Wg_e^T) (z Wu_e^T)) for every pair, rows in expert-sorted order
         GemmArgs g{};
         g.A = lat ? Z : static_cast<const uint16_t *>(x);
@@ -464,7 +514,13 @@ moe_status moe_forward(moe_handle *h, const void *x, int32_t T, const moe_routin
     // zc = bf16(sum_j w_j y_j) in slot order: into the first Lt columns of [zc | h_s], or the output
     MOE_LAUNCH(MOE_KERNEL_COMBINE, launch_combine(Yb, Lt, r->inv, r->topk_w, T, K, lat ? Acat : static_cast<uint16_t *>(out),
                            lat ? ldcat : Lt, st));
-    if (lat) {   // out = bf16([zc | h_s] [W_up | Wd_s]^T)
+    if (lat && T <= SKINNY_MAX_M) {   // out = bf16([zc | h_s] [W_up | Wd_s]^T) from split-K partials
+        const int64_t pstride = (int64_t)(H / 16) * SKINNY_TILE_FLOATS;
+        SkinnyArgs g{Acat, ldcat, T, h->packed + h->off_outside, H, ldcat, partials, pstride};
+        MOE_LAUNCH(MOE_KERNEL_OUT, launch_skinny_persist(g, 8, 28, st));
+        MOE_LAUNCH(MOE_KERNEL_OUT_EPI, launch_out_epilogue(partials, pstride, skinny_splits(ldcat, SKINNY_STEPS), T, H,
+                                                           static_cast<uint16_t *>(out), st));
+    } else if (lat) {
         GemmArgs g{};
         g.A = Acat;
         g.lda = ldcat;

@@ -4,54 +4,6 @@
 
 namespace mxmoe {
 
-// One workgroup (blockDim = 1024 >= E). Expert e with n_e rows gets ceil(n_e / bm) tiles of at
-// most bm consecutive rows of the expert-sorted order; tiles are listed expert by expert.
-// Layout: tiles[0] = tile count, then from element 4 one int4 (expert, row begin, row end, 0).
-__device__ void write_tiles(const int32_t *offsets, int E, int bm, int32_t *tiles, int *sh)
-{
-    const int e = threadIdx.x;
-    const int beg = e < E ? offsets[e] : 0;
-    const int n = e < E ? offsets[e + 1] - beg : 0;
-    const int c = (n + bm - 1) / bm;
-    int total;
-    const int base = [&] {
-        // exclusive scan of c over the workgroup
-        const int lane = threadIdx.x & (WAVE - 1), wid = threadIdx.x / WAVE;
-        const int nw = (blockDim.x + WAVE - 1) / WAVE;
-        int inc = c;
-#pragma unroll
-        for (int o = 1; o < WAVE; o <<= 1) {
-            const int t = __shfl_up(inc, o);
-            if (lane >= o)
-                inc += t;
-        }
-        if (lane == WAVE - 1)
-            sh[wid] = inc;
-        __syncthreads();
-        if (wid == 0) {
-            int x = lane < nw ? sh[lane] : 0;
-#pragma unroll
-            for (int o = 1; o < WAVE; o <<= 1) {
-                const int t = __shfl_up(x, o);
-                if (lane >= o)
-                    x += t;
-            }
-            if (lane < nw)
-                sh[lane] = x;
-        }
-        __syncthreads();
-        const int b = wid ? sh[wid - 1] : 0;
-        total = sh[nw - 1];
-        __syncthreads();
-        return b + inc - c;
-    }();
-    int4 *out = reinterpret_cast<int4 *>(tiles + TILE_HEADER_INTS);
-    for (int j = 0; j < c; j++)
-        out[base + j] = int4{e, beg + j * bm, min(beg + (j + 1) * bm, beg + n), 0};
-    if (threadIdx.x == 0)
-        tiles[0] = total;
-}
-
 __global__ __launch_bounds__(1024) void tilemap_kernel(const int32_t *__restrict__ offsets, int E, int bm1,
                                                        int32_t *__restrict__ tiles1, int bm2,
                                                        int32_t *__restrict__ tiles2)

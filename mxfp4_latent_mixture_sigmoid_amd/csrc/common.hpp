@@ -20,9 +20,10 @@ constexpr int WAVE = 64;
 // within a row block the K axis is cut into steps. A block is laid out so that lane l of a wave
 // reads bytes [16 l, 16 l + 16) and receives exactly its operand of the 16x16x32 BF16 matrix-core
 // instruction: row (l % 16), inputs 8 (l / 16) .. 8 (l / 16) + 7 of each 32-wide input slice.
-// Blocks are stored row-block major: block (nb, kb) at index nb * (K / step) + kb.
+// MX blocks are stored row-block major: block (nb, kb) at index nb * (K / 128) + kb.
 //
 //  BF16 blocks: 16 rows x 32 inputs, 1024 bytes; lane l holds row l%16, inputs 8(l/16)..+7.
+//               Block order: see bf16_block_index (K-chunk major).
 //  MX blocks:   16 rows x 128 inputs = four 32-input slices, 1024 code bytes + 64 scale bytes.
 //               Lane l's 16 code bytes are four 4-byte words; word j holds the 8 E2M1 codes of
 //               row l%16, inputs 32 j + 8 (l/16) .. +7 (low nibble first). Scale byte
@@ -34,6 +35,21 @@ constexpr int BF16_STEP = 32;
 constexpr int MX_CODE_BYTES = 1024;
 constexpr int MX_BLOCK_BYTES = 1088;
 constexpr int MX_STEP = 128;
+constexpr int TILE_HEADER_INTS = 4;   // ints before the first int4 entry of a tile list
+
+// Dense BF16 blocks are grouped by K chunks of BF16_CHUNK_STEPS 32-wide steps (512 inputs): every
+// row block's part of chunk 0, then of chunk 1, ...; within a chunk, row block by row block. Waves
+// that stream one K chunk of consecutive row blocks then read one contiguous range of HBM, which
+// streams far faster than ranges spread one row-block stride apart.
+constexpr int BF16_CHUNK_STEPS = 16;
+__host__ __device__ inline int64_t bf16_block_index(int64_t nb, int64_t kb, int64_t N, int64_t K)
+{
+    const int64_t ksteps = K / BF16_STEP;
+    const int64_t c = kb / BF16_CHUNK_STEPS, within = kb % BF16_CHUNK_STEPS;
+    const int64_t rest = ksteps - c * BF16_CHUNK_STEPS;
+    const int64_t cs = rest < BF16_CHUNK_STEPS ? rest : BF16_CHUNK_STEPS;   // steps in chunk c
+    return c * BF16_CHUNK_STEPS * (N / 16) + nb * cs + within;
+}
 
 __host__ __device__ inline int64_t bf16_packed_bytes(int64_t N, int64_t K) { return N * K * 2; }
 __host__ __device__ inline int64_t mx_packed_bytes(int64_t N, int64_t K)
@@ -102,5 +118,16 @@ __device__ inline f32x4_t mfma16(bf16x8_t a, bf16x8_t b, f32x4_t c)
 __device__ inline float silu_f32(float g) { return g / (1.0f + expf(-g)); }
 
 __device__ inline u32x4_t load16(const void *p) { return *reinterpret_cast<const u32x4_t *>(p); }
+
+// Weight streams are read once per call: non-temporal loads keep them from displacing the
+// activations in the caches and let HBM stream at a markedly higher rate.
+__device__ inline u32x4_t load16_nt(const void *p)
+{
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
+}
+__device__ inline uint32_t load4_nt(const void *p)
+{
+    return __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(p));
+}
 
 } // namespace mxmoe

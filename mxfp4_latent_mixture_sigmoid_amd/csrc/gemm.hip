@@ -22,19 +22,20 @@ __global__ __launch_bounds__(WAVE *WK) void gemm_kernel(const GemmArgs g)
     const int lane = threadIdx.x & (WAVE - 1);
     const int wv = threadIdx.x / WAVE;
 
+    // Column block fastest in the launch order: neighbouring workgroups stream neighbouring weights.
     int group = 0, m0, m1;
     if (g.tiles) {
-        if ((int)blockIdx.x >= g.tiles[0])
+        if ((int)blockIdx.y >= g.tiles[0])
             return;
-        const int4 t = reinterpret_cast<const int4 *>(g.tiles + 4)[blockIdx.x];
+        const int4 t = reinterpret_cast<const int4 *>(g.tiles + TILE_HEADER_INTS)[blockIdx.y];
         group = t.x;
         m0 = t.y;
         m1 = t.z;
     } else {
-        m0 = blockIdx.x * BM;
+        m0 = blockIdx.y * BM;
         m1 = min(g.M, m0 + BM);
     }
-    const int n0 = blockIdx.y * BN;
+    const int n0 = blockIdx.x * BN;
 
     // Activation rows of this lane for each 16-row fragment (gathered when a_index is set).
     const uint16_t *arow[MT];
@@ -69,8 +70,8 @@ __global__ __launch_bounds__(WAVE *WK) void gemm_kernel(const GemmArgs g)
 #pragma unroll
             for (int nf = 0; nf < NT; nf++) {
                 const uint8_t *blk = Bg + ((int64_t)(n0 / 16 + nf) * nsteps + s) * MX_BLOCK_BYTES;
-                codes[nf] = load16(blk + lane * 16);
-                sc[nf] = *reinterpret_cast<const uint32_t *>(blk + MX_CODE_BYTES + 4 * (lane & 15));
+                codes[nf] = load16_nt(blk + lane * 16);
+                sc[nf] = load4_nt(blk + MX_CODE_BYTES + 4 * (lane & 15));
             }
             u32x4_t a[MT][4];
 #pragma unroll
@@ -97,7 +98,7 @@ __global__ __launch_bounds__(WAVE *WK) void gemm_kernel(const GemmArgs g)
             u32x4_t b[NT];
 #pragma unroll
             for (int nf = 0; nf < NT; nf++)
-                b[nf] = load16(Bg + ((int64_t)(n0 / 16 + nf) * nsteps + s) * BF16_BLOCK_BYTES + lane * 16);
+                b[nf] = load16_nt(Bg + bf16_block_index(n0 / 16 + nf, s, g.N, g.K) * BF16_BLOCK_BYTES + lane * 16);
 #pragma unroll
             for (int mf = 0; mf < MT; mf++) {
                 const u32x4_t a = aval[mf] ? load16(arow[mf] + s * STEP) : zero4;
@@ -163,6 +164,139 @@ __global__ __launch_bounds__(WAVE *WK) void gemm_kernel(const GemmArgs g)
     }
 }
 
+// Grouped MXFP4 product for expert tiles of at most 16 rows (few tokens per expert), where the
+// time is the HBM stream of the expert weights. Each wave owns NT 16-row blocks of B and a K range
+// of whole 128-input blocks; for up to MAXS blocks at a time it issues every code, scale and
+// activation load first (addresses clamped into its range, so no load is conditional) and only
+// then converts and multiplies, so a wave keeps MAXS x NT KiB of weights in flight. WN waves
+// split the columns, WK waves the K range (summed in LDS in a fixed order).
+template <int NT, int WN, int WK, int MAXS>
+__global__ __launch_bounds__(WAVE *WN *WK) void mx_stream_kernel(const GemmArgs g)
+{
+    constexpr int BN = 16 * NT * WN;
+    __shared__ float red[WK * 16 * BN];
+    const int lane = threadIdx.x & (WAVE - 1);
+    const int wv = threadIdx.x / WAVE, wn = wv % WN, wk = wv / WN;
+
+    if ((int)blockIdx.y >= g.tiles[0])
+        return;
+    const int4 tile = reinterpret_cast<const int4 *>(g.tiles + TILE_HEADER_INTS)[blockIdx.y];
+    const int group = tile.x, m0 = tile.y, m1 = tile.z;
+    const int n0 = blockIdx.x * BN;
+
+    const int r = m0 + (lane & 15);
+    const bool aval = r < m1;
+    int64_t arow_idx = 0;
+    if (aval)
+        arow_idx = g.a_index ? (int64_t)(g.a_index[r] / g.a_div) : (int64_t)r;
+    const uint16_t *arow = g.A + arow_idx * g.lda + 8 * (lane >> 4);
+
+    const int nblk = g.K / MX_STEP;
+    const int kb0 = (wk * nblk) / WK, kb1 = ((wk + 1) * nblk) / WK;
+    const uint8_t *Bg = g.B + (int64_t)group * g.b_stride;
+    const int nb0 = n0 / 16 + wn * NT;
+    const bool wact = nb0 + NT <= g.N / 16;          // waves past the last column block idle
+
+    f32x4_t acc[NT];
+#pragma unroll
+    for (int nf = 0; nf < NT; nf++)
+        acc[nf] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    const u32x4_t zero4 = {0u, 0u, 0u, 0u};
+
+    for (int kb = kb0; wact && kb < kb1; kb += MAXS) {
+        const int cnt = min(MAXS, kb1 - kb);
+        u32x4_t codes[MAXS][NT];
+        uint32_t sc[MAXS][NT];
+        u32x4_t a[MAXS][4];
+#pragma unroll
+        for (int s = 0; s < MAXS; s++) {
+            const int blk = kb + min(s, cnt - 1);
+#pragma unroll
+            for (int nf = 0; nf < NT; nf++) {
+                const uint8_t *p = Bg + ((int64_t)(nb0 + nf) * nblk + blk) * MX_BLOCK_BYTES;
+                codes[s][nf] = load16_nt(p + lane * 16);
+                sc[s][nf] = load4_nt(p + MX_CODE_BYTES + 4 * (lane & 15));
+            }
+        }
+#pragma unroll
+        for (int s = 0; s < MAXS; s++) {
+            const int blk = kb + min(s, cnt - 1);
+#pragma unroll
+            for (int j = 0; j < 4; j++)
+                a[s][j] = aval ? load16(arow + blk * MX_STEP + 32 * j) : zero4;
+        }
+#pragma unroll
+        for (int s = 0; s < MAXS; s++) {
+            if (s < cnt) {
+#pragma unroll
+                for (int j = 0; j < 4; j++)
+#pragma unroll
+                    for (int nf = 0; nf < NT; nf++)
+                        acc[nf] = mfma16(as_bf16x8(a[s][j]),
+                                         mx_dequant8(codes[s][nf][j], e8m0_to_f32((sc[s][nf] >> (8 * j)) & 0xFFu)),
+                                         acc[nf]);
+            }
+        }
+    }
+
+#pragma unroll
+    for (int nf = 0; nf < NT; nf++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int row = 4 * (lane >> 4) + i, col = (wn * NT + nf) * 16 + (lane & 15);
+            red[(wk * 16 + row) * BN + col] = acc[nf][i];
+        }
+    __syncthreads();
+
+    const OutDesc d = g.lo;
+    const int nthr = WAVE * WN * WK;
+    if (d.kind == OUT_GLU) {
+        constexpr int BO = BN / 2;
+        for (int idx = threadIdx.x; idx < 16 * BO; idx += nthr) {
+            const int row = idx / BO, oc = idx % BO;
+            const int rr = m0 + row;
+            if (rr >= m1)
+                continue;
+            const int gc = (oc / 16) * 32 + (oc % 16), uc = gc + 16;
+            float gs = 0.f, us = 0.f;
+#pragma unroll
+            for (int w = 0; w < WK; w++) {
+                gs += red[(w * 16 + row) * BN + gc];
+                us += red[(w * 16 + row) * BN + uc];
+            }
+            reinterpret_cast<uint16_t *>(d.ptr)[(int64_t)rr * d.ld + (n0 - d.col0) / 2 + oc] =
+                (uint16_t)f32_to_bf16_bits(silu_f32(gs) * us);
+        }
+    } else {
+        for (int idx = threadIdx.x; idx < 16 * BN; idx += nthr) {
+            const int row = idx / BN, col = idx % BN;
+            const int rr = m0 + row, n = n0 + col;
+            if (rr >= m1 || n >= d.n_valid)
+                continue;
+            float v = 0.f;
+#pragma unroll
+            for (int w = 0; w < WK; w++)
+                v += red[(w * 16 + row) * BN + col];
+            reinterpret_cast<uint16_t *>(d.ptr)[(int64_t)rr * d.ld + (n - d.col0)] = (uint16_t)f32_to_bf16_bits(v);
+        }
+    }
+}
+
+template <int NT, int WN, int WK, int MAXS>
+static hipError_t launch_stream(const GemmArgs &g, int max_tiles, hipStream_t st)
+{
+    constexpr int BN = 16 * NT * WN;
+    if (g.N % (16 * NT) != 0 || g.K % MX_STEP != 0 || !g.tiles)
+        return hipErrorInvalidValue;
+    if (max_tiles <= 0)
+        return hipSuccess;
+    if (max_tiles > 65535)
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL((mx_stream_kernel<NT, WN, WK, MAXS>), dim3((g.N + BN - 1) / BN, max_tiles),
+                       dim3(WAVE * WN * WK), 0, st, g);
+    return hipGetLastError();
+}
+
 template <int MT, int NT, int WK, bool MX>
 static hipError_t launch(const GemmArgs &g, int grid_m, hipStream_t st)
 {
@@ -171,7 +305,9 @@ static hipError_t launch(const GemmArgs &g, int grid_m, hipStream_t st)
         return hipErrorInvalidValue;
     if (grid_m <= 0)
         return hipSuccess;
-    hipLaunchKernelGGL((gemm_kernel<MT, NT, WK, MX>), dim3(grid_m, g.N / BN), dim3(WAVE * WK), 0, st, g);
+    if (grid_m > 65535)
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL((gemm_kernel<MT, NT, WK, MX>), dim3(g.N / BN, grid_m), dim3(WAVE * WK), 0, st, g);
     return hipGetLastError();
 }
 
@@ -195,7 +331,27 @@ hipError_t launch_gemm_grouped(const GemmArgs &g, GemmShape shape, int max_tiles
     case GEMM_MX_GLU_M16:
         return launch<1, 2, 4, true>(g, max_tiles, st);
     case GEMM_MX_M16_N64:
+        return launch_stream<4, 1, 1, 3>(g, max_tiles, st);
+    case GEMM_MX_GLU_M16_STEP:
+        return launch<1, 2, 4, true>(g, max_tiles, st);
+    case GEMM_MX_M16_N64_STEP:
         return launch<1, 4, 1, true>(g, max_tiles, st);
+    case GEMM_MX_GLU_M16_W7:
+        return launch_stream<2, 1, 7, 4>(g, max_tiles, st);
+    case GEMM_MX_GLU_M16_W14:
+        return launch_stream<2, 1, 14, 2>(g, max_tiles, st);
+    case GEMM_MX_DOWN_W1:
+        return launch_stream<4, 1, 1, 3>(g, max_tiles, st);
+    case GEMM_MX_DOWN_N2:
+        return launch_stream<2, 4, 1, 3>(g, max_tiles, st);
+    case GEMM_MX_GLU_STEP_W7:
+        return launch<1, 2, 7, true>(g, max_tiles, st);
+    case GEMM_MX_GLU_STEP_W2:
+        return launch<1, 2, 2, true>(g, max_tiles, st);
+    case GEMM_MX_DOWN_STEP_N2:
+        return launch<1, 2, 1, true>(g, max_tiles, st);
+    case GEMM_MX_DOWN_STEP_N8:
+        return launch<1, 8, 1, true>(g, max_tiles, st);
     default:
         return hipErrorInvalidValue;
     }

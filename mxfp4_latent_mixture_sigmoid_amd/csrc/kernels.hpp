@@ -2,6 +2,7 @@
 #pragma once
 
 #include "common.hpp"
+#include "wave.hpp"
 
 namespace mxmoe {
 
@@ -33,11 +34,19 @@ struct GemmArgs {
 enum GemmShape {
     GEMM_SKINNY_N16 = 0,     // dense, 64 rows x 16 columns per workgroup, K split over 8 waves
     GEMM_SKINNY_N32 = 1,     // dense, 64 rows x 32 columns (one GLU pair), K over 8 waves
-    GEMM_MX_GLU_M16 = 2,     // grouped MXFP4, 16 rows x (16 gate + 16 up), K over 4 waves
-    GEMM_MX_M16_N64 = 3,     // grouped MXFP4, 16 rows x 64 columns, one wave
+    GEMM_MX_GLU_M16 = 2,     // grouped MXFP4, 16 rows x (16 gate + 16 up), K over 4 waves, per-step loads
+    GEMM_MX_M16_N64 = 3,     // grouped MXFP4 stream, 16 rows x 64 columns, one wave
+    GEMM_MX_GLU_M16_STEP = 4,   // variants compared when tuning the stream shapes
+    GEMM_MX_M16_N64_STEP = 5,
+    GEMM_MX_GLU_M16_W7 = 6,
+    GEMM_MX_GLU_M16_W14 = 7,
+    GEMM_MX_DOWN_W1 = 8,
+    GEMM_MX_DOWN_N2 = 9,
+    GEMM_MX_GLU_STEP_W7 = 10,
+    GEMM_MX_GLU_STEP_W2 = 11,
+    GEMM_MX_DOWN_STEP_N2 = 12,
+    GEMM_MX_DOWN_STEP_N8 = 13,
 };
-
-constexpr int TILE_HEADER_INTS = 4;
 
 hipError_t launch_gemm_dense(const GemmArgs &g, GemmShape shape, hipStream_t st);
 hipError_t launch_gemm_grouped(const GemmArgs &g, GemmShape shape, int max_tiles, hipStream_t st);
@@ -56,9 +65,65 @@ hipError_t launch_pack_down(uint8_t *dst, const uint8_t *dc, const uint8_t *ds, 
 hipError_t launch_unpack_mx(const uint8_t *packed_expert, int64_t N, int64_t K, int interleave,
                             int which_half, uint16_t *out, hipStream_t st);
 
-// Routing.
+// Dense products for T <= SKINNY_MAX_M tokens: split-K FP32 partial tiles. The partials of one
+// split are stored per 16-column block nb in accumulator order, SKINNY_TILE_FLOATS floats each:
+// element (row, col) sits at skinny_partial_index(row, col) (rows padded to 64).
+constexpr int SKINNY_MAX_M = 64;
+constexpr int SKINNY_TILE_FLOATS = 4 * WAVE * 4;
+__host__ __device__ inline int64_t skinny_partial_index(int row, int col)
+{
+    const int mf = row / 16, r = row % 16;
+    const int lane = (r / 4) * 16 + col % 16;
+    return (int64_t)(col / 16) * SKINNY_TILE_FLOATS + (mf * WAVE + lane) * 4 + r % 4;
+}
+constexpr int SKINNY_CHUNK = BF16_CHUNK_STEPS * BF16_STEP;   // K per split (one packed K chunk)
+struct SkinnyArgs {
+    const uint16_t *A;   // [M, lda] BF16
+    int64_t lda;
+    int M;
+    const uint8_t *B;    // packed BF16 [N, K]
+    int N, K;
+    float *P;            // partials, split s at P + s * p_split_stride (>= N / 16 * SKINNY_TILE_FLOATS)
+    int64_t p_split_stride;
+};
+int skinny_splits(int K, int chunk_steps);
+hipError_t launch_skinny(const SkinnyArgs &g, int waves, int chunk_steps, hipStream_t st);
+hipError_t launch_skinny_persist(const SkinnyArgs &g, int waves, int groups, hipStream_t st);
+
+struct XsideEpiArgs {
+    const float *P;
+    int64_t p_split_stride;
+    int splits, M, N, Lt, shared_cols;   // N = Lt + shared_cols (2 S Is)
+    uint16_t *z;                         // [M, Lt]
+    uint16_t *acat;                      // [M, ldcat]; h_s written at columns Lt..
+    int64_t ldcat;
+    const int32_t *offsets;              // tile lists (workgroup 0)
+    int E, bm1, bm2;
+    int32_t *tiles1, *tiles2;
+};
+hipError_t launch_xside_epilogue(const XsideEpiArgs &e, hipStream_t st);
+hipError_t launch_out_epilogue(const float *P, int64_t split_stride, int splits, int M, int N, uint16_t *out,
+                               hipStream_t st);
+
+// Routing. Logits of token t: sum over `splits` of the partials (skinny_partial_index layout) when
+// `partials`, else src[t * ld + e]; plus bias[e] (nullable); written to logits_out [T, E] when
+// non-null.
+struct TopkArgs {
+    const float *src;
+    int64_t split_stride, ld;
+    int splits;
+    int partials;
+    const float *bias;
+    float *logits_out;
+    int T, E, K;
+    int32_t *ids;
+    float *w;
+};
 constexpr int PERM_TOKENS_PER_BLOCK = 32;
-hipError_t launch_topk(const float *logits, int T, int E, int K, int32_t *ids, float *w, hipStream_t st);
+constexpr int PERM_SMALL_MAX_T = 256;
+hipError_t launch_topk(const TopkArgs &a, hipStream_t st);
+hipError_t launch_permute_small(const int32_t *ids, int T, int K, int E, int32_t *counts, int32_t *offsets,
+                                int32_t *sorted_pairs, int32_t *inv, hipStream_t st);
 hipError_t launch_permute(const int32_t *ids, int T, int K, int E, int32_t *hist, int32_t *counts,
                           int32_t *offsets, int32_t *sorted_pairs, int32_t *inv, hipStream_t st);
 

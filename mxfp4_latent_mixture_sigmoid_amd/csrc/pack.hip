@@ -15,9 +15,10 @@ __global__ void pack_bf16_kernel(uint8_t *__restrict__ dst, int64_t N, int64_t K
         return;
     const int lane = (int)(chunk % WAVE);
     const int64_t blk = chunk / WAVE;
-    const int64_t n = (blk / kblocks) * 16 + (lane & 15);
-    const int64_t k = (blk % kblocks) * BF16_STEP + 8 * (lane >> 4);
-    *reinterpret_cast<u32x4_t *>(dst + chunk * 16) = fetch(n, k);
+    const int64_t nb = blk / kblocks, kb = blk % kblocks;
+    const int64_t n = nb * 16 + (lane & 15);
+    const int64_t k = kb * BF16_STEP + 8 * (lane >> 4);
+    *reinterpret_cast<u32x4_t *>(dst + bf16_block_index(nb, kb, N, K) * BF16_BLOCK_BYTES + lane * 16) = fetch(n, k);
 }
 
 struct FetchRouter {          // [E_pad, Hin]: router rows, zero rows past E

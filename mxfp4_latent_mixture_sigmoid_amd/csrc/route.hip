@@ -2,121 +2,176 @@
 // token/expert pairs by expert (histogram, per-expert scan, stable scatter).
 #include "kernels.hpp"
 
-#include <climits>
 
 namespace mxmoe {
 
-__device__ inline int wave_incl_scan(int v)
+// Order-preserving key of a float: unsigned comparison of keys equals the float comparison, with
+// -0 mapped to the key of +0 so the two compare equal. Every non-NaN value has a key > 0.
+__device__ inline uint32_t order_key(float f)
 {
-    const int lane = threadIdx.x & (WAVE - 1);
-#pragma unroll
-    for (int o = 1; o < WAVE; o <<= 1) {
-        const int t = __shfl_up(v, o);
-        if (lane >= o)
-            v += t;
-    }
-    return v;
+    uint32_t u = __float_as_uint(f);
+    if (u == 0x80000000u)
+        u = 0u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Exclusive prefix sum of one value per thread over the whole workgroup (blockDim <= 1024).
-// `sh` holds >= 16 ints of LDS. Returns the prefix; *total receives the workgroup sum.
-__device__ int block_excl_scan(int v, int *sh, int *total)
-{
-    const int lane = threadIdx.x & (WAVE - 1), wid = threadIdx.x / WAVE;
-    const int nw = (blockDim.x + WAVE - 1) / WAVE;
-    const int inc = wave_incl_scan(v);
-    if (lane == WAVE - 1)
-        sh[wid] = inc;
-    __syncthreads();
-    if (wid == 0) {
-        int x = lane < nw ? sh[lane] : 0;
-        x = wave_incl_scan(x);
-        if (lane < nw)
-            sh[lane] = x;
-    }
-    __syncthreads();
-    const int base = wid ? sh[wid - 1] : 0;
-    *total = sh[nw - 1];
-    __syncthreads();
-    return base + inc - v;
-}
+__device__ inline float key_value(uint32_t k) { return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k); }
 
-// Order used by the selection: larger logit first, equal logits by lower expert index.
-__device__ inline bool before(float va, int ia, float vb, int ib) { return va > vb || (va == vb && ia < ib); }
-
-// One wave per token. Each lane keeps the logits of experts lane, lane + 64, ...; K rounds of a
-// wave-wide arg-max pick the experts in rank order. Gate weights: sigmoid of the selected
-// logits, divided by their sum (a butterfly sum, bitwise identical in every lane).
+// One wave per token. Lane l keeps the keys of experts l, l + 64, ...; each of the K rounds takes
+// the wave-wide largest key (DPP reduction), resolves equal keys to the lowest expert index, and
+// retires the winner. Gate weights: sigmoid of the selected logits over their sum.
 template <int SLOTS>
-__global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ logits, int T, int E, int K,
-                                                   int32_t *__restrict__ ids, float *__restrict__ w)
+__global__ __launch_bounds__(256) void topk_kernel(const TopkArgs a)
 {
     const int lane = threadIdx.x & (WAVE - 1);
     const int t = blockIdx.x * 4 + threadIdx.x / WAVE;
-    if (t >= T)
+    if (t >= a.T)
         return;
-    const float *l = logits + (int64_t)t * E;
+    // Logits: partial sums added in split order, loads issued in batches of 4 splits x SLOTS.
+    const float *row = a.partials ? a.src : a.src + (int64_t)t * a.ld;
     float v[SLOTS];
-    int idx[SLOTS];
+#pragma unroll
+    for (int j = 0; j < SLOTS; j++)
+        v[j] = 0.f;
+    for (int s0 = 0; s0 < a.splits; s0 += 4) {
+        float tmp[4][SLOTS];
+#pragma unroll
+        for (int u = 0; u < 4; u++)
+#pragma unroll
+            for (int j = 0; j < SLOTS; j++)
+            {
+                const int e = min(lane + WAVE * j, a.E - 1);
+                tmp[u][j] = row[min(s0 + u, a.splits - 1) * a.split_stride +
+                                (a.partials ? skinny_partial_index(t, e) : (int64_t)e)];
+            }
+#pragma unroll
+        for (int u = 0; u < 4; u++)
+            if (s0 + u < a.splits)
+#pragma unroll
+                for (int j = 0; j < SLOTS; j++)
+                    v[j] += tmp[u][j];
+    }
+    uint32_t key[SLOTS];
 #pragma unroll
     for (int j = 0; j < SLOTS; j++) {
         const int e = lane + WAVE * j;
-        v[j] = e < E ? l[e] : -INFINITY;
-        idx[j] = e < E ? e : INT_MAX;
+        key[j] = 0u;
+        if (e < a.E) {
+            if (a.bias)
+                v[j] += a.bias[e];
+            if (a.logits_out)
+                a.logits_out[(int64_t)t * a.E + e] = v[j];
+            key[j] = order_key(v[j]);
+        }
     }
+    uint32_t my_key = 0u;
     int my_id = 0;
-    float my_v = 0.f;
-    for (int k = 0; k < K; k++) {
-        float bv = v[0];
-        int bi = idx[0];
+    for (int k = 0; k < a.K; k++) {
+        uint32_t bk = key[0];
+        int bj = 0;
 #pragma unroll
         for (int j = 1; j < SLOTS; j++)
-            if (before(v[j], idx[j], bv, bi)) {
-                bv = v[j];
-                bi = idx[j];
+            if (key[j] > bk) {
+                bk = key[j];
+                bj = j;
             }
-#pragma unroll
-        for (int o = WAVE / 2; o >= 1; o >>= 1) {
-            const float ov = __shfl_xor(bv, o);
-            const int oi = __shfl_xor(bi, o);
-            if (before(ov, oi, bv, bi)) {
-                bv = ov;
-                bi = oi;
-            }
+        const uint32_t wk = wave_max_u32(bk);
+        const unsigned long long hit = __ballot(bk == wk);
+        int win;
+        if (__popcll(hit) == 1) {
+            const int wl = __ffsll((long long)hit) - 1;
+            win = __builtin_amdgcn_readlane(bj, wl) * WAVE + wl;
+        } else {
+            win = (int)wave_min_u32(bk == wk ? (uint32_t)(bj * WAVE + lane) : 0xFFFFFFFFu);
         }
         if (lane == k) {
-            my_id = bi;
-            my_v = bv;
+            my_key = wk;
+            my_id = win;
         }
-        if ((bi & (WAVE - 1)) == lane) {
+        if (lane == (win & (WAVE - 1))) {
 #pragma unroll
             for (int j = 0; j < SLOTS; j++)
-                if (j == (bi / WAVE)) {
-                    v[j] = -INFINITY;
-                    idx[j] = INT_MAX;
-                }
+                if (j == win / WAVE)
+                    key[j] = 0u;
         }
     }
-    const float s = lane < K ? 1.0f / (1.0f + expf(-my_v)) : 0.0f;
-    float sum = s;
-#pragma unroll
-    for (int o = WAVE / 2; o >= 1; o >>= 1)
-        sum += __shfl_xor(sum, o);
-    if (lane < K) {
-        ids[(int64_t)t * K + lane] = my_id;
-        w[(int64_t)t * K + lane] = s / sum;
+    const float s = lane < a.K ? 1.0f / (1.0f + expf(-key_value(my_key))) : 0.0f;
+    const float sum = wave_sum_f32(s);
+    if (lane < a.K) {
+        a.ids[(int64_t)t * a.K + lane] = my_id;
+        a.w[(int64_t)t * a.K + lane] = s / sum;
     }
 }
 
-hipError_t launch_topk(const float *logits, int T, int E, int K, int32_t *ids, float *w, hipStream_t st)
+hipError_t launch_topk(const TopkArgs &a, hipStream_t st)
 {
-    const dim3 grid((T + 3) / 4);
-    if (E <= 2 * WAVE)
-        hipLaunchKernelGGL(topk_kernel<2>, grid, dim3(256), 0, st, logits, T, E, K, ids, w);
-    else if (E <= 16 * WAVE)
-        hipLaunchKernelGGL(topk_kernel<16>, grid, dim3(256), 0, st, logits, T, E, K, ids, w);
+    const dim3 grid((a.T + 3) / 4);
+    if (a.K > WAVE)
+        return hipErrorInvalidValue;
+    if (a.E <= 2 * WAVE)
+        hipLaunchKernelGGL(topk_kernel<2>, grid, dim3(256), 0, st, a);
+    else if (a.E <= 16 * WAVE)
+        hipLaunchKernelGGL(topk_kernel<16>, grid, dim3(256), 0, st, a);
     else
         return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+// Grouping by expert for T <= 256 tokens in one workgroup: a bit mask per expert marks the tokens
+// routed to it (the K experts of a token are distinct, so each (token, expert) bit is set once);
+// counts are popcounts, offsets their exclusive scan, and the position of pair (t, j) is
+// offsets[e] + the number of tokens before t in e's mask -- stable, with no ordering races.
+__global__ __launch_bounds__(1024) void perm_small_kernel(const int32_t *__restrict__ ids, int T, int K, int E,
+                                                          int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
+                                                          int32_t *__restrict__ sorted_pairs, int32_t *__restrict__ inv)
+{
+    extern __shared__ uint32_t masks[];               // [E][W] then off[E]
+    __shared__ int sh[16];
+    const int W = (T + 31) / 32;
+    int *off = reinterpret_cast<int *>(masks + E * W);
+    for (int i = threadIdx.x; i < E * W; i += blockDim.x)
+        masks[i] = 0u;
+    __syncthreads();
+    const int P = T * K;
+    for (int p = threadIdx.x; p < P; p += blockDim.x) {
+        const int t = p / K;
+        atomicOr(&masks[ids[p] * W + t / 32], 1u << (t & 31));
+    }
+    __syncthreads();
+    int c = 0;
+    if ((int)threadIdx.x < E)
+        for (int w = 0; w < W; w++)
+            c += __popc(masks[threadIdx.x * W + w]);
+    int total;
+    const int ex = block_excl_scan(c, sh, &total);
+    if ((int)threadIdx.x < E) {
+        counts[threadIdx.x] = c;
+        offsets[threadIdx.x] = ex;
+        off[threadIdx.x] = ex;
+    }
+    if (threadIdx.x == 0)
+        offsets[E] = total;
+    __syncthreads();
+    for (int p = threadIdx.x; p < P; p += blockDim.x) {
+        const int t = p / K, e = ids[p];
+        const uint32_t *m = masks + e * W;
+        int rank = __popc(m[t / 32] & ((1u << (t & 31)) - 1u));
+        for (int w = 0; w < t / 32; w++)
+            rank += __popc(m[w]);
+        const int pos = off[e] + rank;
+        sorted_pairs[pos] = p;
+        inv[p] = pos;
+    }
+}
+
+hipError_t launch_permute_small(const int32_t *ids, int T, int K, int E, int32_t *counts, int32_t *offsets,
+                                int32_t *sorted_pairs, int32_t *inv, hipStream_t st)
+{
+    if (T > PERM_SMALL_MAX_T || E > 1024)
+        return hipErrorInvalidValue;
+    const size_t lds = ((size_t)E * ((T + 31) / 32) + E) * sizeof(uint32_t);
+    hipLaunchKernelGGL(perm_small_kernel, dim3(1), dim3(1024), lds, st, ids, T, K, E, counts, offsets, sorted_pairs,
+                       inv);
     return hipGetLastError();
 }
 

@@ -1,0 +1,369 @@
+// skinny.hip -- dense BF16 products for a few tokens (T <= 64), where the weights must be streamed
+// from HBM exactly once at full bandwidth.
+//
+// The product C[T, N] = A[T, K] . B[N, K]^T is cut into (column group, K chunk) work items, enough
+// of them to occupy every CU. A workgroup first issues all of its weight loads (one 1 KiB fragment
+// block per wave and 32-wide K step, straight into registers), then stages its activation chunk
+// (T rows x chunk) in LDS once for all of its waves, and finally runs the 16x16x32 BF16 matrix-core
+// instructions. Each item writes an FP32 partial tile; the kernel that consumes the product sums the
+// partials of the K chunks in chunk order (fixed order: the result does not depend on scheduling)
+// and applies the epilogue: router logits (+bias) in the top-K kernel, z and the shared-expert GLU
+// in xside_epilogue_kernel, the final BF16 output in out_epilogue_kernel.
+#include "kernels.hpp"
+
+#include <algorithm>
+
+namespace mxmoe {
+
+
+// LDS holds the activation chunk in matrix-core operand order: for step s and 16-row fragment mf,
+// a 1 KiB block whose 16-byte lane slots are the operand of lane l (row mf*16 + l%16, inputs
+// s*32 + 8(l/16) .. +7). Operand reads are then one sequential 1 KiB per wave (no bank conflicts),
+// and the staging thread t of each 64 writes slot t of a block (sequential as well).
+template <int WAVES, int SK_MAX_STEPS>
+__global__ __launch_bounds__(WAVE *WAVES) void skinny_kernel(const SkinnyArgs g)
+{
+    extern __shared__ u32x4_t lds_a[];   // [nsteps][4 fragments][64 lanes]
+    const int lane = threadIdx.x & (WAVE - 1), wv = threadIdx.x / WAVE;
+    const int split = blockIdx.y;
+    const int kc0 = split * SK_MAX_STEPS * BF16_STEP;
+    const int nsteps = min(SK_MAX_STEPS * BF16_STEP, g.K - kc0) / BF16_STEP;
+    const int mt = (g.M + 15) / 16;
+    const int nb = blockIdx.x * WAVES + wv;           // this wave's 16-row block of B
+    const bool active = nb < g.N / 16;
+
+    // 1. Weight stream: every fragment of this wave's chunk, issued before anything waits (idle
+    //    waves re-read the last valid block; their result is never used). The empty asm with a
+    //    memory clobber keeps the compiler from sinking these loads below the LDS staging.
+    u32x4_t b[SK_MAX_STEPS];
+    {
+        const int nbc = min(nb, g.N / 16 - 1);
+        const uint8_t *bp = g.B + bf16_block_index(nbc, kc0 / BF16_STEP, g.N, g.K) * BF16_BLOCK_BYTES + lane * 16;
+#pragma unroll
+        for (int s = 0; s < SK_MAX_STEPS; s++)
+            b[s] = load16_nt(bp + min(s, nsteps - 1) * BF16_BLOCK_BYTES);
+    }
+    asm volatile("" ::: "memory");
+
+    // 2. Activation chunk -> registers (all loads in flight together) -> LDS in operand order,
+    //    rows >= M zero, shared by all waves of the workgroup.
+    constexpr int A_PER_THREAD = SK_MAX_STEPS * 4 * WAVE / (WAVE * WAVES);
+    u32x4_t av[A_PER_THREAD];
+#pragma unroll
+    for (int u = 0; u < A_PER_THREAD; u++) {
+        const int slot = threadIdx.x + u * WAVE * WAVES;        // block (slot / 64), lane slot % 64
+        const int blk = slot / WAVE, sl = slot % WAVE;
+        const int st = min(blk / 4, nsteps - 1), m = (blk % 4) * 16 + (sl & 15);
+        av[u] = load16(g.A + (int64_t)min(m, g.M - 1) * g.lda + kc0 + st * BF16_STEP + 8 * (sl >> 4));
+    }
+#pragma unroll
+    for (int u = 0; u < A_PER_THREAD; u++) {
+        const int slot = threadIdx.x + u * WAVE * WAVES;
+        const int blk = slot / WAVE, sl = slot % WAVE;
+        const int m = (blk % 4) * 16 + (sl & 15);
+        if (blk / 4 < nsteps && (blk % 4) < mt)
+            lds_a[slot] = m < g.M ? av[u] : u32x4_t{0u, 0u, 0u, 0u};
+    }
+    __syncthreads();
+    if (!active)
+        return;
+
+    // 3. Matrix-core products over the chunk: per step, all A fragments from LDS, then the MFMAs.
+    f32x4_t acc[4];
+#pragma unroll
+    for (int mf = 0; mf < 4; mf++)
+        acc[mf] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < SK_MAX_STEPS; s++) {
+        if (s < nsteps) {
+            u32x4_t a[4];
+#pragma unroll
+            for (int mf = 0; mf < 4; mf++)
+                a[mf] = lds_a[(s * 4 + mf) * WAVE + lane];
+#pragma unroll
+            for (int mf = 0; mf < 4; mf++)
+                if (mf < mt)
+                    acc[mf] = mfma16(as_bf16x8(a[mf]), as_bf16x8(b[s]), acc[mf]);
+        }
+    }
+
+    // 4. FP32 partial tile of this K chunk in accumulator order (see skinny_partial_index): each
+    //    lane stores its four values of a fragment as one 16-byte store, a wave 1 KiB contiguous.
+    float *P = g.P + (int64_t)split * g.p_split_stride + (int64_t)nb * SKINNY_TILE_FLOATS;
+#pragma unroll
+    for (int mf = 0; mf < 4; mf++)
+        if (mf < mt)
+            *reinterpret_cast<f32x4_t *>(P + (mf * WAVE + lane) * 4) = acc[mf];
+}
+
+// Persistent variant: workgroup w owns K split (w % splits) and the 16-row weight blocks
+// nb = (w / splits) * WAVES + wave + j * (groups * WAVES), j = 0, 1, ... where groups = gridDim.x /
+// splits. The activation chunk of its split is staged in LDS once; each wave then streams its blocks
+// with the next block's 16 fragments loaded while the current block is multiplied.
+template <int WAVES>
+__global__ __launch_bounds__(WAVE *WAVES) void skinny_persist_kernel(const SkinnyArgs g, int splits)
+{
+    constexpr int STEPS = 16;
+    extern __shared__ u32x4_t lds_a[];   // [nsteps][4 fragments][64 lanes]
+    const int lane = threadIdx.x & (WAVE - 1), wv = threadIdx.x / WAVE;
+    const int split = blockIdx.x % splits, grp = blockIdx.x / splits;
+    const int groups = gridDim.x / splits;
+    const int kc0 = split * STEPS * BF16_STEP;
+    const int nsteps = min(STEPS * BF16_STEP, g.K - kc0) / BF16_STEP;
+    const int mt = (g.M + 15) / 16;
+    const int nblocks = g.N / 16;
+    const int stride = groups * WAVES;
+    int nb = grp * WAVES + wv;
+
+    auto load_b = [&](int blk, u32x4_t *b) {
+        const int nbc = min(blk, nblocks - 1);
+        const uint8_t *bp = g.B + bf16_block_index(nbc, kc0 / BF16_STEP, g.N, g.K) * BF16_BLOCK_BYTES + lane * 16;
+#pragma unroll
+        for (int s = 0; s < STEPS; s++)
+            b[s] = load16_nt(bp + min(s, nsteps - 1) * BF16_BLOCK_BYTES);
+    };
+    u32x4_t b0[STEPS], b1[STEPS];
+    load_b(nb, b0);
+    asm volatile("" ::: "memory");
+
+    constexpr int A_PER_THREAD = STEPS * 4 * WAVE / (WAVE * WAVES);
+    {
+        u32x4_t av[A_PER_THREAD];
+#pragma unroll
+        for (int u = 0; u < A_PER_THREAD; u++) {
+            const int slot = threadIdx.x + u * WAVE * WAVES;
+            const int blk = slot / WAVE, sl = slot % WAVE;
+            const int st = min(blk / 4, nsteps - 1), m = (blk % 4) * 16 + (sl & 15);
+            av[u] = load16(g.A + (int64_t)min(m, g.M - 1) * g.lda + kc0 + st * BF16_STEP + 8 * (sl >> 4));
+        }
+#pragma unroll
+        for (int u = 0; u < A_PER_THREAD; u++) {
+            const int slot = threadIdx.x + u * WAVE * WAVES;
+            const int blk = slot / WAVE, sl = slot % WAVE;
+            const int m = (blk % 4) * 16 + (sl & 15);
+            if (blk / 4 < nsteps && (blk % 4) < mt)
+                lds_a[slot] = m < g.M ? av[u] : u32x4_t{0u, 0u, 0u, 0u};
+        }
+    }
+    __syncthreads();
+
+    auto compute_store = [&](int blk, const u32x4_t *b) {
+        f32x4_t acc[4];
+#pragma unroll
+        for (int mf = 0; mf < 4; mf++)
+            acc[mf] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < STEPS; s++) {
+            if (s < nsteps) {
+                u32x4_t a[4];
+#pragma unroll
+                for (int mf = 0; mf < 4; mf++)
+                    a[mf] = lds_a[(s * 4 + mf) * WAVE + lane];
+#pragma unroll
+                for (int mf = 0; mf < 4; mf++)
+                    if (mf < mt)
+                        acc[mf] = mfma16(as_bf16x8(a[mf]), as_bf16x8(b[s]), acc[mf]);
+            }
+        }
+        float *P = g.P + (int64_t)split * g.p_split_stride + (int64_t)blk * SKINNY_TILE_FLOATS;
+#pragma unroll
+        for (int mf = 0; mf < 4; mf++)
+            if (mf < mt)
+                *reinterpret_cast<f32x4_t *>(P + (mf * WAVE + lane) * 4) = acc[mf];
+    };
+
+    // Two blocks per iteration, ping-ponging the register buffers.
+    while (nb < nblocks) {
+        const int nb1 = nb + stride;
+        if (nb1 < nblocks)
+            load_b(nb1, b1);
+        compute_store(nb, b0);
+        if (nb1 >= nblocks)
+            break;
+        const int nb2 = nb1 + stride;
+        if (nb2 < nblocks)
+            load_b(nb2, b0);
+        compute_store(nb1, b1);
+        nb = nb2;
+    }
+}
+
+hipError_t launch_skinny_persist(const SkinnyArgs &g, int waves, int groups, hipStream_t st)
+{
+    if (g.M < 1 || g.M > SKINNY_MAX_M || g.N % 16 || g.K % BF16_STEP || groups < 1)
+        return hipErrorInvalidValue;
+    const int splits = skinny_splits(g.K, 16);
+    const int steps = std::min(16 * BF16_STEP, g.K) / BF16_STEP;
+    const size_t lds = (size_t)steps * 4 * WAVE * 16;
+    const dim3 grid(splits * groups);
+    if (waves == 4)
+        hipLaunchKernelGGL(skinny_persist_kernel<4>, grid, dim3(WAVE * 4), lds, st, g, splits);
+    else if (waves == 8)
+        hipLaunchKernelGGL(skinny_persist_kernel<8>, grid, dim3(WAVE * 8), lds, st, g, splits);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+int skinny_splits(int K, int chunk_steps)
+{
+    const int chunk = chunk_steps * BF16_STEP;
+    return (K + chunk - 1) / chunk;
+}
+
+// chunk_steps (8 or 16) sets the K range of a split: a half packed chunk keeps the weight range of a
+// workgroup contiguous and halves its LDS, letting more workgroups share a CU.
+hipError_t launch_skinny(const SkinnyArgs &g, int waves, int chunk_steps, hipStream_t st)
+{
+    if (g.M < 1 || g.M > SKINNY_MAX_M || g.N % 16 || g.K % BF16_STEP)
+        return hipErrorInvalidValue;
+    const int steps = std::min(chunk_steps * BF16_STEP, g.K) / BF16_STEP;
+    const size_t lds = (size_t)steps * 4 * WAVE * 16;
+    const dim3 grid((g.N / 16 + waves - 1) / waves, skinny_splits(g.K, chunk_steps));
+#define MOE_SKINNY(W, S)                                                                                              \
+    if (waves == W && chunk_steps == S) {                                                                             \
+        hipLaunchKernelGGL((skinny_kernel<W, S>), grid, dim3(WAVE * W), lds, st, g);                                   \
+        return hipGetLastError();                                                                                     \
+    }
+    MOE_SKINNY(4, 16)
+    MOE_SKINNY(8, 16)
+    MOE_SKINNY(4, 8)
+    MOE_SKINNY(8, 8)
+#undef MOE_SKINNY
+    return hipErrorInvalidValue;
+}
+
+// Sum of the K-chunk partials of one element, in chunk order; loads are issued in batches of
+// SUM_BATCH (addresses clamped, so every load is valid) before any of them is used.
+constexpr int SUM_BATCH = 8;
+__device__ inline float sum_partials(const float *P, int64_t split_stride, int splits, int64_t idx)
+{
+    float v = 0.f;
+    for (int s0 = 0; s0 < splits; s0 += SUM_BATCH) {
+        float t[SUM_BATCH];
+#pragma unroll
+        for (int u = 0; u < SUM_BATCH; u++)
+            t[u] = P[min(s0 + u, splits - 1) * split_stride + idx];
+#pragma unroll
+        for (int u = 0; u < SUM_BATCH; u++)
+            if (s0 + u < splits)
+                v += t[u];
+    }
+    return v;
+}
+
+// Sum over the splits of one lane's 16-byte partial slot (four rows of one column), split order.
+__device__ inline f32x4_t sum_slot(const float *slot, int64_t split_stride, int splits)
+{
+    f32x4_t v = {0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < splits; s0 += SUM_BATCH) {
+        f32x4_t t[SUM_BATCH];
+#pragma unroll
+        for (int u = 0; u < SUM_BATCH; u++)
+            t[u] = *reinterpret_cast<const f32x4_t *>(slot + min(s0 + u, splits - 1) * split_stride);
+#pragma unroll
+        for (int u = 0; u < SUM_BATCH; u++)
+            if (s0 + u < splits)
+                v += t[u];
+    }
+    return v;
+}
+
+// x-side epilogue. Thread (nb, mf, lane) owns rows mf*16 + 4(lane/16) .. +3 of column
+// nb*16 + lane%16: z = bf16(sum) for the latent blocks; for a shared-expert pair of blocks (16
+// gate columns, then the matching 16 up columns) the thread of the gate block forms
+// h_s = bf16(silu(gate) * up). The last workgroup builds the expert tile lists instead.
+__global__ __launch_bounds__(1024) void xside_epilogue_kernel(const XsideEpiArgs e)
+{
+    if (blockIdx.x == gridDim.x - 1) {
+        __shared__ int sh[16];
+        write_tiles(e.offsets, e.E, e.bm1, e.tiles1, sh);
+        write_tiles(e.offsets, e.E, e.bm2, e.tiles2, sh);
+        return;
+    }
+    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int lane = (int)(gid % WAVE);
+    const int64_t frag = gid / WAVE;
+    const int mf = (int)(frag % 4);
+    const int nbz = e.Lt / 16, npairs = e.shared_cols / 32;
+    const int64_t unit = frag / 4;                           // latent block, then shared pair
+    if (unit >= nbz + npairs || mf * 16 >= e.M)
+        return;
+    const int col16 = lane & 15, r0 = mf * 16 + 4 * (lane >> 4);
+    if (unit < nbz) {
+        const f32x4_t v = sum_slot(e.P + (unit * 4 + mf) * (int64_t)SKINNY_TILE_FLOATS / 4 + lane * 4,
+                                   e.p_split_stride, e.splits);
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+            if (r0 + i < e.M)
+                e.z[(int64_t)(r0 + i) * e.Lt + unit * 16 + col16] = (uint16_t)f32_to_bf16_bits(v[i]);
+    } else {
+        const int pr = (int)(unit - nbz);
+        const int64_t gb = nbz + 2 * pr;                     // gate block; up block is gb + 1
+        const f32x4_t gv = sum_slot(e.P + (gb * 4 + mf) * (int64_t)SKINNY_TILE_FLOATS / 4 + lane * 4,
+                                    e.p_split_stride, e.splits);
+        const f32x4_t uv = sum_slot(e.P + ((gb + 1) * 4 + mf) * (int64_t)SKINNY_TILE_FLOATS / 4 + lane * 4,
+                                    e.p_split_stride, e.splits);
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+            if (r0 + i < e.M)
+                e.acat[(int64_t)(r0 + i) * e.ldcat + e.Lt + pr * 16 + col16] =
+                    (uint16_t)f32_to_bf16_bits(silu_f32(gv[i]) * uv[i]);
+    }
+}
+
+hipError_t launch_xside_epilogue(const XsideEpiArgs &e, hipStream_t st)
+{
+    if (e.E > 1024)
+        return hipErrorInvalidValue;
+    const int64_t threads = (int64_t)(e.Lt / 16 + e.shared_cols / 32) * 4 * WAVE;
+    const unsigned blocks = 1 + (unsigned)((threads + 1023) / 1024);
+    hipLaunchKernelGGL(xside_epilogue_kernel, dim3(blocks), dim3(1024), 0, st, e);
+    return hipGetLastError();
+}
+
+// out = bf16(sum of partials). Thread (row quad q, column c) of a 64 x 16 tile reads the four
+// values of rows 4q..4q+3 as one 16-byte load per split and writes the four BF16 results.
+__global__ __launch_bounds__(256) void out_epilogue_kernel(const float *__restrict__ P, int64_t split_stride,
+                                                           int splits, int M, int N, uint16_t *__restrict__ out)
+{
+    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;   // (nb, mf, lane)
+    const int lane = (int)(gid % WAVE);
+    const int64_t frag = gid / WAVE;
+    const int mf = (int)(frag % 4);
+    const int64_t nb = frag / 4;
+    if (nb >= N / 16 || mf * 16 >= M)
+        return;
+    const float *src = P + gid * 4;
+    f32x4_t v = {0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < splits; s0 += SUM_BATCH) {
+        f32x4_t t[SUM_BATCH];
+#pragma unroll
+        for (int u = 0; u < SUM_BATCH; u++)
+            t[u] = *reinterpret_cast<const f32x4_t *>(src + min(s0 + u, splits - 1) * split_stride);
+#pragma unroll
+        for (int u = 0; u < SUM_BATCH; u++)
+            if (s0 + u < splits)
+                v += t[u];
+    }
+    const int col = (int)nb * 16 + (lane & 15);
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const int row = mf * 16 + 4 * (lane >> 4) + i;
+        if (row < M)
+            out[(int64_t)row * N + col] = (uint16_t)f32_to_bf16_bits(v[i]);
+    }
+}
+
+hipError_t launch_out_epilogue(const float *P, int64_t split_stride, int splits, int M, int N, uint16_t *out,
+                               hipStream_t st)
+{
+    if (N % 16 || M < 1 || M > SKINNY_MAX_M)
+        return hipErrorInvalidValue;
+    const int64_t threads = (int64_t)(N / 16) * 4 * WAVE;
+    const unsigned blocks = (unsigned)((threads + 255) / 256);
+    hipLaunchKernelGGL(out_epilogue_kernel, dim3(blocks), dim3(256), 0, st, P, split_stride, splits, M, N, out);
+    return hipGetLastError();
+}
+
+} // namespace mxmoe

@@ -17,40 +17,14 @@ __device__ inline uint32_t order_key(float f)
 
 __device__ inline float key_value(uint32_t k) { return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k); }
 
-// One wave per token. Lane l keeps the keys of experts l, l + 64, ...; each of the K rounds takes
-// the wave-wide largest key (DPP reduction), resolves equal keys to the lowest expert index, and
-// retires the winner. Gate weights: sigmoid of the selected logits over their sum.
+// Top-K of one token by one wave. Lane l holds the logits of experts l, l + 64, ... in v[]; each of
+// the K rounds takes the wave-wide largest key (DPP reduction), resolves equal keys to the lowest
+// expert index, and retires the winner. Gate weights: sigmoid of the selected logits over their
+// sum. Writes logits_out (if set), ids and w of token t.
 template <int SLOTS>
-__global__ __launch_bounds__(256) void topk_kernel(const TopkArgs a)
+__device__ inline void select_token(const TopkArgs &a, int t, float *v)
 {
     const int lane = threadIdx.x & (WAVE - 1);
-    const int t = blockIdx.x * 4 + threadIdx.x / WAVE;
-    if (t >= a.T)
-        return;
-    // Logits: partial sums added in split order, loads issued in batches of 4 splits x SLOTS.
-    const float *row = a.partials ? a.src : a.src + (int64_t)t * a.ld;
-    float v[SLOTS];
-#pragma unroll
-    for (int j = 0; j < SLOTS; j++)
-        v[j] = 0.f;
-    for (int s0 = 0; s0 < a.splits; s0 += 4) {
-        float tmp[4][SLOTS];
-#pragma unroll
-        for (int u = 0; u < 4; u++)
-#pragma unroll
-            for (int j = 0; j < SLOTS; j++)
-            {
-                const int e = min(lane + WAVE * j, a.E - 1);
-                tmp[u][j] = row[min(s0 + u, a.splits - 1) * a.split_stride +
-                                (a.partials ? skinny_partial_index(t, e) : (int64_t)e)];
-            }
-#pragma unroll
-        for (int u = 0; u < 4; u++)
-            if (s0 + u < a.splits)
-#pragma unroll
-                for (int j = 0; j < SLOTS; j++)
-                    v[j] += tmp[u][j];
-    }
     uint32_t key[SLOTS];
 #pragma unroll
     for (int j = 0; j < SLOTS; j++) {
@@ -103,17 +77,87 @@ __global__ __launch_bounds__(256) void topk_kernel(const TopkArgs a)
     }
 }
 
+// Logits given row by row (src[t * ld + e]): one wave per token.
+template <int SLOTS>
+__global__ __launch_bounds__(256) void topk_kernel(const TopkArgs a)
+{
+    const int lane = threadIdx.x & (WAVE - 1);
+    const int t = blockIdx.x * 4 + threadIdx.x / WAVE;
+    if (t >= a.T)
+        return;
+    float v[SLOTS];
+#pragma unroll
+    for (int j = 0; j < SLOTS; j++)
+        v[j] = a.src[(int64_t)t * a.ld + min(lane + WAVE * j, a.E - 1)];
+    select_token<SLOTS>(a, t, v);
+}
+
+// Logits as split-K partial tiles (accumulator order): the 16-byte slot of an expert holds four
+// consecutive tokens, so one workgroup takes tokens 4 b .. 4 b + 3. Wave w sums the splits
+// w, w + 4, ... of every expert into LDS; each wave then adds the four sums (in wave order) for
+// its own token and selects.
+template <int SLOTS>
+__global__ __launch_bounds__(256) void topk_partials_kernel(const TopkArgs a)
+{
+    extern __shared__ f32x4_t red[];                 // [4 waves][SLOTS * 64 experts]
+    const int lane = threadIdx.x & (WAVE - 1), wv = threadIdx.x / WAVE;
+    const int t0 = blockIdx.x * 4;
+    const int mf = t0 / 16, quad = (t0 % 16) / 4;
+    f32x4_t acc[SLOTS];
+#pragma unroll
+    for (int j = 0; j < SLOTS; j++)
+        acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int s0 = wv; s0 < a.splits; s0 += 8) {      // two splits per batch: w + 8 i and w + 4 + 8 i
+        f32x4_t ta[SLOTS], tb[SLOTS];
+        const int sa = s0, sb = min(s0 + 4, a.splits - 1);
+#pragma unroll
+        for (int j = 0; j < SLOTS; j++) {
+            const int e = min(lane + WAVE * j, a.E - 1);
+            const int64_t off = (int64_t)(e / 16) * SKINNY_TILE_FLOATS + (mf * WAVE + quad * 16 + e % 16) * 4;
+            ta[j] = *reinterpret_cast<const f32x4_t *>(a.src + sa * a.split_stride + off);
+            tb[j] = *reinterpret_cast<const f32x4_t *>(a.src + sb * a.split_stride + off);
+        }
+#pragma unroll
+        for (int j = 0; j < SLOTS; j++) {
+            acc[j] += ta[j];
+            if (s0 + 4 < a.splits)
+                acc[j] += tb[j];
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < SLOTS; j++)
+        red[wv * SLOTS * WAVE + j * WAVE + lane] = acc[j];
+    __syncthreads();
+    const int t = t0 + wv;
+    if (t >= a.T)
+        return;
+    float v[SLOTS];
+#pragma unroll
+    for (int j = 0; j < SLOTS; j++) {
+        const int i = j * WAVE + lane;
+        v[j] = ((red[i][wv] + red[SLOTS * WAVE + i][wv]) + red[2 * SLOTS * WAVE + i][wv]) +
+               red[3 * SLOTS * WAVE + i][wv];
+    }
+    select_token<SLOTS>(a, t, v);
+}
+
 hipError_t launch_topk(const TopkArgs &a, hipStream_t st)
 {
     const dim3 grid((a.T + 3) / 4);
-    if (a.K > WAVE)
+    if (a.K > WAVE || a.E > 16 * WAVE || (a.partials && a.T > SKINNY_MAX_M))
         return hipErrorInvalidValue;
-    if (a.E <= 2 * WAVE)
+    const bool small = a.E <= 2 * WAVE;
+    if (a.partials) {
+        const size_t lds = 4 * (small ? 2 : 16) * WAVE * sizeof(f32x4_t);
+        if (small)
+            hipLaunchKernelGGL(topk_partials_kernel<2>, grid, dim3(256), lds, st, a);
+        else
+            hipLaunchKernelGGL(topk_partials_kernel<16>, grid, dim3(256), lds, st, a);
+    } else if (small) {
         hipLaunchKernelGGL(topk_kernel<2>, grid, dim3(256), 0, st, a);
-    else if (a.E <= 16 * WAVE)
+    } else {
         hipLaunchKernelGGL(topk_kernel<16>, grid, dim3(256), 0, st, a);
-    else
-        return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 

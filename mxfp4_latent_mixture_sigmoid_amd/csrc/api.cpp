@@ -28,8 +28,12 @@ struct moe_handle {
 namespace {
 
 constexpr int64_t ALIGN = 256;
-constexpr int BM_GEMM1 = 16;   // rows per tile of the gate/up product
-constexpr int BM_GEMM2 = 16;   // rows per tile of the down product
+// Expert products: 16-row streaming tiles while experts see few rows (decode), 128-row matrix-core
+// tiles once they average TILED_MIN_ROWS rows or more (prefill).
+constexpr int BM_STREAM = 16;
+constexpr int TILED_MIN_ROWS = 32;
+bool tiled_experts(const moe_config *c, int64_t T) { return T * c->top_k >= (int64_t)TILED_MIN_ROWS * c->n_experts; }
+int expert_bm(const moe_config *c, int64_t T) { return tiled_experts(c, T) ? tiled_rows(TILED_128x512) : BM_STREAM; }
 constexpr int SKINNY_STEPS = 16; // 32-wide K steps per split of the few-token dense products
 
 int64_t align_up(int64_t v) { return (v + ALIGN - 1) / ALIGN * ALIGN; }
@@ -105,8 +109,8 @@ WsLayout ws_layout(const moe_config *c, int64_t T)
     const int64_t E = c->n_experts, K = c->top_k, Lt = c->latent, I = c->inter;
     const int64_t S = c->n_shared, Is = c->shared_inter;
     const int64_t nb = (T + PERM_TOKENS_PER_BLOCK - 1) / PERM_TOKENS_PER_BLOCK;
-    L.max_tiles1 = max_tiles(T, K, E, BM_GEMM1);
-    L.max_tiles2 = max_tiles(T, K, E, BM_GEMM2);
+    L.max_tiles1 = max_tiles(T, K, E, expert_bm(c, T));
+    L.max_tiles2 = max_tiles(T, K, E, expert_bm(c, T));
     int64_t off = 0;
     L.logits = off;
     off = align_up(off + T * E * 4);
@@ -413,7 +417,7 @@ moe_status moe_route(moe_handle *h, const void *x, int32_t T, const float *logit
         g.K = h->Hin;
         g.split = INT_MAX;
         g.lo = OutDesc{OUT_F32, lg, E, 0, E, logit_bias};
-        MOE_LAUNCH(MOE_KERNEL_ROUTER, launch_gemm_dense(g, GEMM_SKINNY_N16, st));
+        MOE_LAUNCH(MOE_KERNEL_ROUTER, launch_tiled(g, TILED_128x512, false, 0, st));
         ta.src = lg;
     }
     MOE_LAUNCH(MOE_KERNEL_TOPK, launch_topk(ta, st));
@@ -460,12 +464,14 @@ moe_status moe_forward(moe_handle *h, const void *x, int32_t T, const moe_routin
 
     float *partials = reinterpret_cast<float *>(ws + W.partials);
     const int Nx = Lt + 2 * S * Is;
+    const bool tiled = tiled_experts(c, T);
+    const int bm = expert_bm(c, T);
     if (lat && T <= SKINNY_MAX_M) {   // z and h_s from split-K partials; the epilogue also builds the tile lists
         const int64_t pstride = (int64_t)(Nx / 16) * SKINNY_TILE_FLOATS;
         SkinnyArgs g{static_cast<const uint16_t *>(x), H, T, h->packed + h->off_xside, Nx, H, partials, pstride};
         MOE_LAUNCH(MOE_KERNEL_XSIDE, launch_skinny_persist(g, 8, 18, st));
         XsideEpiArgs ea{partials, pstride, skinny_splits(H, SKINNY_STEPS), T, Nx, Lt, 2 * S * Is, Z, Acat, ldcat,
-                        r->offsets, E, BM_GEMM1, BM_GEMM2, tiles1, tiles2};
+                        r->offsets, E, bm, bm, tiles1, tiles2};
         MOE_LAUNCH(MOE_KERNEL_XSIDE_EPI, launch_xside_epilogue(ea, st));
     } else {
         if (lat) {   // z = bf16(x W_down^T) and h_s = bf16(silu(x Wg_s^T) (x Wu_s^T)) in one pass over x
@@ -479,9 +485,9 @@ moe_status moe_forward(moe_handle *h, const void *x, int32_t T, const moe_routin
             g.split = Lt;
             g.lo = OutDesc{OUT_BF16, Z, Lt, 0, Lt, nullptr};
             g.hi = OutDesc{OUT_GLU, Acat + Lt, ldcat, Lt, INT_MAX, nullptr};
-            MOE_LAUNCH(MOE_KERNEL_XSIDE, launch_gemm_dense(g, GEMM_SKINNY_N32, st));
+            MOE_LAUNCH(MOE_KERNEL_XSIDE, launch_tiled(g, TILED_128x512, false, 0, st));
         }
-        MOE_LAUNCH(MOE_KERNEL_TILEMAP, launch_tilemap(r->offsets, E, BM_GEMM1, tiles1, BM_GEMM2, tiles2, st));
+        MOE_LAUNCH(MOE_KERNEL_TILEMAP, launch_tilemap(r->offsets, E, bm, tiles1, bm, tiles2, st));
     }
     {   // h = bf16(silu(z Wg_e^T) (z Wu_e^T)) for every pair, rows in expert-sorted order
         GemmArgs g{};
@@ -496,7 +502,8 @@ moe_status moe_forward(moe_handle *h, const void *x, int32_t T, const moe_routin
         g.tiles = tiles1;
         g.split = INT_MAX;
         g.lo = OutDesc{OUT_GLU, Hb, I, 0, INT_MAX, nullptr};
-        MOE_LAUNCH(MOE_KERNEL_GATEUP, launch_gemm_grouped(g, GEMM_MX_GLU_M16, (int)W.max_tiles1, st));
+        MOE_LAUNCH(MOE_KERNEL_GATEUP, tiled ? launch_tiled(g, TILED_128x512, true, (int)W.max_tiles1, st)
+                                            : launch_gemm_grouped(g, GEMM_MX_GLU_M16, (int)W.max_tiles1, st));
     }
     {   // y = bf16(h Wd_e^T), unweighted, expert-sorted rows
         GemmArgs g{};
@@ -509,7 +516,8 @@ moe_status moe_forward(moe_handle *h, const void *x, int32_t T, const moe_routin
         g.tiles = tiles2;
         g.split = INT_MAX;
         g.lo = OutDesc{OUT_BF16, Yb, Lt, 0, Lt, nullptr};
-        MOE_LAUNCH(MOE_KERNEL_DOWN, launch_gemm_grouped(g, GEMM_MX_M16_N64, (int)W.max_tiles2, st));
+        MOE_LAUNCH(MOE_KERNEL_DOWN, tiled ? launch_tiled(g, TILED_128x512, true, (int)W.max_tiles2, st)
+                                          : launch_gemm_grouped(g, GEMM_MX_M16_N64, (int)W.max_tiles2, st));
     }
     // zc = bf16(sum_j w_j y_j) in slot order: into the first Lt columns of [zc | h_s], or the output
     MOE_LAUNCH(MOE_KERNEL_COMBINE, launch_combine(Yb, Lt, r->inv, r->topk_w, T, K, lat ? Acat : static_cast<uint16_t *>(out),
@@ -530,7 +538,7 @@ moe_status moe_forward(moe_handle *h, const void *x, int32_t T, const moe_routin
         g.K = ldcat;
         g.split = INT_MAX;
         g.lo = OutDesc{OUT_BF16, out, H, 0, H, nullptr};
-        MOE_LAUNCH(MOE_KERNEL_OUT, launch_gemm_dense(g, GEMM_SKINNY_N16, st));
+        MOE_LAUNCH(MOE_KERNEL_OUT, launch_tiled(g, TILED_128x512, false, 0, st));
     }
     return MOE_OK;
 }

@@ -317,6 +317,39 @@ void or_experts(const uint16_t *z, int64_t T, int64_t Lt, const int32_t *ids, in
     }
 }
 
+/* O7b. The down half of O7 on given h: y_p = bf16(h_p . Wd_e^T) for every pair p with e = ids[p].
+ * h [T*K, I] bf16 by pair id; y [T*K, Lt]. (Used to check a down product on its own inputs.) */
+void or_expert_down(const uint16_t *h, int64_t T, int64_t K, int64_t I, int64_t Lt, const int32_t *ids,
+                    const uint8_t *down_codes, const uint8_t *down_scales, uint16_t *y_out)
+{
+    const int64_t dcb = Lt * (I / 2), dsb = Lt * (I / 32);
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t p = 0; p < T * K; p++) {
+        const int64_t e = ids[p];
+        for (int64_t n = 0; n < Lt; n++) {
+            double acc = 0.0;
+            for (int64_t j = 0; j < I; j++)
+                acc += or_bf16_to_double(h[p * I + j]) * mx_elem(down_codes + e * dcb, down_scales + e * dsb, I, n, j);
+            y_out[p * Lt + n] = or_double_to_bf16(acc);
+        }
+    }
+}
+
+/* O9b. The down half of O9 on given h_s: ys[t] = sum_s h_s[t] . Wd_s^T (FP64, not rounded).
+ * hs [T, S*Is] bf16; sd [S,H,Is]; ys [T,H]. */
+void or_shared_down(const uint16_t *hs, int64_t T, int64_t S, int64_t Is, const uint16_t *sd, int64_t H, double *ys)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; t++)
+        for (int64_t n = 0; n < H; n++) {
+            double acc = 0.0;
+            for (int64_t s = 0; s < S; s++)
+                for (int64_t j = 0; j < Is; j++)
+                    acc += or_bf16_to_double(hs[t * S * Is + s * Is + j]) * or_bf16_to_double(sd[(s * H + n) * Is + j]);
+            ys[t * H + n] = acc;
+        }
+}
+
 /* O8. Gate-weighted combine in slot order: zc[t] = bf16(sum_j w[t,j] * y[t*K + j]).
  * y [T*K, Lt] by pair id; w [T,K]; zc [T,Lt]. */
 void or_combine(const uint16_t *y, const double *w, int64_t T, int64_t K, int64_t Lt, uint16_t *zc)

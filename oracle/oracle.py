@@ -59,6 +59,8 @@ def lib():
             "or_experts": (None, [P, I64, I64, P, I64, I64, P, P, P, P, P, P, P, P]),
             "or_combine": (None, [P, P, I64, I64, I64, P]),
             "or_num_threads": (ctypes.c_int, []),
+            "or_expert_down": (None, [P, I64, I64, I64, I64, P, P, P, P]),
+            "or_shared_down": (None, [P, I64, I64, I64, P, I64, P]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -208,6 +210,30 @@ def experts(z, ids, gate_codes, gate_scales, up_codes, up_scales, down_codes, do
     y = np.empty((T * K, Lt), np.uint16)
     lib().or_experts(_p(z), T, Lt, _p(ids), K, I, *[_p(a) for a in arrs], _p(h), _p(y))
     return h, y
+
+
+def expert_down(h, ids, down_codes, down_scales) -> np.ndarray:
+    """y by pair id from given h (pair order) -- the down half of `experts`."""
+    h = _c(h, np.uint16)
+    ids = _c(ids, np.int32)
+    T, K = ids.shape
+    I = h.shape[1]
+    Lt = down_codes.shape[1]
+    dc, ds = _c(down_codes, np.uint8), _c(down_scales, np.uint8)
+    y = np.empty((T * K, Lt), np.uint16)
+    lib().or_expert_down(_p(h), T, K, I, Lt, _p(ids), _p(dc), _p(ds), _p(y))
+    return y
+
+
+def shared_down(hs, sh_down) -> np.ndarray:
+    """sum over shared experts of h_s . Wd_s^T (FP64) from given h_s -- the down half of `shared`."""
+    hs = _c(hs, np.uint16)
+    sd = _c(sh_down, np.uint16)
+    T = hs.shape[0]
+    S, H, Is = sd.shape
+    ys = np.empty((T, H), np.float64)
+    lib().or_shared_down(_p(hs), T, S, Is, _p(sd), H, _p(ys))
+    return ys
 
 
 def combine(y, w) -> np.ndarray:

@@ -19,7 +19,11 @@ pytestmark = pytest.mark.gpu
 MID = LayerShape("mid", 200, 1024, 512, 64, 8, 256, 2, 128, True, "uniform", 0.0, 7)
 MID_ZIPF = LayerShape("mid_zipf", 300, 1024, 512, 96, 6, 256, 1, 256, True, "zipf", 0.0, 8)
 NOLAT = LayerShape("nolat", 77, 512, 512, 32, 4, 256, 0, 0, False, "uniform", 0.0, 9)
-SMALL_SHAPES = {s.name: s for s in (SHAPES["tiny"], MID, MID_ZIPF, NOLAT)}
+# Many rows per expert (300 * 4 / 16 = 75 on average, Zipf-skewed): the matrix-core tiled path for
+# the dense and the grouped products, with ragged row tiles and empty experts.
+PREFILL_SMALL = LayerShape("prefill_small", 300, 1024, 512, 16, 4, 256, 1, 128, True, "zipf", 0.0, 12)
+NOLAT_TILED = LayerShape("nolat_tiled", 260, 384, 384, 8, 3, 384, 0, 0, False, "uniform", 0.0, 13)
+SMALL_SHAPES = {s.name: s for s in (SHAPES["tiny"], MID, MID_ZIPF, NOLAT, PREFILL_SMALL, NOLAT_TILED)}
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -75,8 +79,8 @@ def test_forward_parity(name):
     G.log(f"[forward] {name}")
     run = G.GpuRun(layer, shape, inp)
     G.check_forward(shape, inp, run)
-    if shape.routing == "zipf":
-        assert np.sum(run.counts == 0) > 0, "skewed routing should leave experts empty"
+    if shape.routing == "zipf" and shape.E >= 64:
+        assert np.sum(run.counts == 0) > 0, "skewed routing over many experts should leave some empty"
 
 
 @pytest.mark.parametrize("name", ["tiny", "mid"])

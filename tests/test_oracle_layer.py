@@ -129,3 +129,14 @@ def test_unit_scales_integer_exact():
     g = (zi @ gc.T) / 32.0
     u = (zi @ uc.T) / 32.0
     _close_bf16(h, R.bf16_rne(g * scipy.special.expit(g) * u))
+
+
+def test_split_halves_equal_whole_steps():
+    # The down halves evaluated on the whole steps' own intermediates reproduce them bitwise.
+    s = replace(SHAPES["tiny"], T=12, S=2)
+    inp = make_inputs(s)
+    r = O.forward(inp, K=s.K)
+    y = O.expert_down(r["h"], r["ids"], inp["down_codes"], inp["down_scales"])
+    assert np.array_equal(y, r["y"])
+    ys = O.shared_down(r["hs"], inp["sh_down"])
+    assert np.array_equal(ys, r["ys"])

@@ -516,8 +516,9 @@ moe_status moe_forward(moe_handle *h, const void *x, int32_t T, const moe_routin
         g.tiles = tiles2;
         g.split = INT_MAX;
         g.lo = OutDesc{OUT_BF16, Yb, Lt, 0, Lt, nullptr};
-        MOE_LAUNCH(MOE_KERNEL_DOWN, tiled ? launch_tiled(g, TILED_128x512, true, (int)W.max_tiles2, st)
-                                          : launch_gemm_grouped(g, GEMM_MX_M16_N64, (int)W.max_tiles2, st));
+        MOE_LAUNCH(MOE_KERNEL_DOWN, !tiled ? launch_gemm_grouped(g, GEMM_MX_M16_N64, (int)W.max_tiles2, st)
+                                    : astat_supported(g) ? launch_astat(g, (int)W.max_tiles2, st)
+                                                         : launch_tiled(g, TILED_128x512, true, (int)W.max_tiles2, st));
     }
     // zc = bf16(sum_j w_j y_j) in slot order: into the first Lt columns of [zc | h_s], or the output
     MOE_LAUNCH(MOE_KERNEL_COMBINE, launch_combine(Yb, Lt, r->inv, r->topk_w, T, K, lat ? Acat : static_cast<uint16_t *>(out),

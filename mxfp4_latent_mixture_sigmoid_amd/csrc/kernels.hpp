@@ -58,6 +58,10 @@ enum TiledShape {
 int tiled_rows(TiledShape shape);
 // Dense (g.tiles null: rows 0..M-1) or grouped (tile list, `max_tiles` launch rows).
 hipError_t launch_tiled(const GemmArgs &g, TiledShape shape, bool mx, int max_tiles, hipStream_t st);
+// A-stationary grouped MXFP4 product for K <= AS_MAX_K (tile list required, BF16 output only).
+constexpr int AS_MAX_K = 512;
+bool astat_supported(const GemmArgs &g);
+hipError_t launch_astat(const GemmArgs &g, int max_tiles, hipStream_t st);
 hipError_t launch_gemm_grouped(const GemmArgs &g, GemmShape shape, int max_tiles, hipStream_t st);
 
 // Packing (moe_create) and unpacking (test hook).

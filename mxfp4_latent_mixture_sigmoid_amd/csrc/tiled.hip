@@ -15,6 +15,8 @@
 // skipped by whole waves; K needs only be a multiple of 32 (BF16) or 128 (MXFP4).
 #include "kernels.hpp"
 
+#include <algorithm>
+
 namespace mxmoe {
 
 constexpr int TL_WAVE_M = 128, TL_WAVE_N = 64;
@@ -32,7 +34,8 @@ __global__ __launch_bounds__(WAVE * 4) void tiled_kernel(const GemmArgs g)
     constexpr int PER_THREAD = SLOTS / (WAVE * 4);
     __shared__ u32x4_t lds[2][SLOTS];
 
-    const int lane = threadIdx.x & (WAVE - 1), wv = threadIdx.x / WAVE;
+    const int lane = threadIdx.x & (WAVE - 1);
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE);   // wave-uniform
     const int wm = wv / WN, wn = wv % WN;
 
     int group = 0, m0, m1;
@@ -97,24 +100,45 @@ __global__ __launch_bounds__(WAVE * 4) void tiled_kernel(const GemmArgs g)
     __syncthreads();
 
     const bool wave_active = n0 < g.N;
+    // B of this wave, prefetched ahead of use: MXFP4 one stage (128 inputs) ahead, BF16 one 32-wide
+    // step ahead (across stage boundaries). Past-the-end prefetches re-read the last valid block.
+    const int ks = g.K / BF16_STEP;
+    const int kblk = g.K / MX_STEP;
+    auto load_mx = [&](int stage, u32x4_t *codes, uint32_t *sc) {
+#pragma unroll
+        for (int nf = 0; nf < TL_NF; nf++) {
+            const int nb = min(n0 / 16 + nf, nblocks - 1);
+            const uint8_t *p = Bg + ((int64_t)nb * kblk + min(stage, kblk - 1)) * MX_BLOCK_BYTES;
+            codes[nf] = load16_nt(p + lane * 16);
+            sc[nf] = load4_nt(p + MX_CODE_BYTES + 4 * (lane & 15));
+        }
+    };
+    auto load_b = [&](int kstep, u32x4_t *b) {
+#pragma unroll
+        for (int nf = 0; nf < TL_NF; nf++) {
+            const int nb = min(n0 / 16 + nf, nblocks - 1);
+            b[nf] = load16_nt(Bg + bf16_block_index(nb, min(kstep, ks - 1), g.N, g.K) * BF16_BLOCK_BYTES + lane * 16);
+        }
+    };
+    // The stage loop is one basic block: waves past N multiply clamped (valid) B and store nothing,
+    // and the last stage re-stages a clamped valid A stage, so no value crosses a branch.
+    u32x4_t bcur[TL_NF];
+    uint32_t sccur[TL_NF];
+    if constexpr (MX)
+        load_mx(0, bcur, sccur);
+    else
+        load_b(0, bcur);
+
     for (int st = 0; st < nstages; st++) {
         const int cur = st & 1;
         u32x4_t an[PER_THREAD];
-        if (st + 1 < nstages)
-            load_a(st + 1, an);
+        load_a(min(st + 1, nstages - 1), an);
 
-        if (wave_active) {
+        {
             if constexpr (MX) {
-                const int kb = st;                               // one MX block per stage
-                u32x4_t codes[TL_NF];
-                uint32_t sc[TL_NF];
-#pragma unroll
-                for (int nf = 0; nf < TL_NF; nf++) {
-                    const int nb = min(n0 / 16 + nf, nblocks - 1);
-                    const uint8_t *p = Bg + ((int64_t)nb * (g.K / MX_STEP) + kb) * MX_BLOCK_BYTES;
-                    codes[nf] = load16_nt(p + lane * 16);
-                    sc[nf] = load4_nt(p + MX_CODE_BYTES + 4 * (lane & 15));
-                }
+                u32x4_t bnx[TL_NF];
+                uint32_t scnx[TL_NF];
+                load_mx(st + 1, bnx, scnx);
 #pragma unroll
                 for (int s = 0; s < TL_SUB; s++) {
                     u32x4_t a[TL_MF];
@@ -123,100 +147,125 @@ __global__ __launch_bounds__(WAVE * 4) void tiled_kernel(const GemmArgs g)
                         a[f] = lds[cur][(s * MFW + wm * TL_MF + f) * WAVE + lane];
 #pragma unroll
                     for (int nf = 0; nf < TL_NF; nf++) {
-                        if (!nval[nf])
-                            continue;
-                        const bf16x8_t b = mx_dequant8(codes[nf][s], e8m0_to_f32((sc[nf] >> (8 * s)) & 0xFFu));
+                        const bf16x8_t b = mx_dequant8(bcur[nf][s], e8m0_to_f32((sccur[nf] >> (8 * s)) & 0xFFu));
 #pragma unroll
                         for (int f = 0; f < TL_MF; f++)
-                            acc[f][nf] = mfma16(as_bf16x8(a[f]), b, acc[f][nf]);
+                            acc[f][nf] = mfma16(b, as_bf16x8(a[f]), acc[f][nf]);
                     }
+                    __builtin_amdgcn_sched_barrier(0);   // keep one sub-step's operands live at a time
+                }
+#pragma unroll
+                for (int nf = 0; nf < TL_NF; nf++) {
+                    bcur[nf] = bnx[nf];
+                    sccur[nf] = scnx[nf];
                 }
             } else {
-                const int ks = g.K / BF16_STEP;
-                u32x4_t bcur[TL_NF], bnext[TL_NF];
-                auto load_b = [&](int kstep, u32x4_t *b) {
-#pragma unroll
-                    for (int nf = 0; nf < TL_NF; nf++) {
-                        const int nb = min(n0 / 16 + nf, nblocks - 1);
-                        b[nf] = load16_nt(Bg + bf16_block_index(nb, min(kstep, ks - 1), g.N, g.K) * BF16_BLOCK_BYTES +
-                                          lane * 16);
-                    }
-                };
-                load_b(st * TL_SUB, bcur);
 #pragma unroll
                 for (int s = 0; s < TL_SUB; s++) {
                     const int kstep = st * TL_SUB + s;
-                    if (s + 1 < TL_SUB)
-                        load_b(kstep + 1, bnext);
+                    u32x4_t bnx[TL_NF];
+                    load_b(kstep + 1, bnx);
                     if (kstep < ks) {
                         u32x4_t a[TL_MF];
 #pragma unroll
                         for (int f = 0; f < TL_MF; f++)
                             a[f] = lds[cur][(s * MFW + wm * TL_MF + f) * WAVE + lane];
 #pragma unroll
-                        for (int nf = 0; nf < TL_NF; nf++) {
-                            if (!nval[nf])
-                                continue;
+                        for (int nf = 0; nf < TL_NF; nf++)
 #pragma unroll
                             for (int f = 0; f < TL_MF; f++)
-                                acc[f][nf] = mfma16(as_bf16x8(a[f]), as_bf16x8(bcur[nf]), acc[f][nf]);
-                        }
+                                acc[f][nf] = mfma16(as_bf16x8(bcur[nf]), as_bf16x8(a[f]), acc[f][nf]);
                     }
 #pragma unroll
                     for (int nf = 0; nf < TL_NF; nf++)
-                        bcur[nf] = bnext[nf];
+                        bcur[nf] = bnx[nf];
+                    __builtin_amdgcn_sched_barrier(0);
                 }
             }
         }
-        if (st + 1 < nstages) {
-            store_a(cur ^ 1, an);
-            __syncthreads();
-        }
+        store_a(cur ^ 1, an);
+        __syncthreads();
     }
 
     if (!wave_active)
         return;
-    // ---- epilogue: lane holds rows 4(l/16)+i of each fragment, column l % 16
+    // ---- epilogue. The weights are the first MFMA operand, so lane (q = l / 16, c = l % 16) of
+    // fragment (f, nf) holds token row f*16 + c and the four consecutive columns nf*16 + 4q + i:
+    // one 8-byte (BF16) or 16-byte (FP32) store per fragment when the output is aligned for it.
     const OutDesc d = (n0 < g.split) ? g.lo : g.hi;
-    const int rbase = m0 + wm * TL_WAVE_M + 4 * (lane >> 4);
+    const int q = lane >> 4;
+    const int rbase = m0 + wm * TL_WAVE_M + (lane & 15);
+    const bool vec = (d.ld % 4 == 0) && (d.col0 % 4 == 0) &&
+                     (reinterpret_cast<uintptr_t>(d.ptr) % (d.kind == OUT_F32 ? 16 : 8) == 0);
     if (d.kind == OUT_GLU) {
-        // fragments 2p (gate) and 2p+1 (up) hold the same 16 output columns
+        // fragments 2p (gate) and 2p+1 (up) hold the same output columns
         uint16_t *o = reinterpret_cast<uint16_t *>(d.ptr);
 #pragma unroll
         for (int p = 0; p < TL_NF / 2; p++) {
             if (!nval[2 * p + 1])
                 continue;
-            const int oc = (n0 - d.col0) / 2 + p * 16 + (lane & 15);
+            const int oc = (n0 - d.col0) / 2 + p * 16 + 4 * q;
 #pragma unroll
-            for (int f = 0; f < TL_MF; f++)
+            for (int f = 0; f < TL_MF; f++) {
+                const int r = rbase + f * 16;
+                if (r >= m1)
+                    continue;
+                uint32_t hv[4];
 #pragma unroll
-                for (int i = 0; i < 4; i++) {
-                    const int r = rbase + f * 16 + i;
-                    if (r < m1)
-                        o[(int64_t)r * d.ld + oc] =
-                            (uint16_t)f32_to_bf16_bits(silu_f32(acc[f][2 * p][i]) * acc[f][2 * p + 1][i]);
+                for (int i = 0; i < 4; i++)
+                    hv[i] = f32_to_bf16_bits(silu_f32(acc[f][2 * p][i]) * acc[f][2 * p + 1][i]);
+                uint16_t *dst = o + (int64_t)r * d.ld + oc;
+                if (vec) {
+                    *reinterpret_cast<uint2 *>(dst) = make_uint2(hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16));
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; i++)
+                        dst[i] = (uint16_t)hv[i];
                 }
+            }
         }
     } else {
 #pragma unroll
         for (int nf = 0; nf < TL_NF; nf++) {
-            const int n = n0 + nf * 16 + (lane & 15);
+            const int n = n0 + nf * 16 + 4 * q;                  // first of this lane's 4 columns
             if (!nval[nf] || n >= d.n_valid)
                 continue;
-            const float bias = (d.kind == OUT_F32 && d.bias) ? d.bias[n] : 0.f;
+            const bool full = vec && n + 3 < d.n_valid;
+            float bias[4] = {0.f, 0.f, 0.f, 0.f};
+            if (d.kind == OUT_F32 && d.bias)
 #pragma unroll
-            for (int f = 0; f < TL_MF; f++)
+                for (int i = 0; i < 4; i++)
+                    bias[i] = (n + i < d.n_valid) ? d.bias[n + i] : 0.f;
 #pragma unroll
-                for (int i = 0; i < 4; i++) {
-                    const int r = rbase + f * 16 + i;
-                    if (r >= m1)
-                        continue;
-                    if (d.kind == OUT_F32)
-                        reinterpret_cast<float *>(d.ptr)[(int64_t)r * d.ld + (n - d.col0)] = acc[f][nf][i] + bias;
-                    else
-                        reinterpret_cast<uint16_t *>(d.ptr)[(int64_t)r * d.ld + (n - d.col0)] =
-                            (uint16_t)f32_to_bf16_bits(acc[f][nf][i]);
+            for (int f = 0; f < TL_MF; f++) {
+                const int r = rbase + f * 16;
+                if (r >= m1)
+                    continue;
+                if (d.kind == OUT_F32) {
+                    float *dst = reinterpret_cast<float *>(d.ptr) + (int64_t)r * d.ld + (n - d.col0);
+                    if (full) {
+                        *reinterpret_cast<f32x4_t *>(dst) = f32x4_t{acc[f][nf][0] + bias[0], acc[f][nf][1] + bias[1],
+                                                                   acc[f][nf][2] + bias[2], acc[f][nf][3] + bias[3]};
+                    } else {
+#pragma unroll
+                        for (int i = 0; i < 4; i++)
+                            if (n + i < d.n_valid)
+                                dst[i] = acc[f][nf][i] + bias[i];
+                    }
+                } else {
+                    uint16_t *dst = reinterpret_cast<uint16_t *>(d.ptr) + (int64_t)r * d.ld + (n - d.col0);
+                    if (full) {
+                        *reinterpret_cast<uint2 *>(dst) =
+                            make_uint2(f32_to_bf16_bits(acc[f][nf][0]) | (f32_to_bf16_bits(acc[f][nf][1]) << 16),
+                                       f32_to_bf16_bits(acc[f][nf][2]) | (f32_to_bf16_bits(acc[f][nf][3]) << 16));
+                    } else {
+#pragma unroll
+                        for (int i = 0; i < 4; i++)
+                            if (n + i < d.n_valid)
+                                dst[i] = (uint16_t)f32_to_bf16_bits(acc[f][nf][i]);
+                    }
                 }
+            }
         }
     }
 }
@@ -233,6 +282,160 @@ static hipError_t launch_tiled_t(const GemmArgs &g, int grid_m, hipStream_t st)
         return hipErrorInvalidValue;
     hipLaunchKernelGGL((tiled_kernel<WM, WN, MX>), dim3((g.N + BN - 1) / BN, grid_m), dim3(WAVE * 4), 0, st, g);
     return hipGetLastError();
+}
+
+// ---- A-stationary grouped MXFP4 product for short K (the down projection, K = I <= 512).
+// The workgroup stages its whole 128-row A tile (gathered rows, 128 x K BF16, at most 128 KiB) into
+// LDS once, in the operand order above, with direct global->LDS loads (one wave instruction fills
+// one 1 KiB block), then walks its run of 256-column N blocks. Each wave owns 128 x 64 outputs per
+// block; its MXFP4 B for the next block is loaded while this block multiplies, and the block's
+// outputs leave as 8-byte stores (four consecutive columns per lane) before the next block starts.
+// Work is mapped XCD-major: the eight XCDs each take a contiguous run of the (tile, N-run) items
+// counted on the device, so the tiles of one expert share an L2.
+constexpr int AS_BM = 128, AS_BN = 256, AS_MF = 8, AS_NF = 4, AS_XCDS = 8;
+
+template <int KB>
+__global__ __launch_bounds__(WAVE * 4) void astat_kernel(const GemmArgs g, int nsplit)
+{
+    constexpr int KS = KB * TL_SUB;                              // 32-wide sub-steps
+    __shared__ u32x4_t lds[KS * AS_MF * WAVE];
+    const int lane = threadIdx.x & (WAVE - 1);
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE);
+
+    const int total = g.tiles[0] * nsplit;
+    const int per = (total + AS_XCDS - 1) / AS_XCDS;
+    const int slot = blockIdx.x / AS_XCDS;
+    const int item = (blockIdx.x % AS_XCDS) * per + slot;
+    if (slot >= per || item >= total)
+        return;
+    const int4 t = reinterpret_cast<const int4 *>(g.tiles + TILE_HEADER_INTS)[item / nsplit];
+    const int part = item % nsplit;
+    const int m0 = t.y, m1 = t.z;
+    const int nbn = (g.N + AS_BN - 1) / AS_BN;
+    const int j0 = part * nbn / nsplit, j1 = (part + 1) * nbn / nsplit;
+    if (j0 >= j1)
+        return;
+
+    // A tile -> LDS: block b = (s, f) holds lane l's operand (row f*16 + l%16, k = 32 s + 8 (l/16)).
+    for (int b = wv; b < KS * AS_MF; b += 4) {
+        const int s = b / AS_MF, f = b % AS_MF;
+        const int r = min(m0 + f * 16 + (lane & 15), m1 - 1);   // clamped valid row, never stored
+        const int64_t row = g.a_index ? (int64_t)(g.a_index[r] / g.a_div) : (int64_t)r;
+        __builtin_amdgcn_global_load_lds(g.A + row * g.lda + s * 32 + 8 * (lane >> 4),
+                                         (__attribute__((address_space(3))) void *)&lds[b * WAVE], 16, 0, 0);
+    }
+
+    const uint8_t *Bg = g.B + (int64_t)t.x * g.b_stride;
+    const int nbmax = g.N / 16 - 1;
+    auto load_block = [&](int j, u32x4_t (&codes)[AS_NF][KB], uint32_t (&sc)[AS_NF][KB]) {
+#pragma unroll
+        for (int nf = 0; nf < AS_NF; nf++) {
+            const int nb = min((j * AS_BN + wv * TL_WAVE_N) / 16 + nf, nbmax);
+#pragma unroll
+            for (int kb = 0; kb < KB; kb++) {
+                const uint8_t *p = Bg + ((int64_t)nb * KB + kb) * MX_BLOCK_BYTES;
+                codes[nf][kb] = load16_nt(p + lane * 16);
+                sc[nf][kb] = load4_nt(p + MX_CODE_BYTES + 4 * (lane & 15));
+            }
+        }
+    };
+    u32x4_t bc[AS_NF][KB];
+    uint32_t bs[AS_NF][KB];
+    load_block(j0, bc, bs);
+    __builtin_amdgcn_s_waitcnt(0);                               // A tile (and first B) have landed
+    __syncthreads();
+
+    const OutDesc d = g.lo;
+    const int q = lane >> 4;
+    uint16_t *out = reinterpret_cast<uint16_t *>(d.ptr);
+    for (int j = j0; j < j1; j++) {
+        u32x4_t bn[AS_NF][KB];
+        uint32_t bsn[AS_NF][KB];
+        load_block(min(j + 1, j1 - 1), bn, bsn);
+        f32x4_t acc[AS_MF][AS_NF];
+#pragma unroll
+        for (int f = 0; f < AS_MF; f++)
+#pragma unroll
+            for (int nf = 0; nf < AS_NF; nf++)
+                acc[f][nf] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < KB; kb++)
+#pragma unroll
+            for (int s = 0; s < TL_SUB; s++) {
+                u32x4_t a[AS_MF];
+#pragma unroll
+                for (int f = 0; f < AS_MF; f++)
+                    a[f] = lds[((kb * TL_SUB + s) * AS_MF + f) * WAVE + lane];
+#pragma unroll
+                for (int nf = 0; nf < AS_NF; nf++) {
+                    const bf16x8_t b = mx_dequant8(bc[nf][kb][s], e8m0_to_f32((bs[nf][kb] >> (8 * s)) & 0xFFu));
+#pragma unroll
+                    for (int f = 0; f < AS_MF; f++)
+                        acc[f][nf] = mfma16(b, as_bf16x8(a[f]), acc[f][nf]);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        // lane (q, c) of fragment (f, nf): row f*16 + c, columns nf*16 + 4q .. +3
+#pragma unroll
+        for (int nf = 0; nf < AS_NF; nf++) {
+            const int n = j * AS_BN + wv * TL_WAVE_N + nf * 16 + 4 * q;
+            if (n >= d.n_valid)
+                continue;
+#pragma unroll
+            for (int f = 0; f < AS_MF; f++) {
+                const int r = m0 + f * 16 + (lane & 15);
+                if (r < m1)
+                    *reinterpret_cast<uint2 *>(out + (int64_t)r * d.ld + n) =
+                        make_uint2(f32_to_bf16_bits(acc[f][nf][0]) | (f32_to_bf16_bits(acc[f][nf][1]) << 16),
+                                   f32_to_bf16_bits(acc[f][nf][2]) | (f32_to_bf16_bits(acc[f][nf][3]) << 16));
+            }
+        }
+#pragma unroll
+        for (int nf = 0; nf < AS_NF; nf++)
+#pragma unroll
+            for (int kb = 0; kb < KB; kb++) {
+                bc[nf][kb] = bn[nf][kb];
+                bs[nf][kb] = bsn[nf][kb];
+            }
+    }
+}
+
+template <int KB>
+static hipError_t launch_astat_t(const GemmArgs &g, int max_tiles, hipStream_t st)
+{
+    const int nbn = (g.N + AS_BN - 1) / AS_BN;
+    // enough (tile, N-run) items for ~8 rounds of 256 workgroups at the largest tile count
+    const int nsplit = std::max(1, std::min(nbn, (2048 + max_tiles - 1) / max_tiles));
+    const int64_t items = (int64_t)max_tiles * nsplit;
+    const int64_t grid = (items + AS_XCDS - 1) / AS_XCDS * AS_XCDS;
+    if (grid > INT32_MAX)
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL((astat_kernel<KB>), dim3((unsigned)grid), dim3(WAVE * 4), 0, st, g, nsplit);
+    return hipGetLastError();
+}
+
+bool astat_supported(const GemmArgs &g)
+{
+    const OutDesc &d = g.lo;
+    return g.tiles && g.K % MX_STEP == 0 && g.K >= MX_STEP && g.K <= AS_MAX_K && g.N % 16 == 0 && g.N > 0 &&
+           g.split >= g.N && d.kind == OUT_BF16 && d.col0 == 0 && d.n_valid <= g.N && d.n_valid % 4 == 0 &&
+           d.ld % 4 == 0 && reinterpret_cast<uintptr_t>(d.ptr) % 8 == 0 && g.lda % 8 == 0 &&
+           reinterpret_cast<uintptr_t>(g.A) % 16 == 0;
+}
+
+hipError_t launch_astat(const GemmArgs &g, int max_tiles, hipStream_t st)
+{
+    if (!astat_supported(g))
+        return hipErrorInvalidValue;
+    if (max_tiles <= 0)
+        return hipSuccess;
+    switch (g.K / MX_STEP) {
+    case 1: return launch_astat_t<1>(g, max_tiles, st);
+    case 2: return launch_astat_t<2>(g, max_tiles, st);
+    case 3: return launch_astat_t<3>(g, max_tiles, st);
+    case 4: return launch_astat_t<4>(g, max_tiles, st);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 int tiled_rows(TiledShape shape) { return shape == TILED_256x256 ? 256 : 128; }

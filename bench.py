@@ -26,11 +26,10 @@ HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0       # MI355X dense BF16 matrix cores
 MX_BYTES_PER_VALUE = 17 / 32    # E2M1 nibble + one E8M0 byte per 32 values
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-GEMM_SRC = os.path.join(ROOT, "mxfp4_latent_mixture_sigmoid_amd", "csrc", "gemm.hip")
 
 
-def kernel_source_hash() -> str:
-    with open(GEMM_SRC, "rb") as f:
+def source_hash(rel: str) -> str:
+    with open(os.path.join(ROOT, rel), "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
@@ -57,12 +56,13 @@ def algorithmic(shape, n_active: int) -> dict:
 
 
 def read_traffic(workload: str, kernel: str):
-    """HBM bytes per launch from committed PMC counters, or None once the kernel has changed."""
+    """HBM bytes per launch from committed PMC counters (FETCH_SIZE + WRITE_SIZE, each scaled by the
+    counter's reading for a copy of known size), or None once that kernel's source has changed."""
     try:
         with open(TRAFFIC_FILE) as f:
             d = json.load(f)
         e = d[workload][kernel]
-        if e.get("source_sha256_16") != kernel_source_hash():
+        if e.get("source_sha256_16") != source_hash(e["source"]):
             return None
         return float(e["bytes_per_launch"])
     except (OSError, KeyError, ValueError):

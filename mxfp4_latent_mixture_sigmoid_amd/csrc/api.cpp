@@ -33,7 +33,7 @@ constexpr int64_t ALIGN = 256;
 constexpr int BM_STREAM = 16;
 constexpr int TILED_MIN_ROWS = 32;
 bool tiled_experts(const moe_config *c, int64_t T) { return T * c->top_k >= (int64_t)TILED_MIN_ROWS * c->n_experts; }
-int expert_bm(const moe_config *c, int64_t T) { return tiled_experts(c, T) ? tiled_rows(TILED_128x512) : BM_STREAM; }
+int expert_bm(const moe_config *c, int64_t T) { return tiled_experts(c, T) ? TILED_BM : BM_STREAM; }
 constexpr int SKINNY_STEPS = 16; // 32-wide K steps per split of the few-token dense products
 
 int64_t align_up(int64_t v) { return (v + ALIGN - 1) / ALIGN * ALIGN; }
@@ -417,7 +417,7 @@ moe_status moe_route(moe_handle *h, const void *x, int32_t T, const float *logit
         g.K = h->Hin;
         g.split = INT_MAX;
         g.lo = OutDesc{OUT_F32, lg, E, 0, E, logit_bias};
-        MOE_LAUNCH(MOE_KERNEL_ROUTER, launch_tiled(g, TILED_128x512, false, 0, st));
+        MOE_LAUNCH(MOE_KERNEL_ROUTER, launch_tiled(g, false, 0, st));
         ta.src = lg;
     }
     MOE_LAUNCH(MOE_KERNEL_TOPK, launch_topk(ta, st));
@@ -485,7 +485,7 @@ moe_status moe_forward(moe_handle *h, const void *x, int32_t T, const moe_routin
             g.split = Lt;
             g.lo = OutDesc{OUT_BF16, Z, Lt, 0, Lt, nullptr};
             g.hi = OutDesc{OUT_GLU, Acat + Lt, ldcat, Lt, INT_MAX, nullptr};
-            MOE_LAUNCH(MOE_KERNEL_XSIDE, launch_tiled(g, TILED_128x512, false, 0, st));
+            MOE_LAUNCH(MOE_KERNEL_XSIDE, launch_tiled(g, false, 0, st));
         }
         MOE_LAUNCH(MOE_KERNEL_TILEMAP, launch_tilemap(r->offsets, E, bm, tiles1, bm, tiles2, st));
     }
@@ -502,7 +502,7 @@ moe_status moe_forward(moe_handle *h, const void *x, int32_t T, const moe_routin
         g.tiles = tiles1;
         g.split = INT_MAX;
         g.lo = OutDesc{OUT_GLU, Hb, I, 0, INT_MAX, nullptr};
-        MOE_LAUNCH(MOE_KERNEL_GATEUP, tiled ? launch_tiled(g, TILED_128x512, true, (int)W.max_tiles1, st)
+        MOE_LAUNCH(MOE_KERNEL_GATEUP, tiled ? launch_tiled(g, true, (int)W.max_tiles1, st)
                                             : launch_gemm_grouped(g, GEMM_MX_GLU_M16, (int)W.max_tiles1, st));
     }
     {   // y = bf16(h Wd_e^T), unweighted, expert-sorted rows
@@ -518,7 +518,7 @@ moe_status moe_forward(moe_handle *h, const void *x, int32_t T, const moe_routin
         g.lo = OutDesc{OUT_BF16, Yb, Lt, 0, Lt, nullptr};
         MOE_LAUNCH(MOE_KERNEL_DOWN, !tiled ? launch_gemm_grouped(g, GEMM_MX_M16_N64, (int)W.max_tiles2, st)
                                     : astat_supported(g) ? launch_astat(g, (int)W.max_tiles2, st)
-                                                         : launch_tiled(g, TILED_128x512, true, (int)W.max_tiles2, st));
+                                                         : launch_tiled(g, true, (int)W.max_tiles2, st));
     }
     // zc = bf16(sum_j w_j y_j) in slot order: into the first Lt columns of [zc | h_s], or the output
     MOE_LAUNCH(MOE_KERNEL_COMBINE, launch_combine(Yb, Lt, r->inv, r->topk_w, T, K, lat ? Acat : static_cast<uint16_t *>(out),
@@ -539,7 +539,7 @@ moe_status moe_forward(moe_handle *h, const void *x, int32_t T, const moe_routin
         g.K = ldcat;
         g.split = INT_MAX;
         g.lo = OutDesc{OUT_BF16, out, H, 0, H, nullptr};
-        MOE_LAUNCH(MOE_KERNEL_OUT, launch_tiled(g, TILED_128x512, false, 0, st));
+        MOE_LAUNCH(MOE_KERNEL_OUT, launch_tiled(g, false, 0, st));
     }
     return MOE_OK;
 }

@@ -51,13 +51,10 @@ enum GemmShape {
 hipError_t launch_gemm_dense(const GemmArgs &g, GemmShape shape, hipStream_t st);
 
 // Many-token products (tiled.hip): four waves of 128 x 128 outputs each.
-enum TiledShape {
-    TILED_128x512 = 0,   // 1 x 4 waves: 128 rows x 512 columns per workgroup
-    TILED_256x256 = 1,   // 2 x 2 waves: 256 rows x 256 columns
-};
-int tiled_rows(TiledShape shape);
-// Dense (g.tiles null: rows 0..M-1) or grouped (tile list, `max_tiles` launch rows).
-hipError_t launch_tiled(const GemmArgs &g, TiledShape shape, bool mx, int max_tiles, hipStream_t st);
+// Tiled matrix-core product for many rows: 128 x 256 outputs per workgroup.
+// Dense (g.tiles null: rows 0..M-1) or grouped (tile list, at most `max_tiles` entries).
+constexpr int TILED_BM = 128;
+hipError_t launch_tiled(const GemmArgs &g, bool mx, int max_tiles, hipStream_t st);
 // A-stationary grouped MXFP4 product for K <= AS_MAX_K (tile list required, BF16 output only).
 constexpr int AS_MAX_K = 512;
 bool astat_supported(const GemmArgs &g);

@@ -1,9 +1,9 @@
 // tiled.hip -- matrix-core GEMM for many tokens, C = A . B^T, where the time is BF16 MFMA work.
 //
 // Each of the four waves of a workgroup owns a 128 x 64 output tile (8 x 4 fragments of the
-// 16x16x32 BF16 instruction, 128 FP32 accumulators per lane), small enough for two waves per SIMD;
-// at the matrix-core peak this reads ~64 B/clk/CU from LDS and ~32 B/clk/CU from cache. The
-// workgroup is 1 x 4 waves (128 rows x 256 columns) or 2 x 2 waves (256 x 128).
+// 16x16x32 BF16 instruction, 128 FP32 accumulators per lane); the workgroup covers 128 rows x 256
+// columns. At the matrix-core peak this reads ~64 B/clk/CU from LDS and ~47 B/clk/CU (BF16 B) or
+// ~25 B/clk/CU (MXFP4 B) from cache.
 //  * A (activations, optionally gathered rows) is staged per 128-wide K stage into LDS in operand
 //    order -- for K sub-step s and 16-row fragment f, one 1 KiB block holding lane l's operand at
 //    slot l -- so the writes and the reads are sequential (no bank conflicts). Two LDS buffers
@@ -24,8 +24,36 @@ constexpr int TL_MF = TL_WAVE_M / 16, TL_NF = TL_WAVE_N / 16;   // 8 x 4 fragmen
 constexpr int TL_STAGE_K = 128;                                 // K per LDS stage
 constexpr int TL_SUB = TL_STAGE_K / 32;                         // 32-wide sub-steps per stage
 
+constexpr int TL_XCDS = 8;      // workgroups are dealt to the XCDs round-robin by linear id
+constexpr int TL_GROUP_M = 8;   // dense products: M tiles per group, walked M-fastest
+
+// Linear workgroup id -> (N tile, M tile or tile-list entry), XCD-major: XCD c takes the contiguous
+// run c*per .. c*per+per-1 of the work items, so the workgroups sharing one L2 also share operands.
+// Tile lists: items run tile-major (the N tiles of one tile, then the next tile of the same
+// expert). Dense: groups of TL_GROUP_M M tiles, M-fastest within a group. False past the end.
+__device__ inline bool tiled_item(const GemmArgs &g, int gx, int gy, int &bx, int &by)
+{
+    const int total = g.tiles ? g.tiles[0] * gx : gx * gy;
+    const int per = (total + TL_XCDS - 1) / TL_XCDS;
+    const int slot = blockIdx.x / TL_XCDS;
+    const int item = (blockIdx.x % TL_XCDS) * per + slot;
+    if (slot >= per || item >= total)
+        return false;
+    if (g.tiles) {
+        by = item / gx;
+        bx = item % gx;
+    } else {
+        const int first = item / (TL_GROUP_M * gx) * TL_GROUP_M;
+        const int rows = min(gy - first, TL_GROUP_M);
+        const int in = item - first * gx;
+        by = first + in % rows;
+        bx = in / rows;
+    }
+    return true;
+}
+
 template <int WM, int WN, bool MX>
-__global__ __launch_bounds__(WAVE * 4) void tiled_kernel(const GemmArgs g)
+__global__ __launch_bounds__(WAVE * 4) void tiled_kernel(const GemmArgs g, int gx, int gy)
 {
     static_assert(WM * WN == 4, "four waves");
     constexpr int BM = TL_WAVE_M * WM, BN = TL_WAVE_N * WN;
@@ -38,19 +66,20 @@ __global__ __launch_bounds__(WAVE * 4) void tiled_kernel(const GemmArgs g)
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE);   // wave-uniform
     const int wm = wv / WN, wn = wv % WN;
 
+    int bx, by;
+    if (!tiled_item(g, gx, gy, bx, by))
+        return;
     int group = 0, m0, m1;
     if (g.tiles) {
-        if ((int)blockIdx.y >= g.tiles[0])
-            return;
-        const int4 t = reinterpret_cast<const int4 *>(g.tiles + TILE_HEADER_INTS)[blockIdx.y];
+        const int4 t = reinterpret_cast<const int4 *>(g.tiles + TILE_HEADER_INTS)[by];
         group = t.x;
         m0 = t.y;
         m1 = t.z;
     } else {
-        m0 = blockIdx.y * BM;
+        m0 = by * BM;
         m1 = min(g.M, m0 + BM);
     }
-    const int n0 = blockIdx.x * BN + wn * TL_WAVE_N;            // this wave's first column
+    const int n0 = bx * BN + wn * TL_WAVE_N;                     // this wave's first column
     const int nblocks = g.N / 16;
     const uint8_t *Bg = g.B + (int64_t)group * g.b_stride;
 
@@ -270,17 +299,15 @@ __global__ __launch_bounds__(WAVE * 4) void tiled_kernel(const GemmArgs g)
     }
 }
 
-template <int WM, int WN, bool MX>
+template <bool MX>
 static hipError_t launch_tiled_t(const GemmArgs &g, int grid_m, hipStream_t st)
 {
-    constexpr int BN = TL_WAVE_N * WN;
-    if (g.N % 16 || g.K % (MX ? MX_STEP : BF16_STEP) || g.K < 8)
+    constexpr int BN = TL_WAVE_N * 4;
+    const int gx = (g.N + BN - 1) / BN;
+    const int64_t grid = ((int64_t)gx * grid_m + TL_XCDS - 1) / TL_XCDS * TL_XCDS;
+    if (grid > INT32_MAX)
         return hipErrorInvalidValue;
-    if (grid_m <= 0)
-        return hipSuccess;
-    if (grid_m > 65535)
-        return hipErrorInvalidValue;
-    hipLaunchKernelGGL((tiled_kernel<WM, WN, MX>), dim3((g.N + BN - 1) / BN, grid_m), dim3(WAVE * 4), 0, st, g);
+    hipLaunchKernelGGL((tiled_kernel<1, 4, MX>), dim3((unsigned)grid), dim3(WAVE * 4), 0, st, g, gx, grid_m);
     return hipGetLastError();
 }
 
@@ -438,17 +465,14 @@ hipError_t launch_astat(const GemmArgs &g, int max_tiles, hipStream_t st)
     }
 }
 
-int tiled_rows(TiledShape shape) { return shape == TILED_256x256 ? 256 : 128; }
-
-hipError_t launch_tiled(const GemmArgs &g, TiledShape shape, bool mx, int max_tiles, hipStream_t st)
+hipError_t launch_tiled(const GemmArgs &g, bool mx, int max_tiles, hipStream_t st)
 {
-    const int bm = tiled_rows(shape);
-    const int grid_m = g.tiles ? max_tiles : (g.M + bm - 1) / bm;
-    if (shape == TILED_128x512)
-        return mx ? launch_tiled_t<1, 4, true>(g, grid_m, st) : launch_tiled_t<1, 4, false>(g, grid_m, st);
-    if (shape == TILED_256x256)
-        return mx ? launch_tiled_t<2, 2, true>(g, grid_m, st) : launch_tiled_t<2, 2, false>(g, grid_m, st);
-    return hipErrorInvalidValue;
+    if (g.N % 16 || g.N <= 0 || g.K % (mx ? MX_STEP : BF16_STEP) || g.K <= 0)
+        return hipErrorInvalidValue;
+    const int grid_m = g.tiles ? max_tiles : (g.M + TILED_BM - 1) / TILED_BM;
+    if (grid_m <= 0)
+        return hipSuccess;
+    return mx ? launch_tiled_t<true>(g, grid_m, st) : launch_tiled_t<false>(g, grid_m, st);
 }
 
 } // namespace mxmoe

@@ -503,7 +503,8 @@ moe_status moe_forward(moe_handle *h, const void *x, int32_t T, const moe_routin
         g.split = INT_MAX;
         g.lo = OutDesc{OUT_GLU, Hb, I, 0, INT_MAX, nullptr};
         MOE_LAUNCH(MOE_KERNEL_GATEUP, tiled ? launch_tiled(g, true, (int)W.max_tiles1, st)
-                                            : launch_gemm_grouped(g, GEMM_MX_GLU_M16, (int)W.max_tiles1, st));
+                                            : launch_gemm_grouped(g, (2 * I) % 64 ? GEMM_MX_GLU_M16 : GEMM_MX_GLU_M16_N64,
+                                                                  (int)W.max_tiles1, st));
     }
     {   // y = bf16(h Wd_e^T), unweighted, expert-sorted rows
         GemmArgs g{};

@@ -17,8 +17,6 @@ __global__ __launch_bounds__(1024) void tilemap_kernel(const int32_t *__restrict
 hipError_t launch_tilemap(const int32_t *offsets, int E, int bm1, int32_t *tiles1, int bm2, int32_t *tiles2,
                           hipStream_t st)
 {
-    if (E > 1024)
-        return hipErrorInvalidValue;
     hipLaunchKernelGGL(tilemap_kernel, dim3(1), dim3(1024), 0, st, offsets, E, bm1, tiles1, bm2, tiles2);
     return hipGetLastError();
 }

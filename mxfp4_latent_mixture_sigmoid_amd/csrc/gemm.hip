@@ -332,26 +332,8 @@ hipError_t launch_gemm_grouped(const GemmArgs &g, GemmShape shape, int max_tiles
         return launch<1, 2, 4, true>(g, max_tiles, st);
     case GEMM_MX_M16_N64:
         return launch_stream<4, 1, 1, 3>(g, max_tiles, st);
-    case GEMM_MX_GLU_M16_STEP:
-        return launch<1, 2, 4, true>(g, max_tiles, st);
-    case GEMM_MX_M16_N64_STEP:
-        return launch<1, 4, 1, true>(g, max_tiles, st);
-    case GEMM_MX_GLU_M16_W7:
-        return launch_stream<2, 1, 7, 4>(g, max_tiles, st);
-    case GEMM_MX_GLU_M16_W14:
-        return launch_stream<2, 1, 14, 2>(g, max_tiles, st);
-    case GEMM_MX_DOWN_W1:
-        return launch_stream<4, 1, 1, 3>(g, max_tiles, st);
-    case GEMM_MX_DOWN_N2:
-        return launch_stream<2, 4, 1, 3>(g, max_tiles, st);
-    case GEMM_MX_GLU_STEP_W7:
-        return launch<1, 2, 7, true>(g, max_tiles, st);
-    case GEMM_MX_GLU_STEP_W2:
-        return launch<1, 2, 2, true>(g, max_tiles, st);
-    case GEMM_MX_DOWN_STEP_N2:
-        return launch<1, 2, 1, true>(g, max_tiles, st);
-    case GEMM_MX_DOWN_STEP_N8:
-        return launch<1, 8, 1, true>(g, max_tiles, st);
+    case GEMM_MX_GLU_M16_N64:
+        return launch<1, 4, 4, true>(g, max_tiles, st);
     default:
         return hipErrorInvalidValue;
     }

@@ -34,23 +34,13 @@ struct GemmArgs {
 enum GemmShape {
     GEMM_SKINNY_N16 = 0,     // dense, 64 rows x 16 columns per workgroup, K split over 8 waves
     GEMM_SKINNY_N32 = 1,     // dense, 64 rows x 32 columns (one GLU pair), K over 8 waves
-    GEMM_MX_GLU_M16 = 2,     // grouped MXFP4, 16 rows x (16 gate + 16 up), K over 4 waves, per-step loads
+    GEMM_MX_GLU_M16 = 2,     // grouped MXFP4, 16 rows x one (16 gate + 16 up) pair, K over 4 waves
     GEMM_MX_M16_N64 = 3,     // grouped MXFP4 stream, 16 rows x 64 columns, one wave
-    GEMM_MX_GLU_M16_STEP = 4,   // variants compared when tuning the stream shapes
-    GEMM_MX_M16_N64_STEP = 5,
-    GEMM_MX_GLU_M16_W7 = 6,
-    GEMM_MX_GLU_M16_W14 = 7,
-    GEMM_MX_DOWN_W1 = 8,
-    GEMM_MX_DOWN_N2 = 9,
-    GEMM_MX_GLU_STEP_W7 = 10,
-    GEMM_MX_GLU_STEP_W2 = 11,
-    GEMM_MX_DOWN_STEP_N2 = 12,
-    GEMM_MX_DOWN_STEP_N8 = 13,
+    GEMM_MX_GLU_M16_N64 = 4, // grouped MXFP4, 16 rows x two (gate, up) pairs, K over 4 waves, per-step loads
 };
 
 hipError_t launch_gemm_dense(const GemmArgs &g, GemmShape shape, hipStream_t st);
 
-// Many-token products (tiled.hip): four waves of 128 x 128 outputs each.
 // Tiled matrix-core product for many rows: 128 x 256 outputs per workgroup.
 // Dense (g.tiles null: rows 0..M-1) or grouped (tile list, at most `max_tiles` entries).
 constexpr int TILED_BM = 128;

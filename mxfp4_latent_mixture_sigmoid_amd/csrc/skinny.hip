@@ -273,7 +273,7 @@ __device__ inline f32x4_t sum_slot(const float *slot, int64_t split_stride, int 
 // nb*16 + lane%16: z = bf16(sum) for the latent blocks; for a shared-expert pair of blocks (16
 // gate columns, then the matching 16 up columns) the thread of the gate block forms
 // h_s = bf16(silu(gate) * up). The last workgroup builds the expert tile lists instead.
-__global__ __launch_bounds__(1024) void xside_epilogue_kernel(const XsideEpiArgs e)
+__global__ __launch_bounds__(256) void xside_epilogue_kernel(const XsideEpiArgs e)
 {
     if (blockIdx.x == gridDim.x - 1) {
         __shared__ int sh[16];
@@ -314,11 +314,9 @@ __global__ __launch_bounds__(1024) void xside_epilogue_kernel(const XsideEpiArgs
 
 hipError_t launch_xside_epilogue(const XsideEpiArgs &e, hipStream_t st)
 {
-    if (e.E > 1024)
-        return hipErrorInvalidValue;
     const int64_t threads = (int64_t)(e.Lt / 16 + e.shared_cols / 32) * 4 * WAVE;
-    const unsigned blocks = 1 + (unsigned)((threads + 1023) / 1024);
-    hipLaunchKernelGGL(xside_epilogue_kernel, dim3(blocks), dim3(1024), 0, st, e);
+    const unsigned blocks = 1 + (unsigned)((threads + 255) / 256);
+    hipLaunchKernelGGL(xside_epilogue_kernel, dim3(blocks), dim3(256), 0, st, e);
     return hipGetLastError();
 }
 

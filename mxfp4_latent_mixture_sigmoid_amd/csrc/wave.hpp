@@ -91,21 +91,32 @@ __device__ inline int block_excl_scan(int v, int *sh, int *total)
     return base + inc - v;
 }
 
-// Expert tile list for row tiles of `bm` rows (blockDim = 1024 >= E; every thread calls it).
-// Expert e with n_e rows gets ceil(n_e / bm) tiles of consecutive rows of the expert-sorted
-// order, listed expert by expert. Layout: tiles[0] = tile count, then from element
-// TILE_HEADER_INTS one int4 (expert, first row, end row, 0) per tile.
+// Expert tile list for row tiles of `bm` rows (every thread of the block calls it; thread i takes
+// the run of consecutive experts i*per .. i*per+per-1, per = ceil(E / blockDim)). Expert e with n_e
+// rows gets ceil(n_e / bm) tiles of consecutive rows of the expert-sorted order, listed expert by
+// expert. Layout: tiles[0] = tile count, then from element TILE_HEADER_INTS one int4 (expert,
+// first row, end row, 0) per tile.
 __device__ inline void write_tiles(const int32_t *offsets, int E, int bm, int32_t *tiles, int *sh)
 {
-    const int e = threadIdx.x;
-    const int beg = e < E ? offsets[e] : 0;
-    const int n = e < E ? offsets[e + 1] - beg : 0;
-    const int c = (n + bm - 1) / bm;
+    const int per = (E + (int)blockDim.x - 1) / (int)blockDim.x;
+    const int e0 = (int)threadIdx.x * per;
+    int c = 0;
+    for (int i = 0; i < per; i++) {
+        const int e = e0 + i;
+        if (e < E)
+            c += (offsets[e + 1] - offsets[e] + bm - 1) / bm;
+    }
     int total;
-    const int base = block_excl_scan(c, sh, &total);
+    int base = block_excl_scan(c, sh, &total);
     int4 *out = reinterpret_cast<int4 *>(tiles + TILE_HEADER_INTS);
-    for (int j = 0; j < c; j++)
-        out[base + j] = int4{e, beg + j * bm, min(beg + (j + 1) * bm, beg + n), 0};
+    for (int i = 0; i < per; i++) {
+        const int e = e0 + i;
+        if (e >= E)
+            break;
+        const int beg = offsets[e], n = offsets[e + 1] - beg;
+        for (int j = 0; j * bm < n; j++)
+            out[base++] = int4{e, beg + j * bm, min(beg + (j + 1) * bm, beg + n), 0};
+    }
     if (threadIdx.x == 0)
         tiles[0] = total;
 }

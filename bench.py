@@ -1,10 +1,12 @@
 #!/usr/bin/env python3
 """Throughput of the routed-expert forward of one MXFP4 Stable LatentMoE layer on one MI355X.
 
-One step = moe_route + moe_forward over one batch of seeded synthetic tokens (router, top-K,
-grouping by expert, latent down-projection and shared gate/up, MXFP4 gate/up and down expert
-products, gate-weighted combine, up-projection plus shared down-projection), all enqueued on one
-HIP stream with the inputs already resident in HBM. Prints one JSON line.
+One step = moe_route_forward over one batch of seeded synthetic tokens (router, top-K, grouping by
+expert, latent down-projection and shared gate/up, MXFP4 gate/up and down expert products,
+gate-weighted combine, up-projection plus shared down-projection) with the inputs already resident
+in HBM; the x-side products run on the library's second stream, concurrently with the routing, and
+the step is timed on the caller's stream, which waits for both. The same work as two calls
+(moe_route, then moe_forward, one stream) is timed too and reported beside it. Prints one JSON line.
 
 Default workload: one GPU's TP8 share of a Kimi K3 layer at decode size (64 tokens, hidden 7168,
 latent 3584, 896 experts top-16, expert intermediate 384, 2 shared experts).
@@ -85,7 +87,7 @@ def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="tp8_decode_t64")
     ap.add_argument("--cpu-sample", type=int, default=16, help="tokens the CPU oracle evaluates")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -133,6 +135,9 @@ def main() -> int:
     out = torch.empty(T, layer.H, dtype=torch.bfloat16, device="cuda")
 
     def step():
+        layer.route_forward(x, T, routing, out=out, logit_bias=bias)
+
+    def step_separate():
         layer.route(x, T, routing, logit_bias=bias)
         layer.forward(x, T, routing, out=out)
 
@@ -154,6 +159,16 @@ def main() -> int:
     gpu_ms = ev0.elapsed_time(ev1)
     ms_per_step = wall * 1e3 / args.steps
     print(f"[bench] timed {args.steps} steps: {ms_per_step:.4f} ms/step", file=sys.stderr, flush=True)
+
+    # The same work as two calls (moe_route, then moe_forward) on the one stream, for reference.
+    for _ in range(args.warmup):
+        step_separate()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step_separate()
+    torch.cuda.synchronize()
+    ms_separate = (time.perf_counter() - t0) * 1e3 / args.steps
 
     # Per-kernel durations from HIP events recorded around each launch on the same stream.
     n_launch = 16 * args.steps
@@ -214,6 +229,7 @@ def main() -> int:
         "roofline": roof,
         "cpu_baseline": cpu,
         "gpu_ms_per_step": round(gpu_ms / args.steps, 5),
+        "ms_per_step_route_then_forward": round(ms_separate, 5),
         "step_hbm_gbps": round(alg["step_bytes"] / step_s / 1e9, 1),
         "step_tflops": round(alg["step_flops"] / step_s / 1e12, 2),
         "kernels_us": kernels_us,

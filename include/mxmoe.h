@@ -20,8 +20,9 @@
  *  - Every pointer argument except the handle, the config and the structs themselves is DEVICE
  *    memory owned by the caller. The library never allocates device memory (no hipMalloc).
  *  - BF16 tensors are passed as 16-bit bit patterns, row-major, innermost dimension contiguous.
- *  - `stream` is a hipStream_t (NULL = the null stream). All device work is enqueued on it and
- *    the call returns without synchronising. Argument errors are reported synchronously before
+ *  - `stream` is a hipStream_t (NULL = the null stream). All device work is enqueued on it (the
+ *    x-side products of moe_route_forward may run on the handle's second stream, ordered between
+ *    the call's earlier and later work on `stream`) and the call returns without synchronising. Argument errors are reported synchronously before
  *    anything is enqueued; launch failures return MOE_ERR_HIP; device faults surface at the
  *    caller's next synchronisation. No C++ exception crosses this boundary.
  *  - Results are deterministic: identical inputs give bitwise-identical outputs (no
@@ -131,6 +132,19 @@ moe_status moe_route(moe_handle *h, const void *x, int32_t T, const float *logit
  * x. workspace: >= moe_query(cfg, T).workspace_bytes (may be the one given to moe_route). */
 moe_status moe_forward(moe_handle *h, const void *x, int32_t T, const moe_routing *r, void *out,
                        void *workspace, size_t workspace_bytes, void *stream);
+
+/* moe_route (with logits_in = NULL) followed by moe_forward, in one call, with results identical
+ * bit for bit to the two calls. With latent projections and more than 64 tokens, the x-side
+ * products (latent down-projection, shared gate/up), which do not depend on the routing, run on a
+ * second stream owned by the handle, concurrently with the top-K and grouping on `stream`;
+ * `stream` waits for both before the expert products, so all of the call's work is ordered after
+ * earlier work on `stream` and before later work on it. With 64 tokens or fewer everything runs
+ * on `stream` (the fork and join would cost more than they hide).
+ * Arguments as for the two calls; logits_out may be NULL and must not alias x or out. Calls on
+ * one handle must not overlap (they share its second stream). */
+moe_status moe_route_forward(moe_handle *h, const void *x, int32_t T, const float *logit_bias,
+                             float *logits_out, const moe_routing *r, void *out, void *workspace,
+                             size_t workspace_bytes, void *stream);
 
 /* Test hook: dequantise expert e's packed matrix `which` (0 gate [I, Lt], 1 up [I, Lt],
  * 2 down [Lt, I]) back to canonical row-major BF16 in `out` through the same in-register

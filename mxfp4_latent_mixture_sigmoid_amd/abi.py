@@ -58,6 +58,8 @@ SIGNATURES = {
                            ctypes.POINTER(c_vp)]),
     "moe_route": (c_i32, [c_vp, c_vp, c_i32, c_vp, c_vp, c_vp, ctypes.POINTER(MoeRouting), c_vp, c_size, c_vp]),
     "moe_forward": (c_i32, [c_vp, c_vp, c_i32, ctypes.POINTER(MoeRouting), c_vp, c_vp, c_size, c_vp]),
+    "moe_route_forward": (c_i32, [c_vp, c_vp, c_i32, c_vp, c_vp, ctypes.POINTER(MoeRouting), c_vp, c_vp, c_size,
+                                  c_vp]),
     "moe_unpack_expert": (c_i32, [c_vp, c_i32, c_i32, c_vp, c_vp]),
     "moe_profile_begin": (c_i32, [c_vp, c_i32]),
     "moe_profile_end": (c_i32, [c_vp, ctypes.POINTER(c_i32), ctypes.POINTER(ctypes.c_float), ctypes.POINTER(c_i32)]),
@@ -150,6 +152,12 @@ def forward(h, x, T, routing: dict, out, workspace, stream=None) -> None:
     rs = routing_struct(routing)
     check(lib().moe_forward(h, ptr(x), T, ctypes.byref(rs), ptr(out), ptr(workspace), workspace.numel(),
                             stream_handle(stream)), "moe_forward")
+
+
+def route_forward(h, x, T, routing: dict, out, workspace, logit_bias=None, logits_out=None, stream=None) -> None:
+    rs = routing_struct(routing)
+    check(lib().moe_route_forward(h, ptr(x), T, ptr(logit_bias), ptr(logits_out), ctypes.byref(rs), ptr(out),
+                                  ptr(workspace), workspace.numel(), stream_handle(stream)), "moe_route_forward")
 
 
 def unpack_expert(h, e: int, which: int, out, stream=None) -> None:

@@ -18,6 +18,9 @@ struct moe_handle {
     uint8_t *packed;
     int64_t off_router, off_xside, off_outside, off_gateup, off_down;
     int64_t gateup_stride, down_stride;   // packed bytes per expert
+    // moe_route_forward: second stream for the x-side products, fork / join events (host objects)
+    hipStream_t side = nullptr;
+    hipEvent_t fork = nullptr, join = nullptr;
     // profiling hook state
     bool prof = false;
     int prof_max = 0;
@@ -35,6 +38,8 @@ constexpr int TILED_MIN_ROWS = 32;
 bool tiled_experts(const moe_config *c, int64_t T) { return T * c->top_k >= (int64_t)TILED_MIN_ROWS * c->n_experts; }
 int expert_bm(const moe_config *c, int64_t T) { return tiled_experts(c, T) ? TILED_BM : BM_STREAM; }
 constexpr int SKINNY_STEPS = 16; // 32-wide K steps per split of the few-token dense products
+// Few-token x-side product: column groups per K split (14 splits x 18 = 252 workgroups, one per CU).
+constexpr int XSIDE_GROUPS = 18;
 
 int64_t align_up(int64_t v) { return (v + ALIGN - 1) / ALIGN * ALIGN; }
 
@@ -94,6 +99,7 @@ PackedLayout packed_layout(const moe_config *c)
 
 struct WsLayout {
     int64_t logits, hist, tiles1, tiles2, z, acat, h, y, partials, total;
+    int64_t rpartials;                  // router partials (inside the partials region, before the dense ones)
     int64_t max_tiles1, max_tiles2;
 };
 
@@ -131,16 +137,20 @@ WsLayout ws_layout(const moe_config *c, int64_t T)
     L.y = off;
     off = align_up(off + T * K * Lt * 2);
     L.partials = off;
+    L.rpartials = off;
     if (T <= SKINNY_MAX_M) {   // split-K partial tiles of the few-token dense products
+        // The router's partials and those of the x-side / output products live side by side, so
+        // the router and the x-side product can run concurrently (moe_route_forward).
         const int64_t Hin = c->has_latent_proj ? c->hidden : c->latent, E_pad = (E + 15) / 16 * 16;
         const int64_t R = SKINNY_MAX_M;   // partial tiles keep 64 rows whatever T is
-        int64_t p = skinny_splits((int)Hin, SKINNY_STEPS) * R * E_pad;
+        off = align_up(off + (int64_t)skinny_splits((int)Hin, SKINNY_STEPS) * R * E_pad * 4);
+        L.partials = off;
         if (c->has_latent_proj) {
             const int64_t H = c->hidden;
-            p = std::max(p, (int64_t)skinny_splits((int)H, SKINNY_STEPS) * R * (Lt + 2 * S * Is));
-            p = std::max(p, (int64_t)skinny_splits((int)(Lt + S * Is), SKINNY_STEPS) * R * H);
+            const int64_t p = std::max((int64_t)skinny_splits((int)H, SKINNY_STEPS) * R * (Lt + 2 * S * Is),
+                                       (int64_t)skinny_splits((int)(Lt + S * Is), SKINNY_STEPS) * R * H);
+            off = align_up(off + p * 4);
         }
-        off = align_up(off + p * 4);
     }
     L.total = off;
     return L;
@@ -228,7 +238,7 @@ moe_status moe_query_workspace_layout(const moe_config *cfg, int32_t T, size_t *
     if (!valid_config(cfg) || T < 0 || !sizes_fit_int32(cfg, T) || !offsets)
         return MOE_ERR_INVALID_ARG;
     const WsLayout W = ws_layout(cfg, T);
-    const int64_t v[10] = {W.logits, W.hist, W.tiles1, W.tiles2, W.z, W.acat, W.h, W.y, W.partials, W.total};
+    const int64_t v[10] = {W.logits, W.hist, W.tiles1, W.tiles2, W.z, W.acat, W.h, W.y, W.rpartials, W.total};
     for (int i = 0; i < 10; i++)
         offsets[i] = (size_t)v[i];
     return MOE_OK;
@@ -294,8 +304,15 @@ moe_status moe_create(const moe_config *cfg, const moe_weights *w, void *packed,
     if (e == hipSuccess)
         e = launch_pack_down(h->packed + L.down, static_cast<const uint8_t *>(w->down_codes),
                              static_cast<const uint8_t *>(w->down_scales), E, I, Lt, st);
+    // moe_route_forward's second stream (default priority) and its fork / join events
+    if (e == hipSuccess)
+        e = hipStreamCreateWithFlags(&h->side, hipStreamNonBlocking);
+    if (e == hipSuccess)
+        e = hipEventCreateWithFlags(&h->fork, hipEventDisableTiming);
+    if (e == hipSuccess)
+        e = hipEventCreateWithFlags(&h->join, hipEventDisableTiming);
     if (e != hipSuccess) {
-        delete h;
+        moe_destroy(h);
         return MOE_ERR_HIP;
     }
     *out = h;
@@ -356,36 +373,27 @@ void moe_destroy(moe_handle *h)
     if (!h)
         return;
     prof_clear(h);
+    if (h->join)
+        (void)hipEventDestroy(h->join);
+    if (h->fork)
+        (void)hipEventDestroy(h->fork);
+    if (h->side)
+        (void)hipStreamDestroy(h->side);
     delete h;
 }
 
-moe_status moe_route(moe_handle *h, const void *x, int32_t T, const float *logit_bias, const float *logits_in,
-                     float *logits_out, const moe_routing *r, void *workspace, size_t workspace_bytes, void *stream)
-{
-    if (!h || T < 0 || !r)
-        return MOE_ERR_INVALID_ARG;
-    const moe_config *c = &h->cfg;
-    if (!sizes_fit_int32(c, T))
-        return MOE_ERR_INVALID_ARG;
-    if (T == 0)
-        return MOE_OK;
-    if (logits_in ? (x || logit_bias || logits_out) : !x)
-        return MOE_ERR_INVALID_ARG;
-    if (!r->topk_ids || !r->topk_w || !r->counts || !r->offsets || !r->sorted_pairs || !r->inv)
-        return MOE_ERR_INVALID_ARG;
-    if (x && !aligned(x, 16))
-        return MOE_ERR_INVALID_ARG;
-    const WsLayout W = ws_layout(c, T);
-    if (!workspace || !aligned(workspace, ALIGN))
-        return MOE_ERR_INVALID_ARG;
-    if (workspace_bytes < (size_t)W.total)
-        return MOE_ERR_BUFFER_TOO_SMALL;
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    uint8_t *ws = static_cast<uint8_t *>(workspace);
-    const int E = c->n_experts, K = c->top_k;
+} // extern "C"
 
-    float *partials = reinterpret_cast<float *>(ws + W.partials);
-    TopkArgs ta{};
+namespace {
+
+// Router product (logits, or split-K partials for few tokens); fills the top-K arguments.
+moe_status router_impl(moe_handle *h, const void *x, int32_t T, const float *logit_bias, const float *logits_in,
+                       float *logits_out, const moe_routing *r, const WsLayout &W, uint8_t *ws, hipStream_t st,
+                       TopkArgs &ta)
+{
+    const moe_config *c = &h->cfg;
+    const int E = c->n_experts, K = c->top_k;
+    ta = TopkArgs{};
     ta.T = T;
     ta.E = E;
     ta.K = K;
@@ -396,6 +404,7 @@ moe_status moe_route(moe_handle *h, const void *x, int32_t T, const float *logit
     if (logits_in) {
         ta.src = logits_in;
     } else if (T <= SKINNY_MAX_M) {   // few tokens: split-K partials, summed (+bias) by the top-K kernel
+        float *partials = reinterpret_cast<float *>(ws + W.rpartials);
         const int64_t pstride = (int64_t)(h->E_pad / 16) * SKINNY_TILE_FLOATS;
         SkinnyArgs g{static_cast<const uint16_t *>(x), h->Hin, T, h->packed + h->off_router, h->E_pad, h->Hin,
                      partials, pstride};
@@ -420,39 +429,85 @@ moe_status moe_route(moe_handle *h, const void *x, int32_t T, const float *logit
         MOE_LAUNCH(MOE_KERNEL_ROUTER, launch_tiled(g, false, 0, st));
         ta.src = lg;
     }
-    MOE_LAUNCH(MOE_KERNEL_TOPK, launch_topk(ta, st));
-    if (T <= PERM_SMALL_MAX_T)
-        MOE_LAUNCH(MOE_KERNEL_PERMUTE, launch_permute_small(r->topk_ids, T, K, E, r->counts, r->offsets,
-                                                            r->sorted_pairs, r->inv, st));
-    else
-        MOE_LAUNCH(MOE_KERNEL_PERMUTE, launch_permute(r->topk_ids, T, K, E, reinterpret_cast<int32_t *>(ws + W.hist),
-                                                      r->counts, r->offsets, r->sorted_pairs, r->inv, st));
     return MOE_OK;
 }
 
-moe_status moe_forward(moe_handle *h, const void *x, int32_t T, const moe_routing *r, void *out, void *workspace,
-                       size_t workspace_bytes, void *stream)
+// Top-K -> grouping. With `tiles` set (moe_route_forward), the expert tile lists are built here too,
+// from the offsets, so the forward part needs no tile-list launch.
+moe_status select_impl(moe_handle *h, int32_t T, const TopkArgs &ta, const moe_routing *r, const WsLayout &W,
+                       uint8_t *ws, hipStream_t st, bool tiles)
 {
-    if (!h || T < 0 || !r)
-        return MOE_ERR_INVALID_ARG;
     const moe_config *c = &h->cfg;
-    if (!sizes_fit_int32(c, T))
-        return MOE_ERR_INVALID_ARG;
-    if (T == 0)
-        return MOE_OK;
-    if (!x || !out || !aligned(x, 16) || !aligned(out, 16) || x == out)
-        return MOE_ERR_INVALID_ARG;
-    if (!r->topk_w || !r->offsets || !r->sorted_pairs || !r->inv)
-        return MOE_ERR_INVALID_ARG;
-    const WsLayout W = ws_layout(c, T);
-    if (!workspace || !aligned(workspace, ALIGN))
-        return MOE_ERR_INVALID_ARG;
-    if (workspace_bytes < (size_t)W.total)
-        return MOE_ERR_BUFFER_TOO_SMALL;
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    uint8_t *ws = static_cast<uint8_t *>(workspace);
+    const int E = c->n_experts, K = c->top_k;
+    MOE_LAUNCH(MOE_KERNEL_TOPK, launch_topk(ta, st));
+    int32_t *tiles1 = reinterpret_cast<int32_t *>(ws + W.tiles1);
+    int32_t *tiles2 = reinterpret_cast<int32_t *>(ws + W.tiles2);
+    const int bm = expert_bm(c, T);
+    if (T <= PERM_SMALL_MAX_T) {
+        MOE_LAUNCH(MOE_KERNEL_PERMUTE, launch_permute_small(r->topk_ids, T, K, E, r->counts, r->offsets,
+                                                            r->sorted_pairs, r->inv, st, bm,
+                                                            tiles ? tiles1 : nullptr, tiles ? tiles2 : nullptr));
+    } else {
+        MOE_LAUNCH(MOE_KERNEL_PERMUTE, launch_permute(r->topk_ids, T, K, E, reinterpret_cast<int32_t *>(ws + W.hist),
+                                                      r->counts, r->offsets, r->sorted_pairs, r->inv, st));
+        if (tiles)
+            MOE_LAUNCH(MOE_KERNEL_TILEMAP, launch_tilemap(r->offsets, E, bm, tiles1, bm, tiles2, st));
+    }
+    return MOE_OK;
+}
+
+// The x-side products, which need only x: z = bf16(x W_down^T) and h_s = bf16(silu(x Wg_s^T) (x Wu_s^T)).
+// With `tiles` set (moe_forward alone) the expert tile lists are built here as well: by the few-token
+// epilogue, or by a tile-list launch.
+moe_status xside_impl(moe_handle *h, const void *x, int32_t T, const moe_routing *r, const WsLayout &W, uint8_t *ws,
+                      hipStream_t st, bool tiles)
+{
+    const moe_config *c = &h->cfg;
     const bool lat = c->has_latent_proj != 0;
-    const int E = c->n_experts, K = c->top_k, Lt = c->latent, I = c->inter, H = c->hidden;
+    const int E = c->n_experts, Lt = c->latent, H = c->hidden;
+    const int S = lat ? c->n_shared : 0, Is = S ? c->shared_inter : 0;
+    const int ldcat = Lt + S * Is, Nx = Lt + 2 * S * Is;
+    const int bm = expert_bm(c, T);
+    uint16_t *Z = reinterpret_cast<uint16_t *>(ws + W.z);
+    uint16_t *Acat = reinterpret_cast<uint16_t *>(ws + W.acat);
+    int32_t *tiles1 = reinterpret_cast<int32_t *>(ws + W.tiles1);
+    int32_t *tiles2 = reinterpret_cast<int32_t *>(ws + W.tiles2);
+    if (lat && T <= SKINNY_MAX_M) {   // z and h_s from split-K partials, summed by the epilogue
+        float *partials = reinterpret_cast<float *>(ws + W.partials);
+        const int64_t pstride = (int64_t)(Nx / 16) * SKINNY_TILE_FLOATS;
+        SkinnyArgs g{static_cast<const uint16_t *>(x), H, T, h->packed + h->off_xside, Nx, H, partials, pstride};
+        MOE_LAUNCH(MOE_KERNEL_XSIDE, launch_skinny_persist(g, 8, XSIDE_GROUPS, st));
+        XsideEpiArgs ea{partials, pstride, skinny_splits(H, SKINNY_STEPS), T, Nx, Lt, 2 * S * Is, Z, Acat, ldcat,
+                        r->offsets, E, bm, bm, tiles ? tiles1 : nullptr, tiles ? tiles2 : nullptr};
+        MOE_LAUNCH(MOE_KERNEL_XSIDE_EPI, launch_xside_epilogue(ea, st));
+        return MOE_OK;
+    }
+    if (lat) {   // z and h_s in one pass over x
+        GemmArgs g{};
+        g.A = static_cast<const uint16_t *>(x);
+        g.lda = H;
+        g.B = h->packed + h->off_xside;
+        g.M = T;
+        g.N = Nx;
+        g.K = H;
+        g.split = Lt;
+        g.lo = OutDesc{OUT_BF16, Z, Lt, 0, Lt, nullptr};
+        g.hi = OutDesc{OUT_GLU, Acat + Lt, ldcat, Lt, INT_MAX, nullptr};
+        MOE_LAUNCH(MOE_KERNEL_XSIDE, launch_tiled(g, false, 0, st));
+    }
+    if (tiles)
+        MOE_LAUNCH(MOE_KERNEL_TILEMAP, launch_tilemap(r->offsets, E, bm, tiles1, bm, tiles2, st));
+    return MOE_OK;
+}
+
+// Expert products, combine and the output product; needs the routing, the x-side results and the
+// tile lists.
+moe_status experts_impl(moe_handle *h, const void *x, int32_t T, const moe_routing *r, void *out, const WsLayout &W,
+                        uint8_t *ws, hipStream_t st)
+{
+    const moe_config *c = &h->cfg;
+    const bool lat = c->has_latent_proj != 0;
+    const int K = c->top_k, Lt = c->latent, I = c->inter, H = c->hidden;
     const int S = lat ? c->n_shared : 0, Is = S ? c->shared_inter : 0;
     const int ldcat = Lt + S * Is;
     uint16_t *Z = reinterpret_cast<uint16_t *>(ws + W.z);
@@ -461,34 +516,7 @@ moe_status moe_forward(moe_handle *h, const void *x, int32_t T, const moe_routin
     uint16_t *Yb = reinterpret_cast<uint16_t *>(ws + W.y);
     int32_t *tiles1 = reinterpret_cast<int32_t *>(ws + W.tiles1);
     int32_t *tiles2 = reinterpret_cast<int32_t *>(ws + W.tiles2);
-
-    float *partials = reinterpret_cast<float *>(ws + W.partials);
-    const int Nx = Lt + 2 * S * Is;
     const bool tiled = tiled_experts(c, T);
-    const int bm = expert_bm(c, T);
-    if (lat && T <= SKINNY_MAX_M) {   // z and h_s from split-K partials; the epilogue also builds the tile lists
-        const int64_t pstride = (int64_t)(Nx / 16) * SKINNY_TILE_FLOATS;
-        SkinnyArgs g{static_cast<const uint16_t *>(x), H, T, h->packed + h->off_xside, Nx, H, partials, pstride};
-        MOE_LAUNCH(MOE_KERNEL_XSIDE, launch_skinny_persist(g, 8, 18, st));
-        XsideEpiArgs ea{partials, pstride, skinny_splits(H, SKINNY_STEPS), T, Nx, Lt, 2 * S * Is, Z, Acat, ldcat,
-                        r->offsets, E, bm, bm, tiles1, tiles2};
-        MOE_LAUNCH(MOE_KERNEL_XSIDE_EPI, launch_xside_epilogue(ea, st));
-    } else {
-        if (lat) {   // z = bf16(x W_down^T) and h_s = bf16(silu(x Wg_s^T) (x Wu_s^T)) in one pass over x
-            GemmArgs g{};
-            g.A = static_cast<const uint16_t *>(x);
-            g.lda = H;
-            g.B = h->packed + h->off_xside;
-            g.M = T;
-            g.N = Nx;
-            g.K = H;
-            g.split = Lt;
-            g.lo = OutDesc{OUT_BF16, Z, Lt, 0, Lt, nullptr};
-            g.hi = OutDesc{OUT_GLU, Acat + Lt, ldcat, Lt, INT_MAX, nullptr};
-            MOE_LAUNCH(MOE_KERNEL_XSIDE, launch_tiled(g, false, 0, st));
-        }
-        MOE_LAUNCH(MOE_KERNEL_TILEMAP, launch_tilemap(r->offsets, E, bm, tiles1, bm, tiles2, st));
-    }
     {   // h = bf16(silu(z Wg_e^T) (z Wu_e^T)) for every pair, rows in expert-sorted order
         GemmArgs g{};
         g.A = lat ? Z : static_cast<const uint16_t *>(x);
@@ -525,6 +553,7 @@ moe_status moe_forward(moe_handle *h, const void *x, int32_t T, const moe_routin
     MOE_LAUNCH(MOE_KERNEL_COMBINE, launch_combine(Yb, Lt, r->inv, r->topk_w, T, K, lat ? Acat : static_cast<uint16_t *>(out),
                            lat ? ldcat : Lt, st));
     if (lat && T <= SKINNY_MAX_M) {   // out = bf16([zc | h_s] [W_up | Wd_s]^T) from split-K partials
+        float *partials = reinterpret_cast<float *>(ws + W.partials);
         const int64_t pstride = (int64_t)(H / 16) * SKINNY_TILE_FLOATS;
         SkinnyArgs g{Acat, ldcat, T, h->packed + h->off_outside, H, ldcat, partials, pstride};
         MOE_LAUNCH(MOE_KERNEL_OUT, launch_skinny_persist(g, 8, 28, st));
@@ -543,6 +572,131 @@ moe_status moe_forward(moe_handle *h, const void *x, int32_t T, const moe_routin
         MOE_LAUNCH(MOE_KERNEL_OUT, launch_tiled(g, false, 0, st));
     }
     return MOE_OK;
+}
+
+moe_status check_route_args(moe_handle *h, const void *x, int32_t T, const float *logit_bias, const float *logits_in,
+                            const float *logits_out, const moe_routing *r)
+{
+    if (!h || T < 0 || !r || !sizes_fit_int32(&h->cfg, T))
+        return MOE_ERR_INVALID_ARG;
+    if (T == 0)
+        return MOE_OK;
+    if (logits_in ? (x || logit_bias || logits_out) : !x)
+        return MOE_ERR_INVALID_ARG;
+    if (!r->topk_ids || !r->topk_w || !r->counts || !r->offsets || !r->sorted_pairs || !r->inv)
+        return MOE_ERR_INVALID_ARG;
+    if (x && !aligned(x, 16))
+        return MOE_ERR_INVALID_ARG;
+    return MOE_OK;
+}
+
+moe_status check_forward_args(moe_handle *h, const void *x, int32_t T, const moe_routing *r, const void *out)
+{
+    if (!h || T < 0 || !r || !sizes_fit_int32(&h->cfg, T))
+        return MOE_ERR_INVALID_ARG;
+    if (T == 0)
+        return MOE_OK;
+    if (!x || !out || !aligned(x, 16) || !aligned(out, 16) || x == out)
+        return MOE_ERR_INVALID_ARG;
+    if (!r->topk_w || !r->offsets || !r->sorted_pairs || !r->inv)
+        return MOE_ERR_INVALID_ARG;
+    return MOE_OK;
+}
+
+moe_status check_workspace(const WsLayout &W, const void *workspace, size_t workspace_bytes)
+{
+    if (!workspace || !aligned(workspace, ALIGN))
+        return MOE_ERR_INVALID_ARG;
+    if (workspace_bytes < (size_t)W.total)
+        return MOE_ERR_BUFFER_TOO_SMALL;
+    return MOE_OK;
+}
+
+} // namespace
+
+extern "C" {
+
+moe_status moe_route(moe_handle *h, const void *x, int32_t T, const float *logit_bias, const float *logits_in,
+                     float *logits_out, const moe_routing *r, void *workspace, size_t workspace_bytes, void *stream)
+{
+    moe_status e = check_route_args(h, x, T, logit_bias, logits_in, logits_out, r);
+    if (e != MOE_OK || T == 0)
+        return e;
+    const WsLayout W = ws_layout(&h->cfg, T);
+    if ((e = check_workspace(W, workspace, workspace_bytes)) != MOE_OK)
+        return e;
+    uint8_t *ws = static_cast<uint8_t *>(workspace);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    TopkArgs ta;
+    if ((e = router_impl(h, x, T, logit_bias, logits_in, logits_out, r, W, ws, st, ta)) != MOE_OK)
+        return e;
+    return select_impl(h, T, ta, r, W, ws, st, false);
+}
+
+moe_status moe_forward(moe_handle *h, const void *x, int32_t T, const moe_routing *r, void *out, void *workspace,
+                       size_t workspace_bytes, void *stream)
+{
+    moe_status e = check_forward_args(h, x, T, r, out);
+    if (e != MOE_OK || T == 0)
+        return e;
+    const WsLayout W = ws_layout(&h->cfg, T);
+    if ((e = check_workspace(W, workspace, workspace_bytes)) != MOE_OK)
+        return e;
+    uint8_t *ws = static_cast<uint8_t *>(workspace);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if ((e = xside_impl(h, x, T, r, W, ws, st, true)) != MOE_OK)
+        return e;
+    return experts_impl(h, x, T, r, out, W, ws, st);
+}
+
+moe_status moe_route_forward(moe_handle *h, const void *x, int32_t T, const float *logit_bias, float *logits_out,
+                             const moe_routing *r, void *out, void *workspace, size_t workspace_bytes, void *stream)
+{
+    moe_status e = check_route_args(h, x, T, logit_bias, nullptr, logits_out, r);
+    if (e == MOE_OK)
+        e = check_forward_args(h, x, T, r, out);
+    if (e != MOE_OK || T == 0)
+        return e;
+    if (logits_out == out || (const void *)logits_out == x)
+        return MOE_ERR_INVALID_ARG;
+    const WsLayout W = ws_layout(&h->cfg, T);
+    if ((e = check_workspace(W, workspace, workspace_bytes)) != MOE_OK)
+        return e;
+    uint8_t *ws = static_cast<uint8_t *>(workspace);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    TopkArgs ta;
+    if ((e = router_impl(h, x, T, logit_bias, nullptr, logits_out, r, W, ws, st, ta)) != MOE_OK)
+        return e;
+    if (!h->cfg.has_latent_proj) {   // no x-side products: the grouping builds the tile lists
+        if ((e = select_impl(h, T, ta, r, W, ws, st, true)) != MOE_OK)
+            return e;
+        return experts_impl(h, x, T, r, out, W, ws, st);
+    }
+    if (T <= SKINNY_MAX_M) {
+        // Few tokens: the fork and join cost more than the overlap hides (measured at 64 tokens),
+        // so the call is the two calls' sequence on the caller's stream; the few-token x-side
+        // epilogue builds the tile lists alongside its own work, off the critical path.
+        if ((e = select_impl(h, T, ta, r, W, ws, st, false)) != MOE_OK)
+            return e;
+        if ((e = xside_impl(h, x, T, r, W, ws, st, true)) != MOE_OK)
+            return e;
+        return experts_impl(h, x, T, r, out, W, ws, st);
+    }
+    // fork after the router product (which wants the whole GPU): the x-side product then overlaps
+    // the top-K and grouping
+    if (hipEventRecord(h->fork, st) != hipSuccess || hipStreamWaitEvent(h->side, h->fork, 0) != hipSuccess)
+        return MOE_ERR_HIP;
+    const moe_status ex = xside_impl(h, x, T, r, W, ws, h->side, false);
+    const moe_status ro = select_impl(h, T, ta, r, W, ws, st, true);
+    // join: always, so that the side stream never runs past the call's stream, even after an error
+    const bool joined = hipEventRecord(h->join, h->side) == hipSuccess && hipStreamWaitEvent(st, h->join, 0) == hipSuccess;
+    if (ex != MOE_OK)
+        return ex;
+    if (ro != MOE_OK)
+        return ro;
+    if (!joined)
+        return MOE_ERR_HIP;
+    return experts_impl(h, x, T, r, out, W, ws, st);
 }
 
 moe_status moe_unpack_expert(moe_handle *h, int32_t e, int32_t which, void *out, void *stream)

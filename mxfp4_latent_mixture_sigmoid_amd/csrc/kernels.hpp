@@ -97,7 +97,7 @@ struct XsideEpiArgs {
     uint16_t *z;                         // [M, Lt]
     uint16_t *acat;                      // [M, ldcat]; h_s written at columns Lt..
     int64_t ldcat;
-    const int32_t *offsets;              // tile lists (workgroup 0)
+    const int32_t *offsets;              // tile lists (extra last workgroup; none if tiles1 is null)
     int E, bm1, bm2;
     int32_t *tiles1, *tiles2;
 };
@@ -122,8 +122,11 @@ struct TopkArgs {
 constexpr int PERM_TOKENS_PER_BLOCK = 32;
 constexpr int PERM_SMALL_MAX_T = 256;
 hipError_t launch_topk(const TopkArgs &a, hipStream_t st);
+// Grouping for T <= PERM_SMALL_MAX_T in one workgroup; with tiles1 set it also writes the expert tile
+// list(s) of bm rows (tiles2 may be null).
 hipError_t launch_permute_small(const int32_t *ids, int T, int K, int E, int32_t *counts, int32_t *offsets,
-                                int32_t *sorted_pairs, int32_t *inv, hipStream_t st);
+                                int32_t *sorted_pairs, int32_t *inv, hipStream_t st, int bm = 0,
+                                int32_t *tiles1 = nullptr, int32_t *tiles2 = nullptr);
 hipError_t launch_permute(const int32_t *ids, int T, int K, int E, int32_t *hist, int32_t *counts,
                           int32_t *offsets, int32_t *sorted_pairs, int32_t *inv, hipStream_t st);
 

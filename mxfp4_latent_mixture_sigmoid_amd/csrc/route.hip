@@ -165,11 +165,14 @@ hipError_t launch_topk(const TopkArgs &a, hipStream_t st)
 // routed to it (the K experts of a token are distinct, so each (token, expert) bit is set once);
 // counts are popcounts, offsets their exclusive scan, and the position of pair (t, j) is
 // offsets[e] + the number of tokens before t in e's mask -- stable, with no ordering races.
+// With `tiles` set, the workgroup also writes the expert tile list(s) of `bm` rows from the offsets.
 __global__ __launch_bounds__(1024) void perm_small_kernel(const int32_t *__restrict__ ids, int T, int K, int E,
                                                           int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
-                                                          int32_t *__restrict__ sorted_pairs, int32_t *__restrict__ inv)
+                                                          int32_t *__restrict__ sorted_pairs, int32_t *__restrict__ inv,
+                                                          int bm, int32_t *__restrict__ tiles1,
+                                                          int32_t *__restrict__ tiles2)
 {
-    extern __shared__ uint32_t masks[];               // [E][W] then off[E]
+    extern __shared__ uint32_t masks[];               // [E][W] then off[E + 1]
     __shared__ int sh[16];
     const int W = (T + 31) / 32;
     int *off = reinterpret_cast<int *>(masks + E * W);
@@ -193,8 +196,10 @@ __global__ __launch_bounds__(1024) void perm_small_kernel(const int32_t *__restr
         offsets[threadIdx.x] = ex;
         off[threadIdx.x] = ex;
     }
-    if (threadIdx.x == 0)
+    if (threadIdx.x == 0) {
         offsets[E] = total;
+        off[E] = total;
+    }
     __syncthreads();
     for (int p = threadIdx.x; p < P; p += blockDim.x) {
         const int t = p / K, e = ids[p];
@@ -206,16 +211,22 @@ __global__ __launch_bounds__(1024) void perm_small_kernel(const int32_t *__restr
         sorted_pairs[pos] = p;
         inv[p] = pos;
     }
+    if (tiles1) {
+        write_tiles(off, E, bm, tiles1, sh);
+        if (tiles2)
+            write_tiles(off, E, bm, tiles2, sh);
+    }
 }
 
 hipError_t launch_permute_small(const int32_t *ids, int T, int K, int E, int32_t *counts, int32_t *offsets,
-                                int32_t *sorted_pairs, int32_t *inv, hipStream_t st)
+                                int32_t *sorted_pairs, int32_t *inv, hipStream_t st, int bm, int32_t *tiles1,
+                                int32_t *tiles2)
 {
-    if (T > PERM_SMALL_MAX_T || E > 1024)
+    if (T > PERM_SMALL_MAX_T || E > 1024 || (tiles1 && bm < 1))
         return hipErrorInvalidValue;
-    const size_t lds = ((size_t)E * ((T + 31) / 32) + E) * sizeof(uint32_t);
+    const size_t lds = ((size_t)E * ((T + 31) / 32) + E + 1) * sizeof(uint32_t);
     hipLaunchKernelGGL(perm_small_kernel, dim3(1), dim3(1024), lds, st, ids, T, K, E, counts, offsets, sorted_pairs,
-                       inv);
+                       inv, bm, tiles1, tiles2);
     return hipGetLastError();
 }
 

@@ -272,10 +272,10 @@ __device__ inline f32x4_t sum_slot(const float *slot, int64_t split_stride, int 
 // x-side epilogue. Thread (nb, mf, lane) owns rows mf*16 + 4(lane/16) .. +3 of column
 // nb*16 + lane%16: z = bf16(sum) for the latent blocks; for a shared-expert pair of blocks (16
 // gate columns, then the matching 16 up columns) the thread of the gate block forms
-// h_s = bf16(silu(gate) * up). The last workgroup builds the expert tile lists instead.
+// h_s = bf16(silu(gate) * up). With tile lists requested, one extra (last) workgroup builds them.
 __global__ __launch_bounds__(256) void xside_epilogue_kernel(const XsideEpiArgs e)
 {
-    if (blockIdx.x == gridDim.x - 1) {
+    if (e.tiles1 && blockIdx.x == gridDim.x - 1) {
         __shared__ int sh[16];
         write_tiles(e.offsets, e.E, e.bm1, e.tiles1, sh);
         write_tiles(e.offsets, e.E, e.bm2, e.tiles2, sh);
@@ -315,7 +315,7 @@ __global__ __launch_bounds__(256) void xside_epilogue_kernel(const XsideEpiArgs 
 hipError_t launch_xside_epilogue(const XsideEpiArgs &e, hipStream_t st)
 {
     const int64_t threads = (int64_t)(e.Lt / 16 + e.shared_cols / 32) * 4 * WAVE;
-    const unsigned blocks = 1 + (unsigned)((threads + 255) / 256);
+    const unsigned blocks = (e.tiles1 ? 1 : 0) + (unsigned)((threads + 255) / 256);
     hipLaunchKernelGGL(xside_epilogue_kernel, dim3(blocks), dim3(256), 0, st, e);
     return hipGetLastError();
 }

@@ -51,6 +51,14 @@ class MoELayer:
         abi.forward(self.handle, x, T, routing, out, self.workspace, stream)
         return out
 
+    def route_forward(self, x, T, routing, out=None, logit_bias=None, logits_out=None, stream=None):
+        """route + forward in one call (x-side products concurrent with the routing)."""
+        self._check_T(T)
+        if out is None:
+            out = torch.empty(max(T, 1), self.H, dtype=torch.bfloat16, device=self.device)
+        abi.route_forward(self.handle, x, T, routing, out, self.workspace, logit_bias, logits_out, stream)
+        return out
+
     def unpack_expert(self, e: int, which: int, stream=None):
         rows, cols = (self.cfg.inter, self.Lt) if which < 2 else (self.Lt, self.cfg.inter)
         out = torch.empty(rows, cols, dtype=torch.bfloat16, device=self.device)

@@ -150,6 +150,28 @@ class GpuRun:
         return d
 
 
+def check_fused_identical(layer, shape, inp: dict, run: GpuRun) -> None:
+    """moe_route_forward (x-side products on the handle's second stream, concurrent with the
+    routing) must reproduce the separate moe_route + moe_forward run bit for bit: the same kernels
+    and fixed-order sums, only the scheduling differs."""
+    T = inp["x"].shape[0]
+    x = dev(inp["x"])
+    bias = None if inp.get("router_bias") is None else dev(inp["router_bias"])
+    r = layer.alloc_routing(T)
+    lg = torch.empty(max(T, 1), shape.E, dtype=torch.float32, device="cuda")
+    out = layer.route_forward(x, T, r, logit_bias=bias, logits_out=lg)
+    torch.cuda.synchronize()
+    K = shape.K
+    got = dict(ids=r["topk_ids"][:T], w=r["topk_w"][:T].view(torch.int32), counts=r["counts"],
+               offsets=r["offsets"], sorted_pairs=r["sorted_pairs"][:T * K], inv=r["inv"][:T * K],
+               logits=lg[:T].view(torch.int32))
+    ref = dict(ids=run.ids, w=run.w.view(np.int32), counts=run.counts, offsets=run.offsets,
+               sorted_pairs=run.sorted_pairs, inv=run.inv, logits=run.logits.view(np.int32))
+    for k, v in got.items():
+        assert np.array_equal(v.cpu().numpy(), ref[k]), f"route_forward {k} differs from route + forward"
+    assert torch.equal(out[:T].view(torch.int16), run._out.view(torch.int16)), "route_forward output differs"
+
+
 def check_routing_exact(run: GpuRun, E: int, K: int, logits_for_select: np.ndarray):
     """ids, counts, offsets, sorted_pairs and inv must equal the oracle's on the same logits."""
     ids_ref = O.select(logits_for_select.astype(np.float64), K)

@@ -1,7 +1,8 @@
 """GPU parity at the full workload sizes: one GPU's TP8 share at decode (64 tokens) and prefill
 (8192 tokens, Zipf-skewed), the full block (16384 tokens, Zipf, 1% exact rank-16/17 ties) and the
 full unsharded experts (4096 tokens, intermediate 3072). Routing is compared bit for bit on every
-token; floating-point tensors on a seeded token sample that the oracle computes one by one."""
+token; floating-point tensors on a seeded token sample that the oracle computes one by one. The
+fused route + forward call must reproduce the separate calls bit for bit at every size."""
 import numpy as np
 import pytest
 import torch
@@ -32,6 +33,8 @@ def test_full_size_parity(name, n_sample):
     inp = make_inputs(shape)
     layer = G.make_layer(shape, inp, T_max=shape.T)
     run = G.GpuRun(layer, shape, inp)
+    G.check_fused_identical(layer, shape, inp, run)
+    G.log("  route_forward: bit-identical to route + forward")
     tokens = None if n_sample is None else sample_tokens(shape, n_sample)
     tied_logits = None
     if shape.tie_frac > 0:

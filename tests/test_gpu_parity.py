@@ -105,6 +105,49 @@ def test_ragged_token_counts(T):
     G.check_forward(replace(shape, T=T), sub, run)
 
 
+@pytest.mark.parametrize("name", list(SMALL_SHAPES))
+def test_route_forward_bit_identical(name):
+    shape, inp, layer = _setup(name)
+    run = G.GpuRun(layer, shape, inp)
+    G.check_fused_identical(layer, shape, inp, run)
+
+
+@pytest.mark.parametrize("T", [1, 17, 64, 65])
+def test_route_forward_ragged_and_size_boundaries(T):
+    """Around the few-token paths: T = 64 is the last split-K size, 65 the first tiled one."""
+    shape = replace(MID, name=f"fused{T}", T=T, seed=21)
+    inp = make_inputs(shape)
+    layer = G.make_layer(shape, inp, T_max=shape.T)
+    run = G.GpuRun(layer, shape, inp)
+    G.check_fused_identical(layer, shape, inp, run)
+    G.check_forward(shape, inp, run)
+    layer.close()
+
+
+def test_route_forward_zero_tokens_and_bad_arguments():
+    from mxfp4_latent_mixture_sigmoid_amd import abi
+    shape, inp, layer = _setup("tiny")
+    x = G.dev(inp["x"])
+    r = layer.alloc_routing(1)
+    r["counts"].fill_(-7)
+    out = torch.full((1, shape.H), 3.0, dtype=torch.bfloat16, device="cuda")
+    abi.route_forward(layer.handle, x, 0, r, out, layer.workspace)
+    torch.cuda.synchronize()
+    assert int(r["counts"][0]) == -7 and float(out[0, 0]) == 3.0
+    r = layer.alloc_routing(shape.T)
+    out = torch.empty(shape.T, shape.H, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(abi.MoEError) as ei:       # workspace too small
+        abi.route_forward(layer.handle, x, shape.T, r, out, layer.workspace[:256])
+    assert ei.value.status == abi.Status.BUFFER_TOO_SMALL
+    with pytest.raises(abi.MoEError) as ei:       # output aliases input
+        abi.route_forward(layer.handle, x, shape.T, r, x, layer.workspace)
+    assert ei.value.status == abi.Status.INVALID_ARG
+    lg = torch.empty(shape.T, shape.E, dtype=torch.float32, device="cuda")
+    with pytest.raises(abi.MoEError) as ei:       # logits_out aliases the output
+        abi.route_forward(layer.handle, x, shape.T, r, out, layer.workspace, logits_out=out)
+    assert ei.value.status == abi.Status.INVALID_ARG
+
+
 def test_zero_tokens_is_noop():
     shape, inp, layer = _setup("tiny")
     r = layer.alloc_routing(1)

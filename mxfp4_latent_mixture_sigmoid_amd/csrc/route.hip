@@ -17,15 +17,12 @@ __device__ inline uint32_t order_key(float f)
 
 __device__ inline float key_value(uint32_t k) { return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k); }
 
-// Top-K of one token by one wave. Lane l holds the logits of experts l, l + 64, ... in v[]; each of
-// the K rounds takes the wave-wide largest key (DPP reduction), resolves equal keys to the lowest
-// expert index, and retires the winner. Gate weights: sigmoid of the selected logits over their
-// sum. Writes logits_out (if set), ids and w of token t.
+// Keys of one token, one wave: lane l holds the logits of experts l, l + 64, ... in v[]; adds the
+// bias, writes logits_out (if set) and returns the order keys (0 past the last expert).
 template <int SLOTS>
-__device__ inline void select_token(const TopkArgs &a, int t, float *v)
+__device__ inline void token_keys(const TopkArgs &a, int t, float *v, uint32_t *key)
 {
     const int lane = threadIdx.x & (WAVE - 1);
-    uint32_t key[SLOTS];
 #pragma unroll
     for (int j = 0; j < SLOTS; j++) {
         const int e = lane + WAVE * j;
@@ -38,35 +35,93 @@ __device__ inline void select_token(const TopkArgs &a, int t, float *v)
             key[j] = order_key(v[j]);
         }
     }
+}
+
+__device__ inline uint64_t shfl_xor_u64(uint64_t v, int mask)
+{
+    const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, mask, WAVE);
+    const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), mask, WAVE);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// Bitonic sort of one 64-bit value per lane into descending lane order (lane 0 the largest).
+__device__ inline uint64_t wave_sort_desc_u64(uint64_t v)
+{
+    const int lane = threadIdx.x & (WAVE - 1);
+#pragma unroll
+    for (int k = 2; k <= WAVE; k <<= 1)
+#pragma unroll
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            const uint64_t p = shfl_xor_u64(v, j);
+            const bool keep_max = ((lane & j) == 0) == ((lane & k) == 0);
+            v = keep_max ? (p > v ? p : v) : (p < v ? p : v);
+        }
+    return v;
+}
+
+// Top-K of one token by one wave from the order keys (0 = no expert), ties to the lower expert, and
+// the gate weights: sigmoid of the selected logits over their sum. Writes ids and w of token t.
+// Every candidate becomes one 64-bit value, key above the complemented expert index, so the order
+// (key descending, expert ascending) is plain unsigned order and all values differ. The K-th largest
+// of the 64 lane maxima bounds the K-th largest value from below (K lanes hold a value at least that
+// large), so only values at or above it can be selected; at most K lanes hold such values. When they
+// number at most 64 (the usual case), they are gathered through `scratch` (64 entries of this wave)
+// and sorted across the wave: lanes 0 .. K-1 then hold the selection in rank order. Otherwise K
+// rounds of wave-wide maxima select directly.
+template <int SLOTS>
+__device__ inline void select_keys(const TopkArgs &a, int t, const uint32_t *key, uint64_t *scratch)
+{
+    const int lane = threadIdx.x & (WAVE - 1);
+    uint64_t c[SLOTS];
+    uint64_t m = 0;
+#pragma unroll
+    for (int j = 0; j < SLOTS; j++) {
+        c[j] = key[j] ? ((uint64_t)key[j] << 32) | (uint32_t)~(uint32_t)(lane + WAVE * j) : 0;
+        m = c[j] > m ? c[j] : m;
+    }
+    const uint64_t lane_max_sorted = wave_sort_desc_u64(m);
+    const uint32_t th_lo = (uint32_t)__shfl((int)(uint32_t)lane_max_sorted, a.K - 1, WAVE);
+    const uint32_t th_hi = (uint32_t)__shfl((int)(uint32_t)(lane_max_sorted >> 32), a.K - 1, WAVE);
+    const uint64_t th = ((uint64_t)th_hi << 32) | th_lo;
+    int n = 0;
+#pragma unroll
+    for (int j = 0; j < SLOTS; j++)
+        n += (c[j] >= th && c[j] != 0) ? 1 : 0;
+    const int incl = wave_incl_scan(n);
+    const int total = __shfl(incl, WAVE - 1, WAVE);
     uint32_t my_key = 0u;
     int my_id = 0;
-    for (int k = 0; k < a.K; k++) {
-        uint32_t bk = key[0];
-        int bj = 0;
+    if (total <= WAVE) {
+        int pos = incl - n;
 #pragma unroll
-        for (int j = 1; j < SLOTS; j++)
-            if (key[j] > bk) {
-                bk = key[j];
-                bj = j;
+        for (int j = 0; j < SLOTS; j++)
+            if (c[j] >= th && c[j] != 0)
+                scratch[pos++] = c[j];
+        const uint64_t mine = lane < total ? scratch[lane] : 0;
+        const uint64_t r = wave_sort_desc_u64(mine);
+        my_key = (uint32_t)(r >> 32);
+        my_id = (int)~(uint32_t)r;
+    } else {
+        uint64_t left[SLOTS];
+#pragma unroll
+        for (int j = 0; j < SLOTS; j++)
+            left[j] = c[j];
+        for (int k = 0; k < a.K; k++) {
+            uint64_t bm = left[0];
+#pragma unroll
+            for (int j = 1; j < SLOTS; j++)
+                bm = left[j] > bm ? left[j] : bm;
+            const uint32_t wk = wave_max_u32((uint32_t)(bm >> 32));
+            const uint32_t wl = wave_max_u32((uint32_t)(bm >> 32) == wk ? (uint32_t)bm : 0u);
+            if (lane == k) {
+                my_key = wk;
+                my_id = (int)~wl;
             }
-        const uint32_t wk = wave_max_u32(bk);
-        const unsigned long long hit = __ballot(bk == wk);
-        int win;
-        if (__popcll(hit) == 1) {
-            const int wl = __ffsll((long long)hit) - 1;
-            win = __builtin_amdgcn_readlane(bj, wl) * WAVE + wl;
-        } else {
-            win = (int)wave_min_u32(bk == wk ? (uint32_t)(bj * WAVE + lane) : 0xFFFFFFFFu);
-        }
-        if (lane == k) {
-            my_key = wk;
-            my_id = win;
-        }
-        if (lane == (win & (WAVE - 1))) {
+            const uint64_t win = ((uint64_t)wk << 32) | wl;
 #pragma unroll
             for (int j = 0; j < SLOTS; j++)
-                if (j == win / WAVE)
-                    key[j] = 0u;
+                if (left[j] == win)
+                    left[j] = 0;
         }
     }
     const float s = lane < a.K ? 1.0f / (1.0f + expf(-key_value(my_key))) : 0.0f;
@@ -81,64 +136,88 @@ __device__ inline void select_token(const TopkArgs &a, int t, float *v)
 template <int SLOTS>
 __global__ __launch_bounds__(256) void topk_kernel(const TopkArgs a)
 {
-    const int lane = threadIdx.x & (WAVE - 1);
-    const int t = blockIdx.x * 4 + threadIdx.x / WAVE;
+    __shared__ uint64_t scratch[4][WAVE];
+    const int lane = threadIdx.x & (WAVE - 1), wv = threadIdx.x / WAVE;
+    const int t = blockIdx.x * 4 + wv;
     if (t >= a.T)
         return;
     float v[SLOTS];
 #pragma unroll
     for (int j = 0; j < SLOTS; j++)
         v[j] = a.src[(int64_t)t * a.ld + min(lane + WAVE * j, a.E - 1)];
-    select_token<SLOTS>(a, t, v);
+    uint32_t key[SLOTS];
+    token_keys<SLOTS>(a, t, v, key);
+    select_keys<SLOTS>(a, t, key, scratch[wv]);
 }
 
-// Logits as split-K partial tiles (accumulator order): the 16-byte slot of an expert holds four
-// consecutive tokens, so one workgroup takes tokens 4 b .. 4 b + 3. Wave w sums the splits
-// w, w + 4, ... of every expert into LDS; each wave then adds the four sums (in wave order) for
-// its own token and selects.
+// Logits as split-K partial tiles (accumulator order): eight waves per workgroup, which takes tokens
+// 4 b .. 4 b + 3 (one 16-byte partial slot of an expert holds four consecutive tokens). Wave w adds
+// splits w, w + 8, ... of every expert (lane l, slot j: expert l + 64 j), then the eight wave sums
+// are added pairwise through LDS in a fixed tree (w += w + 4, w += w + 2, w += w + 1); waves 0..3
+// then select tokens 4 b .. 4 b + 3 from the totals.
 template <int SLOTS>
-__global__ __launch_bounds__(256) void topk_partials_kernel(const TopkArgs a)
+__global__ __launch_bounds__(512) void topk_wide_kernel(const TopkArgs a)
 {
-    extern __shared__ f32x4_t red[];                 // [4 waves][SLOTS * 64 experts]
-    const int lane = threadIdx.x & (WAVE - 1), wv = threadIdx.x / WAVE;
+    constexpr int WAVES = 8;
+    __shared__ f32x4_t red[WAVES / 2 * SLOTS * WAVE];     // tree level buffer, then the totals
+    __shared__ uint64_t scratch[4][WAVE];
+    const int lane = threadIdx.x & (WAVE - 1);
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE);
     const int t0 = blockIdx.x * 4;
     const int mf = t0 / 16, quad = (t0 % 16) / 4;
+
+    // expert e = lane + 64 j sits in partial tile e / 16 = lane / 16 + 4 j at column e % 16 = lane % 16
+    const float *base = a.src + (int64_t)(lane / 16) * SKINNY_TILE_FLOATS + (mf * WAVE + quad * 16 + lane % 16) * 4;
+    auto slot = [&](int s, int j) {
+        f32x4_t v = {0.f, 0.f, 0.f, 0.f};
+        if (lane + WAVE * j < a.E)
+            v = *reinterpret_cast<const f32x4_t *>(base + s * a.split_stride + (int64_t)j * 4 * SKINNY_TILE_FLOATS);
+        return v;
+    };
     f32x4_t acc[SLOTS];
 #pragma unroll
     for (int j = 0; j < SLOTS; j++)
-        acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    for (int s0 = wv; s0 < a.splits; s0 += 8) {      // two splits per batch: w + 8 i and w + 4 + 8 i
-        f32x4_t ta[SLOTS], tb[SLOTS];
-        const int sa = s0, sb = min(s0 + 4, a.splits - 1);
+        acc[j] = wv < a.splits ? slot(wv, j) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int s = wv + WAVES; s < a.splits; s += WAVES)
 #pragma unroll
-        for (int j = 0; j < SLOTS; j++) {
-            const int e = min(lane + WAVE * j, a.E - 1);
-            const int64_t off = (int64_t)(e / 16) * SKINNY_TILE_FLOATS + (mf * WAVE + quad * 16 + e % 16) * 4;
-            ta[j] = *reinterpret_cast<const f32x4_t *>(a.src + sa * a.split_stride + off);
-            tb[j] = *reinterpret_cast<const f32x4_t *>(a.src + sb * a.split_stride + off);
+        for (int h = 0; h < 2; h++) {          // half the slots at a time (register budget)
+            f32x4_t ld[SLOTS / 2];
+#pragma unroll
+            for (int j = 0; j < SLOTS / 2; j++)
+                ld[j] = slot(s, h * (SLOTS / 2) + j);
+#pragma unroll
+            for (int j = 0; j < SLOTS / 2; j++)
+                acc[h * (SLOTS / 2) + j] += ld[j];
         }
 #pragma unroll
-        for (int j = 0; j < SLOTS; j++) {
-            acc[j] += ta[j];
-            if (s0 + 4 < a.splits)
-                acc[j] += tb[j];
-        }
+    for (int half = WAVES / 2; half >= 1; half /= 2) {
+        if (wv >= half && wv < 2 * half)
+#pragma unroll
+            for (int j = 0; j < SLOTS; j++)
+                red[((wv - half) * SLOTS + j) * WAVE + lane] = acc[j];
+        __syncthreads();
+        if (wv < half)
+#pragma unroll
+            for (int j = 0; j < SLOTS; j++)
+                acc[j] += red[(wv * SLOTS + j) * WAVE + lane];
+        __syncthreads();
     }
+    if (wv == 0)
 #pragma unroll
-    for (int j = 0; j < SLOTS; j++)
-        red[wv * SLOTS * WAVE + j * WAVE + lane] = acc[j];
+        for (int j = 0; j < SLOTS; j++)
+            red[j * WAVE + lane] = acc[j];
     __syncthreads();
+
     const int t = t0 + wv;
-    if (t >= a.T)
+    if (wv >= 4 || t >= a.T)
         return;
     float v[SLOTS];
 #pragma unroll
-    for (int j = 0; j < SLOTS; j++) {
-        const int i = j * WAVE + lane;
-        v[j] = ((red[i][wv] + red[SLOTS * WAVE + i][wv]) + red[2 * SLOTS * WAVE + i][wv]) +
-               red[3 * SLOTS * WAVE + i][wv];
-    }
-    select_token<SLOTS>(a, t, v);
+    for (int j = 0; j < SLOTS; j++)
+        v[j] = red[j * WAVE + lane][wv];
+    uint32_t key[SLOTS];
+    token_keys<SLOTS>(a, t, v, key);
+    select_keys<SLOTS>(a, t, key, scratch[wv]);
 }
 
 hipError_t launch_topk(const TopkArgs &a, hipStream_t st)
@@ -146,14 +225,15 @@ hipError_t launch_topk(const TopkArgs &a, hipStream_t st)
     const dim3 grid((a.T + 3) / 4);
     if (a.K > WAVE || a.E > 16 * WAVE || (a.partials && a.T > SKINNY_MAX_M))
         return hipErrorInvalidValue;
-    const bool small = a.E <= 2 * WAVE;
+    const int slots = (a.E + WAVE - 1) / WAVE;
     if (a.partials) {
-        const size_t lds = 4 * (small ? 2 : 16) * WAVE * sizeof(f32x4_t);
-        if (small)
-            hipLaunchKernelGGL(topk_partials_kernel<2>, grid, dim3(256), lds, st, a);
+        if (slots <= 4)
+            hipLaunchKernelGGL(topk_wide_kernel<4>, grid, dim3(512), 0, st, a);
+        else if (slots <= 8)
+            hipLaunchKernelGGL(topk_wide_kernel<8>, grid, dim3(512), 0, st, a);
         else
-            hipLaunchKernelGGL(topk_partials_kernel<16>, grid, dim3(256), lds, st, a);
-    } else if (small) {
+            hipLaunchKernelGGL(topk_wide_kernel<16>, grid, dim3(512), 0, st, a);
+    } else if (slots <= 2) {
         hipLaunchKernelGGL(topk_kernel<2>, grid, dim3(256), 0, st, a);
     } else {
         hipLaunchKernelGGL(topk_kernel<16>, grid, dim3(256), 0, st, a);

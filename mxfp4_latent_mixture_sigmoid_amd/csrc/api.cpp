@@ -37,9 +37,12 @@ constexpr int BM_STREAM = 16;
 constexpr int TILED_MIN_ROWS = 32;
 bool tiled_experts(const moe_config *c, int64_t T) { return T * c->top_k >= (int64_t)TILED_MIN_ROWS * c->n_experts; }
 int expert_bm(const moe_config *c, int64_t T) { return tiled_experts(c, T) ? TILED_BM : BM_STREAM; }
-constexpr int SKINNY_STEPS = 16; // 32-wide K steps per split of the few-token dense products
-// Few-token x-side product: column groups per K split (14 splits x 18 = 252 workgroups, one per CU).
-constexpr int XSIDE_GROUPS = 18;
+constexpr int SKINNY_STEPS = 16;   // 32-wide K steps per split of the few-token router product
+constexpr int SKINNY_XSTEPS = 16;  // ... and of the few-token x-side and output products
+// Few-token x-side and output products: column groups per 512-wide K split (14 x 18 = 252 and
+// 9 x 28 = 252 workgroups at K = 7168 and 4352; measured best of 18..72 groups and 512 / 1024-wide
+// splits at 64 tokens).
+constexpr int XSIDE_GROUPS = 18, OUT_GROUPS = 28;
 
 int64_t align_up(int64_t v) { return (v + ALIGN - 1) / ALIGN * ALIGN; }
 
@@ -147,8 +150,8 @@ WsLayout ws_layout(const moe_config *c, int64_t T)
         L.partials = off;
         if (c->has_latent_proj) {
             const int64_t H = c->hidden;
-            const int64_t p = std::max((int64_t)skinny_splits((int)H, SKINNY_STEPS) * R * (Lt + 2 * S * Is),
-                                       (int64_t)skinny_splits((int)(Lt + S * Is), SKINNY_STEPS) * R * H);
+            const int64_t p = std::max((int64_t)skinny_splits((int)H, SKINNY_XSTEPS) * R * (Lt + 2 * S * Is),
+                                       (int64_t)skinny_splits((int)(Lt + S * Is), SKINNY_XSTEPS) * R * H);
             off = align_up(off + p * 4);
         }
     }
@@ -476,8 +479,8 @@ moe_status xside_impl(moe_handle *h, const void *x, int32_t T, const moe_routing
         float *partials = reinterpret_cast<float *>(ws + W.partials);
         const int64_t pstride = (int64_t)(Nx / 16) * SKINNY_TILE_FLOATS;
         SkinnyArgs g{static_cast<const uint16_t *>(x), H, T, h->packed + h->off_xside, Nx, H, partials, pstride};
-        MOE_LAUNCH(MOE_KERNEL_XSIDE, launch_skinny_persist(g, 8, XSIDE_GROUPS, st));
-        XsideEpiArgs ea{partials, pstride, skinny_splits(H, SKINNY_STEPS), T, Nx, Lt, 2 * S * Is, Z, Acat, ldcat,
+        MOE_LAUNCH(MOE_KERNEL_XSIDE, launch_skinny_persist(g, 8, XSIDE_GROUPS, SKINNY_XSTEPS, st));
+        XsideEpiArgs ea{partials, pstride, skinny_splits(H, SKINNY_XSTEPS), T, Nx, Lt, 2 * S * Is, Z, Acat, ldcat,
                         r->offsets, E, bm, bm, tiles ? tiles1 : nullptr, tiles ? tiles2 : nullptr};
         MOE_LAUNCH(MOE_KERNEL_XSIDE_EPI, launch_xside_epilogue(ea, st));
         return MOE_OK;
@@ -556,8 +559,8 @@ moe_status experts_impl(moe_handle *h, const void *x, int32_t T, const moe_routi
         float *partials = reinterpret_cast<float *>(ws + W.partials);
         const int64_t pstride = (int64_t)(H / 16) * SKINNY_TILE_FLOATS;
         SkinnyArgs g{Acat, ldcat, T, h->packed + h->off_outside, H, ldcat, partials, pstride};
-        MOE_LAUNCH(MOE_KERNEL_OUT, launch_skinny_persist(g, 8, 28, st));
-        MOE_LAUNCH(MOE_KERNEL_OUT_EPI, launch_out_epilogue(partials, pstride, skinny_splits(ldcat, SKINNY_STEPS), T, H,
+        MOE_LAUNCH(MOE_KERNEL_OUT, launch_skinny_persist(g, 8, OUT_GROUPS, SKINNY_XSTEPS, st));
+        MOE_LAUNCH(MOE_KERNEL_OUT_EPI, launch_out_epilogue(partials, pstride, skinny_splits(ldcat, SKINNY_XSTEPS), T, H,
                                                            static_cast<uint16_t *>(out), st));
     } else if (lat) {
         GemmArgs g{};

@@ -88,7 +88,7 @@ struct SkinnyArgs {
 };
 int skinny_splits(int K, int chunk_steps);
 hipError_t launch_skinny(const SkinnyArgs &g, int waves, int chunk_steps, hipStream_t st);
-hipError_t launch_skinny_persist(const SkinnyArgs &g, int waves, int groups, hipStream_t st);
+hipError_t launch_skinny_persist(const SkinnyArgs &g, int waves, int groups, int chunk_steps, hipStream_t st);
 
 struct XsideEpiArgs {
     const float *P;

@@ -96,37 +96,42 @@ __global__ __launch_bounds__(WAVE *WAVES) void skinny_kernel(const SkinnyArgs g)
             *reinterpret_cast<f32x4_t *>(P + (mf * WAVE + lane) * 4) = acc[mf];
 }
 
-// Persistent variant: workgroup w owns K split (w % splits) and the 16-row weight blocks
-// nb = (w / splits) * WAVES + wave + j * (groups * WAVES), j = 0, 1, ... where groups = gridDim.x /
-// splits. The activation chunk of its split is staged in LDS once; each wave then streams its blocks
-// with the next block's 16 fragments loaded while the current block is multiplied.
-template <int WAVES>
+// Persistent variant: workgroup w owns K split (w % splits) -- a chunk of UNITS x 16 steps -- and the
+// 16-row weight blocks nb = (w / splits) * WAVES + wave + j * (groups * WAVES), j = 0, 1, ... where
+// groups = gridDim.x / splits. The activation chunk of its split is staged in LDS once; each wave
+// then streams its blocks as 16-step units (one contiguous 16 KiB range each), loading the next unit
+// while the current one is multiplied, and writes a block's partial tile after its last unit.
+template <int WAVES, int UNITS>
 __global__ __launch_bounds__(WAVE *WAVES) void skinny_persist_kernel(const SkinnyArgs g, int splits)
 {
-    constexpr int STEPS = 16;
-    extern __shared__ u32x4_t lds_a[];   // [nsteps][4 fragments][64 lanes]
+    constexpr int STEPS = 16, CSTEPS = STEPS * UNITS;
+    __shared__ u32x4_t lds_a[CSTEPS * 4 * WAVE];   // [steps][4 fragments][64 lanes]
     const int lane = threadIdx.x & (WAVE - 1), wv = threadIdx.x / WAVE;
     const int split = blockIdx.x % splits, grp = blockIdx.x / splits;
     const int groups = gridDim.x / splits;
-    const int kc0 = split * STEPS * BF16_STEP;
-    const int nsteps = min(STEPS * BF16_STEP, g.K - kc0) / BF16_STEP;
+    const int kc0 = split * CSTEPS * BF16_STEP;
+    const int nsteps = min(CSTEPS * BF16_STEP, g.K - kc0) / BF16_STEP;
+    const int nunits = (nsteps + STEPS - 1) / STEPS;
     const int mt = (g.M + 15) / 16;
     const int nblocks = g.N / 16;
     const int stride = groups * WAVES;
-    int nb = grp * WAVES + wv;
+    const int nb0 = grp * WAVES + wv;
+    const int items = (nb0 < nblocks ? (nblocks - 1 - nb0) / stride + 1 : 0) * nunits;   // (block, unit)
 
-    auto load_b = [&](int blk, u32x4_t *b) {
-        const int nbc = min(blk, nblocks - 1);
-        const uint8_t *bp = g.B + bf16_block_index(nbc, kc0 / BF16_STEP, g.N, g.K) * BF16_BLOCK_BYTES + lane * 16;
+    auto load_b = [&](int i, u32x4_t *b) {
+        const int blk = min(nb0 + (i / nunits) * stride, nblocks - 1), s0 = (i % nunits) * STEPS;
+        const uint8_t *bp =
+            g.B + bf16_block_index(blk, kc0 / BF16_STEP + s0, g.N, g.K) * BF16_BLOCK_BYTES + lane * 16;
 #pragma unroll
         for (int s = 0; s < STEPS; s++)
-            b[s] = load16_nt(bp + min(s, nsteps - 1) * BF16_BLOCK_BYTES);
+            b[s] = load16_nt(bp + min(s, nsteps - s0 - 1) * BF16_BLOCK_BYTES);
     };
     u32x4_t b0[STEPS], b1[STEPS];
-    load_b(nb, b0);
+    if (items > 0)
+        load_b(0, b0);
     asm volatile("" ::: "memory");
 
-    constexpr int A_PER_THREAD = STEPS * 4 * WAVE / (WAVE * WAVES);
+    constexpr int A_PER_THREAD = CSTEPS * 4 * WAVE / (WAVE * WAVES);
     {
         u32x4_t av[A_PER_THREAD];
 #pragma unroll
@@ -147,62 +152,68 @@ __global__ __launch_bounds__(WAVE *WAVES) void skinny_persist_kernel(const Skinn
     }
     __syncthreads();
 
-    auto compute_store = [&](int blk, const u32x4_t *b) {
-        f32x4_t acc[4];
+    f32x4_t acc[4];
+    auto compute = [&](int i, const u32x4_t *b) {
+        const int unit = i % nunits;
+        if (unit == 0)
 #pragma unroll
-        for (int mf = 0; mf < 4; mf++)
-            acc[mf] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            for (int mf = 0; mf < 4; mf++)
+                acc[mf] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < STEPS; s++) {
-            if (s < nsteps) {
+            const int step = unit * STEPS + s;
+            if (step < nsteps) {
                 u32x4_t a[4];
 #pragma unroll
                 for (int mf = 0; mf < 4; mf++)
-                    a[mf] = lds_a[(s * 4 + mf) * WAVE + lane];
+                    a[mf] = lds_a[(step * 4 + mf) * WAVE + lane];
 #pragma unroll
                 for (int mf = 0; mf < 4; mf++)
                     if (mf < mt)
                         acc[mf] = mfma16(as_bf16x8(a[mf]), as_bf16x8(b[s]), acc[mf]);
             }
         }
-        float *P = g.P + (int64_t)split * g.p_split_stride + (int64_t)blk * SKINNY_TILE_FLOATS;
+        if (unit == nunits - 1) {
+            const int blk = nb0 + (i / nunits) * stride;
+            float *P = g.P + (int64_t)split * g.p_split_stride + (int64_t)blk * SKINNY_TILE_FLOATS;
 #pragma unroll
-        for (int mf = 0; mf < 4; mf++)
-            if (mf < mt)
-                *reinterpret_cast<f32x4_t *>(P + (mf * WAVE + lane) * 4) = acc[mf];
+            for (int mf = 0; mf < 4; mf++)
+                if (mf < mt)
+                    *reinterpret_cast<f32x4_t *>(P + (mf * WAVE + lane) * 4) = acc[mf];
+        }
     };
 
-    // Two blocks per iteration, ping-ponging the register buffers.
-    while (nb < nblocks) {
-        const int nb1 = nb + stride;
-        if (nb1 < nblocks)
-            load_b(nb1, b1);
-        compute_store(nb, b0);
-        if (nb1 >= nblocks)
+    // Two units per iteration, ping-ponging the register buffers.
+    for (int i = 0; i < items; i += 2) {
+        if (i + 1 < items)
+            load_b(i + 1, b1);
+        compute(i, b0);
+        if (i + 1 >= items)
             break;
-        const int nb2 = nb1 + stride;
-        if (nb2 < nblocks)
-            load_b(nb2, b0);
-        compute_store(nb1, b1);
-        nb = nb2;
+        if (i + 2 < items)
+            load_b(i + 2, b0);
+        compute(i + 1, b1);
     }
 }
 
-hipError_t launch_skinny_persist(const SkinnyArgs &g, int waves, int groups, hipStream_t st)
+// chunk_steps (16 or 32) is the K range of a split in 32-wide steps.
+hipError_t launch_skinny_persist(const SkinnyArgs &g, int waves, int groups, int chunk_steps, hipStream_t st)
 {
     if (g.M < 1 || g.M > SKINNY_MAX_M || g.N % 16 || g.K % BF16_STEP || groups < 1)
         return hipErrorInvalidValue;
-    const int splits = skinny_splits(g.K, 16);
-    const int steps = std::min(16 * BF16_STEP, g.K) / BF16_STEP;
-    const size_t lds = (size_t)steps * 4 * WAVE * 16;
+    const int splits = skinny_splits(g.K, chunk_steps);
     const dim3 grid(splits * groups);
-    if (waves == 4)
-        hipLaunchKernelGGL(skinny_persist_kernel<4>, grid, dim3(WAVE * 4), lds, st, g, splits);
-    else if (waves == 8)
-        hipLaunchKernelGGL(skinny_persist_kernel<8>, grid, dim3(WAVE * 8), lds, st, g, splits);
-    else
-        return hipErrorInvalidValue;
-    return hipGetLastError();
+#define MOE_PERSIST(W, U)                                                                                            \
+    if (waves == W && chunk_steps == 16 * U) {                                                                       \
+        hipLaunchKernelGGL((skinny_persist_kernel<W, U>), grid, dim3(WAVE * W), 0, st, g, splits);                   \
+        return hipGetLastError();                                                                                    \
+    }
+    MOE_PERSIST(8, 1)
+    MOE_PERSIST(8, 2)
+    MOE_PERSIST(4, 1)
+    MOE_PERSIST(4, 2)
+#undef MOE_PERSIST
+    return hipErrorInvalidValue;
 }
 
 int skinny_splits(int K, int chunk_steps)

@@ -23,7 +23,10 @@ NOLAT = LayerShape("nolat", 77, 512, 512, 32, 4, 256, 0, 0, False, "uniform", 0.
 # the dense and the grouped products, with ragged row tiles and empty experts.
 PREFILL_SMALL = LayerShape("prefill_small", 300, 1024, 512, 16, 4, 256, 1, 128, True, "zipf", 0.0, 12)
 NOLAT_TILED = LayerShape("nolat_tiled", 260, 384, 384, 8, 3, 384, 0, 0, False, "uniform", 0.0, 13)
-SMALL_SHAPES = {s.name: s for s in (SHAPES["tiny"], MID, MID_ZIPF, NOLAT, PREFILL_SMALL, NOLAT_TILED)}
+# One or two rows per expert (24 * 4 / 128 < 1): the decode expert kernels with 4-row tiles and the
+# activations staged in LDS.
+SPARSE = LayerShape("sparse", 24, 1024, 512, 128, 4, 256, 1, 128, True, "uniform", 0.0, 14)
+SMALL_SHAPES = {s.name: s for s in (SHAPES["tiny"], MID, MID_ZIPF, NOLAT, PREFILL_SMALL, NOLAT_TILED, SPARSE)}
 
 
 @pytest.fixture(scope="module", autouse=True)

@@ -429,7 +429,7 @@ moe_status router_impl(moe_handle *h, const void *x, int32_t T, const float *log
         g.K = h->Hin;
         g.split = INT_MAX;
         g.lo = OutDesc{OUT_F32, lg, E, 0, E, logit_bias};
-        MOE_LAUNCH(MOE_KERNEL_ROUTER, launch_tiled(g, false, 0, st));
+        MOE_LAUNCH(MOE_KERNEL_ROUTER, (ring_preferred(g) ? launch_ring(g, st) : launch_tiled(g, false, 0, st)));
         ta.src = lg;
     }
     return MOE_OK;
@@ -496,7 +496,7 @@ moe_status xside_impl(moe_handle *h, const void *x, int32_t T, const moe_routing
         g.split = Lt;
         g.lo = OutDesc{OUT_BF16, Z, Lt, 0, Lt, nullptr};
         g.hi = OutDesc{OUT_GLU, Acat + Lt, ldcat, Lt, INT_MAX, nullptr};
-        MOE_LAUNCH(MOE_KERNEL_XSIDE, launch_tiled(g, false, 0, st));
+        MOE_LAUNCH(MOE_KERNEL_XSIDE, (ring_preferred(g) ? launch_ring(g, st) : launch_tiled(g, false, 0, st)));
     }
     if (tiles)
         MOE_LAUNCH(MOE_KERNEL_TILEMAP, launch_tilemap(r->offsets, E, bm, tiles1, bm, tiles2, st));
@@ -572,7 +572,7 @@ moe_status experts_impl(moe_handle *h, const void *x, int32_t T, const moe_routi
         g.K = ldcat;
         g.split = INT_MAX;
         g.lo = OutDesc{OUT_BF16, out, H, 0, H, nullptr};
-        MOE_LAUNCH(MOE_KERNEL_OUT, launch_tiled(g, false, 0, st));
+        MOE_LAUNCH(MOE_KERNEL_OUT, (ring_preferred(g) ? launch_ring(g, st) : launch_tiled(g, false, 0, st)));
     }
     return MOE_OK;
 }

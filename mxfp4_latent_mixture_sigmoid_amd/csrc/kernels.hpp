@@ -45,6 +45,10 @@ hipError_t launch_gemm_dense(const GemmArgs &g, GemmShape shape, hipStream_t st)
 // Dense (g.tiles null: rows 0..M-1) or grouped (tile list, at most `max_tiles` entries).
 constexpr int TILED_BM = 128;
 hipError_t launch_tiled(const GemmArgs &g, bool mx, int max_tiles, hipStream_t st);
+// Dense BF16 product for many rows with both operands staged through LDS (256 x 256 per workgroup).
+bool ring_supported(const GemmArgs &g);
+bool ring_preferred(const GemmArgs &g);   // supported and at least 256 tiles
+hipError_t launch_ring(const GemmArgs &g, hipStream_t st);
 // A-stationary grouped MXFP4 product for K <= AS_MAX_K (tile list required, BF16 output only).
 constexpr int AS_MAX_K = 512;
 bool astat_supported(const GemmArgs &g);

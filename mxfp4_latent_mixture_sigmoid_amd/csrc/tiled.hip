@@ -311,6 +311,208 @@ static hipError_t launch_tiled_t(const GemmArgs &g, int grid_m, hipStream_t st)
     return hipGetLastError();
 }
 
+// ---- Ring product: dense BF16 C = A . B^T for many rows (M, N >= 256) with both operands staged
+// through LDS. The workgroup computes 256 x 256 outputs. K advances in 32-input stages; RG_NBUF
+// stages are resident in LDS, each 32 KiB: 16 operand-order 1 KiB blocks of A (16 rows each) and 16
+// of B (the packed fragment blocks). Both are moved by direct global->LDS loads -- one wave instruction fills one
+// 1 KiB block, no register round trip -- issued RG_NBUF - 1 stages ahead; a wave waits for its own
+// loads of the next stage (vmcnt) and a barrier makes every wave's loads visible. K must be a
+// multiple of 32; the lo/hi output split must leave both parts a multiple of 128 columns.
+constexpr int RG_BM = 256, RG_BN = 256, RG_WM = 128;
+constexpr int RG_MF = RG_WM / 16;                          // 8 row fragments per wave
+constexpr int RG_AF = RG_BM / 16, RG_BF = RG_BN / 16;      // 16 + 16 blocks per stage
+constexpr int RG_NBUF = 4;
+
+// s_waitcnt immediate that waits until at most n vector-memory operations are outstanding
+constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | (((n >> 4) & 3) << 14); }
+
+// Eight waves, 2 x 4, each 128 x 64 outputs (128 accumulators): two waves per SIMD, which cover
+// each other's waits (measured 1.07 PFLOP/s against 0.82 for four waves of 128 x 128 at one wave per
+// SIMD with the next stage's fragments read during the MFMAs).
+__global__ __launch_bounds__(WAVE * 8) void ring_kernel(const GemmArgs g, int gx, int gy)
+{
+    constexpr int NWN = 4, NW = 2 * NWN, RG_WN = RG_BN / NWN, RG_NF = RG_WN / 16;
+    constexpr int RG_LOADS = (RG_AF + RG_BF) / NW;        // loads per wave per stage
+    __shared__ u32x4_t lds[RG_NBUF][RG_AF + RG_BF][WAVE];
+    const int lane = threadIdx.x & (WAVE - 1);
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE);
+    const int wm = wv / NWN, wn = wv % NWN;
+    int bx, by;
+    if (!tiled_item(g, gx, gy, bx, by))
+        return;
+    // The last tile of each axis is shifted back to end at M (N): it overlaps its neighbour and
+    // recomputes identical values in the same order, so no load or store leaves the matrices.
+    const int m0 = min(by * RG_BM, g.M - RG_BM), n0 = min(bx * RG_BN, g.N - RG_BN);
+    const int nst = g.K / BF16_STEP;
+
+    // This wave's loads: blocks wv*L .. wv*L+L-1 of a stage (the first half of the waves load A, the
+    // rest B). Within a stage they are one base plus a fixed stride: 16 rows of A, or one row-block
+    // stride of B's current 16-step chunk.
+    const bool loads_a = wv < NW / 2;
+    const int li = loads_a ? wv : wv - NW / 2;
+    const uint8_t *a_base = reinterpret_cast<const uint8_t *>(
+        g.A + (int64_t)(m0 + li * (RG_LOADS * 16) + (lane & 15)) * g.lda + 8 * (lane >> 4));
+    const int bnb0 = n0 / 16 + li * RG_LOADS;
+    auto issue = [&](int s) {                // stage min(s, nst - 1) into buffer s % RG_NBUF
+        const int ss = min(s, nst - 1), buf = s % RG_NBUF;
+        const uint8_t *base;
+        int64_t stride;
+        if (loads_a) {
+            base = a_base + ss * (BF16_STEP * 2);
+            stride = 16 * g.lda * 2;
+        } else {
+            const int64_t rest = nst - ss / BF16_CHUNK_STEPS * BF16_CHUNK_STEPS;
+            base = g.B + bf16_block_index(bnb0, ss, g.N, g.K) * BF16_BLOCK_BYTES + lane * 16;
+            stride = (rest < BF16_CHUNK_STEPS ? rest : BF16_CHUNK_STEPS) * BF16_BLOCK_BYTES;
+        }
+#pragma unroll
+        for (int i = 0; i < RG_LOADS; i++)
+            __builtin_amdgcn_global_load_lds(base + i * stride,
+                                             (__attribute__((address_space(3))) void *)&lds[buf][wv * RG_LOADS + i][0],
+                                             16, 0, 0);
+    };
+
+    f32x4_t acc[RG_MF][RG_NF];
+#pragma unroll
+    for (int f = 0; f < RG_MF; f++)
+#pragma unroll
+        for (int j = 0; j < RG_NF; j++)
+            acc[f][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    auto read_frags = [&](int s, u32x4_t *bf, u32x4_t *af) {
+        const int buf = s % RG_NBUF;
+#pragma unroll
+        for (int j = 0; j < RG_NF; j++)
+            bf[j] = lds[buf][RG_AF + wn * RG_NF + j][lane];
+#pragma unroll
+        for (int f = 0; f < RG_MF; f++)
+            af[f] = lds[buf][wm * RG_MF + f][lane];
+    };
+    // Wait until only the later stages' loads of this wave are outstanding, then a barrier makes every
+    // wave's loads of this stage visible (and all waves are past the previous stage).
+    auto sync_stages = [&]() {
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm((RG_NBUF - 2) * RG_LOADS));
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+    };
+    auto mma = [&](const u32x4_t *bc, const u32x4_t *ac) {
+#pragma unroll
+        for (int j = 0; j < RG_NF; j++)
+#pragma unroll
+            for (int f = 0; f < RG_MF; f++)
+                acc[f][j] = mfma16(as_bf16x8(bc[j]), as_bf16x8(ac[f]), acc[f][j]);
+    };
+#pragma unroll
+    for (int s = 0; s < RG_NBUF - 1; s++)
+        issue(s);
+    for (int s = 0; s < nst; s++) {
+        sync_stages();                        // stage s landed for every wave; buffer s - 1 free
+        issue(s + RG_NBUF - 1);
+        u32x4_t bc[RG_NF], ac[RG_MF];
+        read_frags(s, bc, ac);
+        mma(bc, ac);
+    }
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // no load may land in LDS after the workgroup ends
+
+    // Epilogue: lane (q, c) of fragment (f, j) holds row 16 f + c and columns 16 j + 4 q .. +3.
+    const int n0w = n0 + wn * RG_WN;
+    if (n0w >= g.N)
+        return;
+    const OutDesc d = (n0w < g.split) ? g.lo : g.hi;
+    const int q = lane >> 4;
+    const int rbase = m0 + wm * RG_WM + (lane & 15);
+    if (d.kind == OUT_GLU) {
+        uint16_t *o = reinterpret_cast<uint16_t *>(d.ptr);
+#pragma unroll
+        for (int p = 0; p < RG_NF / 2; p++) {
+            if (n0w + 32 * p + 32 > g.N)
+                break;
+            const int oc = (n0w - d.col0) / 2 + p * 16 + 4 * q;
+#pragma unroll
+            for (int f = 0; f < RG_MF; f++) {
+                const int r = rbase + f * 16;
+                uint32_t hv[4];
+#pragma unroll
+                for (int i = 0; i < 4; i++)
+                    hv[i] = f32_to_bf16_bits(silu_f32(acc[f][2 * p][i]) * acc[f][2 * p + 1][i]);
+                *reinterpret_cast<uint2 *>(o + (int64_t)r * d.ld + oc) =
+                    make_uint2(hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16));
+            }
+        }
+        return;
+    }
+#pragma unroll
+    for (int j = 0; j < RG_NF; j++) {
+        const int n = n0w + j * 16 + 4 * q;
+        if (n >= d.n_valid)
+            continue;
+        const bool full = n + 3 < d.n_valid;
+        float bias[4] = {0.f, 0.f, 0.f, 0.f};
+        if (d.kind == OUT_F32 && d.bias)
+#pragma unroll
+            for (int i = 0; i < 4; i++)
+                bias[i] = (n + i < d.n_valid) ? d.bias[n + i] : 0.f;
+#pragma unroll
+        for (int f = 0; f < RG_MF; f++) {
+            const int r = rbase + f * 16;
+            if (d.kind == OUT_F32) {
+                float *dst = reinterpret_cast<float *>(d.ptr) + (int64_t)r * d.ld + (n - d.col0);
+                if (full) {
+                    *reinterpret_cast<f32x4_t *>(dst) = f32x4_t{acc[f][j][0] + bias[0], acc[f][j][1] + bias[1],
+                                                               acc[f][j][2] + bias[2], acc[f][j][3] + bias[3]};
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; i++)
+                        if (n + i < d.n_valid)
+                            dst[i] = acc[f][j][i] + bias[i];
+                }
+            } else {
+                uint16_t *dst = reinterpret_cast<uint16_t *>(d.ptr) + (int64_t)r * d.ld + (n - d.col0);
+                if (full) {
+                    *reinterpret_cast<uint2 *>(dst) =
+                        make_uint2(f32_to_bf16_bits(acc[f][j][0]) | (f32_to_bf16_bits(acc[f][j][1]) << 16),
+                                   f32_to_bf16_bits(acc[f][j][2]) | (f32_to_bf16_bits(acc[f][j][3]) << 16));
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; i++)
+                        if (n + i < d.n_valid)
+                            dst[i] = (uint16_t)f32_to_bf16_bits(acc[f][j][i]);
+                }
+            }
+        }
+    }
+}
+
+bool ring_supported(const GemmArgs &g)
+{
+    auto out_ok = [](const OutDesc &d) {
+        return d.ld % 4 == 0 && d.col0 % 4 == 0 && reinterpret_cast<uintptr_t>(d.ptr) % 16 == 0;
+    };
+    return !g.tiles && !g.a_index && g.M >= RG_BM && g.N >= RG_BN && g.N % 16 == 0 && g.K > 0 && g.K % BF16_STEP == 0 &&
+           g.lda % 8 == 0 && reinterpret_cast<uintptr_t>(g.A) % 16 == 0 && out_ok(g.lo) &&
+           (g.split >= g.N || (g.split % 128 == 0 && (g.N - g.split) % 128 == 0 && out_ok(g.hi)));
+}
+
+// Ring tiles fill the GPU (256 CUs) only from 256 tiles on; below that (e.g. the router's 896
+// columns) the 128 x 256 tiled kernel keeps more CUs busy.
+bool ring_preferred(const GemmArgs &g)
+{
+    return ring_supported(g) && (int64_t)((g.M + RG_BM - 1) / RG_BM) * ((g.N + RG_BN - 1) / RG_BN) >= 256;
+}
+
+hipError_t launch_ring(const GemmArgs &g, hipStream_t st)
+{
+    if (!ring_supported(g))
+        return hipErrorInvalidValue;
+    const int gx = (g.N + RG_BN - 1) / RG_BN, gy = (g.M + RG_BM - 1) / RG_BM;
+    const int64_t grid = ((int64_t)gx * gy + TL_XCDS - 1) / TL_XCDS * TL_XCDS;
+    if (grid > INT32_MAX)
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL(ring_kernel, dim3((unsigned)grid), dim3(WAVE * 8), 0, st, g, gx, gy);
+    return hipGetLastError();
+}
+
 // ---- A-stationary grouped MXFP4 product for short K (the down projection, K = I <= 512).
 // The workgroup stages its whole 128-row A tile (gathered rows, 128 x K BF16, at most 128 KiB) into
 // LDS once, in the operand order above, with direct global->LDS loads (one wave instruction fills

@@ -22,7 +22,10 @@ hipError_t launch_tilemap(const int32_t *offsets, int E, int bm1, int32_t *tiles
 }
 
 // zc[t, c] = bf16(sum over slots j = 0..K-1, in order, of w[t, j] * Y[inv[t K + j], c]).
-// Each thread owns 8 consecutive columns of one token (16-byte loads and store); FP32 sums.
+// Each thread owns 8 consecutive columns of one token (16-byte loads and store); FP32 sums. Slots
+// go in batches of CB: the batch's rows and weights, then all its row loads, are issued before any
+// is used, so a wave keeps CB loads in flight; the sums still run in slot order.
+constexpr int CB = 8;
 __global__ __launch_bounds__(64) void combine_kernel(const uint16_t *__restrict__ Y, int Lt,
                                                      const int32_t *__restrict__ inv, const float *__restrict__ w,
                                                      int K, uint16_t *__restrict__ out, int64_t ldo)
@@ -31,17 +34,35 @@ __global__ __launch_bounds__(64) void combine_kernel(const uint16_t *__restrict_
     const int c8 = blockIdx.y * 64 + threadIdx.x;
     if (c8 * 8 >= Lt)
         return;
+    const int32_t *it = inv + (int64_t)t * K;
+    const float *wt = w + (int64_t)t * K;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < K; j++) {
-        const int64_t r = inv[(int64_t)t * K + j];
-        const float wj = w[(int64_t)t * K + j];
-        const u32x4_t y = load16(Y + r * Lt + c8 * 8);
+    auto add = [&](float wj, const u32x4_t &y) {
 #pragma unroll
         for (int i = 0; i < 4; i++) {
             acc[2 * i] += wj * bf16_bits_to_f32(y[i] & 0xFFFFu);
             acc[2 * i + 1] += wj * bf16_bits_to_f32(y[i] >> 16);
         }
+    };
+    int j0 = 0;
+    for (; j0 + CB <= K; j0 += CB) {
+        int64_t r[CB];
+        float wj[CB];
+#pragma unroll
+        for (int u = 0; u < CB; u++) {
+            r[u] = it[j0 + u];
+            wj[u] = wt[j0 + u];
+        }
+        u32x4_t y[CB];
+#pragma unroll
+        for (int u = 0; u < CB; u++)
+            y[u] = load16(Y + r[u] * Lt + c8 * 8);
+#pragma unroll
+        for (int u = 0; u < CB; u++)
+            add(wj[u], y[u]);
     }
+    for (; j0 < K; j0++)
+        add(wt[j0], load16(Y + (int64_t)it[j0] * Lt + c8 * 8));
     u32x4_t o;
 #pragma unroll
     for (int i = 0; i < 4; i++)

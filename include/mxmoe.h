@@ -134,14 +134,11 @@ moe_status moe_forward(moe_handle *h, const void *x, int32_t T, const moe_routin
                        void *workspace, size_t workspace_bytes, void *stream);
 
 /* moe_route (with logits_in = NULL) followed by moe_forward, in one call, with results identical
- * bit for bit to the two calls. With latent projections and more than 64 tokens, the x-side
- * products (latent down-projection, shared gate/up), which do not depend on the routing, run on a
- * second stream owned by the handle, concurrently with the top-K and grouping on `stream`;
- * `stream` waits for both before the expert products, so all of the call's work is ordered after
- * earlier work on `stream` and before later work on it. With 64 tokens or fewer everything runs
- * on `stream` (the fork and join would cost more than they hide).
- * Arguments as for the two calls; logits_out may be NULL and must not alias x or out. Calls on
- * one handle must not overlap (they share its second stream). */
+ * bit for bit to the two calls. With latent projections the router and the x-side products
+ * (latent down-projection, shared gate/up), which both read only x, run as one product over a
+ * combined copy of their weights kept in the packed buffer, so x is read once and one launch
+ * streams both weight matrices. All work runs on `stream`, in order.
+ * Arguments as for the two calls; logits_out may be NULL and must not alias x or out. */
 moe_status moe_route_forward(moe_handle *h, const void *x, int32_t T, const float *logit_bias,
                              float *logits_out, const moe_routing *r, void *out, void *workspace,
                              size_t workspace_bytes, void *stream);
@@ -163,7 +160,8 @@ typedef enum {
     MOE_KERNEL_COMBINE = 7,  /* gate-weighted combine                               */
     MOE_KERNEL_OUT = 8,      /* up-projection + shared down-projection              */
     MOE_KERNEL_XSIDE_EPI = 9,/* few-token x-side partial sums, GLU and tile lists   */
-    MOE_KERNEL_OUT_EPI = 10  /* few-token output partial sums                       */
+    MOE_KERNEL_OUT_EPI = 10, /* few-token output partial sums                       */
+    MOE_KERNEL_ROUTER_XSIDE = 11 /* router + x-side product as one (moe_route_forward) */
 } moe_kernel;
 
 /* Profiling hook (benchmarks, tests): after moe_profile_begin, every kernel launch of moe_route

@@ -165,7 +165,7 @@ def unpack_expert(h, e: int, which: int, out, stream=None) -> None:
 
 
 KERNELS = ("router", "topk", "permute", "xside", "tilemap", "gateup", "down", "combine", "out", "xside_epi",
-           "out_epi")
+           "out_epi", "router_xside")
 
 
 def profile_begin(h, max_launches: int) -> None:

@@ -15,12 +15,10 @@ struct moe_handle {
     moe_config cfg;
     int Hin;             // width of x and of the router's input
     int E_pad;           // router rows padded to 16
+    int E_rx;            // router rows padded to 64 in the combined router + x-side matrix
     uint8_t *packed;
-    int64_t off_router, off_xside, off_outside, off_gateup, off_down;
+    int64_t off_router, off_xside, off_rx, off_outside, off_gateup, off_down;
     int64_t gateup_stride, down_stride;   // packed bytes per expert
-    // moe_route_forward: second stream for the x-side products, fork / join events (host objects)
-    hipStream_t side = nullptr;
-    hipEvent_t fork = nullptr, join = nullptr;
     // profiling hook state
     bool prof = false;
     int prof_max = 0;
@@ -43,6 +41,11 @@ constexpr int SKINNY_XSTEPS = 16;  // ... and of the few-token x-side and output
 // 9 x 28 = 252 workgroups at K = 7168 and 4352; measured best of 18..72 groups and 512 / 1024-wide
 // splits at 64 tokens).
 constexpr int XSIDE_GROUPS = 18, OUT_GROUPS = 28;
+// ... and of the combined router + x-side product (6016 columns at the full size)
+constexpr int RX_GROUPS = 18;
+// Router rows in the combined router + x-side matrix: a multiple of the 64-column wave width, so
+// that no wave of the many-token product straddles the logits and the z columns.
+int64_t router_rows_rx(const moe_config *c) { return ((int64_t)c->n_experts + 63) / 64 * 64; }
 
 int64_t align_up(int64_t v) { return (v + ALIGN - 1) / ALIGN * ALIGN; }
 
@@ -72,7 +75,7 @@ bool valid_config(const moe_config *c)
 }
 
 struct PackedLayout {
-    int64_t router, xside, outside, gateup, down, total, gateup_stride, down_stride;
+    int64_t router, xside, rx, outside, gateup, down, total, gateup_stride, down_stride;
 };
 
 PackedLayout packed_layout(const moe_config *c)
@@ -87,6 +90,10 @@ PackedLayout packed_layout(const moe_config *c)
     L.xside = off;
     if (c->has_latent_proj)
         off = align_up(off + bf16_packed_bytes(Lt + 2 * S * Is, H));
+    // the router and x-side rows once more as one matrix, for moe_route_forward's single product
+    L.rx = off;
+    if (c->has_latent_proj)
+        off = align_up(off + bf16_packed_bytes(router_rows_rx(c) + Lt + 2 * S * Is, H));
     L.outside = off;
     if (c->has_latent_proj)
         off = align_up(off + bf16_packed_bytes(H, Lt + S * Is));
@@ -142,11 +149,12 @@ WsLayout ws_layout(const moe_config *c, int64_t T)
     L.partials = off;
     L.rpartials = off;
     if (T <= SKINNY_MAX_M) {   // split-K partial tiles of the few-token dense products
-        // The router's partials and those of the x-side / output products live side by side, so
-        // the router and the x-side product can run concurrently (moe_route_forward).
-        const int64_t Hin = c->has_latent_proj ? c->hidden : c->latent, E_pad = (E + 15) / 16 * 16;
+        // The router's partials and those of the x-side / output products are adjacent, so that
+        // the combined router + x-side product of moe_route_forward covers both regions.
+        const int64_t Hin = c->has_latent_proj ? c->hidden : c->latent;
+        const int64_t Er = c->has_latent_proj ? router_rows_rx(c) : (E + 15) / 16 * 16;
         const int64_t R = SKINNY_MAX_M;   // partial tiles keep 64 rows whatever T is
-        off = align_up(off + (int64_t)skinny_splits((int)Hin, SKINNY_STEPS) * R * E_pad * 4);
+        off = align_up(off + (int64_t)skinny_splits((int)Hin, SKINNY_STEPS) * R * Er * 4);
         L.partials = off;
         if (c->has_latent_proj) {
             const int64_t H = c->hidden;
@@ -282,6 +290,8 @@ moe_status moe_create(const moe_config *cfg, const moe_weights *w, void *packed,
     h->packed = static_cast<uint8_t *>(packed);
     h->off_router = L.router;
     h->off_xside = L.xside;
+    h->off_rx = L.rx;
+    h->E_rx = (int)router_rows_rx(cfg);
     h->off_outside = L.outside;
     h->off_gateup = L.gateup;
     h->off_down = L.down;
@@ -298,6 +308,10 @@ moe_status moe_create(const moe_config *cfg, const moe_weights *w, void *packed,
                               static_cast<const uint16_t *>(w->sh_gate), static_cast<const uint16_t *>(w->sh_up), Lt,
                               H, S, Is, st);
     if (e == hipSuccess && lat)
+        e = launch_pack_router_xside(h->packed + L.rx, static_cast<const uint16_t *>(w->w_router), E, h->E_rx,
+                                     static_cast<const uint16_t *>(w->w_down), static_cast<const uint16_t *>(w->sh_gate),
+                                     static_cast<const uint16_t *>(w->sh_up), Lt, H, S, Is, st);
+    if (e == hipSuccess && lat)
         e = launch_pack_outside(h->packed + L.outside, static_cast<const uint16_t *>(w->w_up),
                                 static_cast<const uint16_t *>(w->sh_down), Lt, H, S, Is, st);
     if (e == hipSuccess)
@@ -307,13 +321,6 @@ moe_status moe_create(const moe_config *cfg, const moe_weights *w, void *packed,
     if (e == hipSuccess)
         e = launch_pack_down(h->packed + L.down, static_cast<const uint8_t *>(w->down_codes),
                              static_cast<const uint8_t *>(w->down_scales), E, I, Lt, st);
-    // moe_route_forward's second stream (default priority) and its fork / join events
-    if (e == hipSuccess)
-        e = hipStreamCreateWithFlags(&h->side, hipStreamNonBlocking);
-    if (e == hipSuccess)
-        e = hipEventCreateWithFlags(&h->fork, hipEventDisableTiming);
-    if (e == hipSuccess)
-        e = hipEventCreateWithFlags(&h->join, hipEventDisableTiming);
     if (e != hipSuccess) {
         moe_destroy(h);
         return MOE_ERR_HIP;
@@ -376,12 +383,6 @@ void moe_destroy(moe_handle *h)
     if (!h)
         return;
     prof_clear(h);
-    if (h->join)
-        (void)hipEventDestroy(h->join);
-    if (h->fork)
-        (void)hipEventDestroy(h->fork);
-    if (h->side)
-        (void)hipStreamDestroy(h->side);
     delete h;
 }
 
@@ -501,6 +502,72 @@ moe_status xside_impl(moe_handle *h, const void *x, int32_t T, const moe_routing
     if (tiles)
         MOE_LAUNCH(MOE_KERNEL_TILEMAP, launch_tilemap(r->offsets, E, bm, tiles1, bm, tiles2, st));
     return MOE_OK;
+}
+
+// moe_route_forward with the latent projections: the router and the x-side products as one
+// product over the combined [router rows (zero-padded to E_rx) | x-side rows] matrix, so that x is
+// read once and one launch streams both weight matrices; then top-K and grouping. Few tokens: the
+// product leaves split-K partials, the top-K kernel sums the router columns' and the x-side
+// epilogue (which also builds the tile lists) the rest. Many tokens: the product's epilogue writes
+// the logits (+bias), z and the shared GLU directly, and the grouping builds the tile lists.
+// Every output element is computed in the same order as by the separate products.
+moe_status front_impl(moe_handle *h, const void *x, int32_t T, const float *logit_bias, float *logits_out,
+                      const moe_routing *r, const WsLayout &W, uint8_t *ws, hipStream_t st)
+{
+    const moe_config *c = &h->cfg;
+    const int E = c->n_experts, K = c->top_k, Lt = c->latent, H = c->hidden;
+    const int S = c->n_shared, Is = S ? c->shared_inter : 0;
+    const int ldcat = Lt + S * Is, Nx = Lt + 2 * S * Is, Erx = h->E_rx, Nrx = Erx + Nx;
+    const int bm = expert_bm(c, T);
+    uint16_t *Z = reinterpret_cast<uint16_t *>(ws + W.z);
+    uint16_t *Acat = reinterpret_cast<uint16_t *>(ws + W.acat);
+    TopkArgs ta{};
+    ta.T = T;
+    ta.E = E;
+    ta.K = K;
+    ta.ids = r->topk_ids;
+    ta.w = r->topk_w;
+    ta.ld = E;
+    if (T <= SKINNY_MAX_M) {
+        // the partials of all Nrx columns fill the router's and the x-side's partial regions, which
+        // are adjacent in the workspace
+        float *P = reinterpret_cast<float *>(ws + W.rpartials);
+        const int64_t pstride = (int64_t)(Nrx / 16) * SKINNY_TILE_FLOATS;
+        const int splits = skinny_splits(H, SKINNY_XSTEPS);
+        SkinnyArgs g{static_cast<const uint16_t *>(x), H, T, h->packed + h->off_rx, Nrx, H, P, pstride};
+        MOE_LAUNCH(MOE_KERNEL_ROUTER_XSIDE, launch_skinny_persist(g, 8, RX_GROUPS, SKINNY_XSTEPS, st));
+        ta.src = P;
+        ta.partials = 1;
+        ta.split_stride = pstride;
+        ta.splits = splits;
+        ta.bias = logit_bias;
+        ta.logits_out = logits_out;
+        moe_status e = select_impl(h, T, ta, r, W, ws, st, false);
+        if (e != MOE_OK)
+            return e;
+        XsideEpiArgs ea{P + (int64_t)(Erx / 16) * SKINNY_TILE_FLOATS, pstride, splits, T, Nx, Lt, 2 * S * Is, Z,
+                        Acat, ldcat, r->offsets, E, bm, bm,
+                        reinterpret_cast<int32_t *>(ws + W.tiles1), reinterpret_cast<int32_t *>(ws + W.tiles2)};
+        MOE_LAUNCH(MOE_KERNEL_XSIDE_EPI, launch_xside_epilogue(ea, st));
+        return MOE_OK;
+    }
+    float *lg = logits_out ? logits_out : reinterpret_cast<float *>(ws + W.logits);
+    GemmArgs g{};
+    g.A = static_cast<const uint16_t *>(x);
+    g.lda = H;
+    g.B = h->packed + h->off_rx;
+    g.M = T;
+    g.N = Nrx;
+    g.K = H;
+    g.split = Erx;
+    g.split2 = Erx + Lt;
+    g.lo = OutDesc{OUT_F32, lg, E, 0, E, logit_bias};
+    g.hi = OutDesc{OUT_BF16, Z, Lt, Erx, Erx + Lt, nullptr};
+    g.top = OutDesc{OUT_GLU, Acat + Lt, ldcat, Erx + Lt, INT_MAX, nullptr};
+    MOE_LAUNCH(MOE_KERNEL_ROUTER_XSIDE, (ring_preferred(g) ? launch_ring(g, st) : launch_tiled(g, false, 0, st)));
+    ta.src = lg;
+    ta.splits = 1;
+    return select_impl(h, T, ta, r, W, ws, st, true);
 }
 
 // Expert products, combine and the output product; needs the routing, the x-side results and the
@@ -667,38 +734,16 @@ moe_status moe_route_forward(moe_handle *h, const void *x, int32_t T, const floa
         return e;
     uint8_t *ws = static_cast<uint8_t *>(workspace);
     hipStream_t st = static_cast<hipStream_t>(stream);
-    TopkArgs ta;
-    if ((e = router_impl(h, x, T, logit_bias, nullptr, logits_out, r, W, ws, st, ta)) != MOE_OK)
+    if (h->cfg.has_latent_proj)
+        e = front_impl(h, x, T, logit_bias, logits_out, r, W, ws, st);
+    else {   // no x-side products: router, then the grouping builds the tile lists
+        TopkArgs ta;
+        e = router_impl(h, x, T, logit_bias, nullptr, logits_out, r, W, ws, st, ta);
+        if (e == MOE_OK)
+            e = select_impl(h, T, ta, r, W, ws, st, true);
+    }
+    if (e != MOE_OK)
         return e;
-    if (!h->cfg.has_latent_proj) {   // no x-side products: the grouping builds the tile lists
-        if ((e = select_impl(h, T, ta, r, W, ws, st, true)) != MOE_OK)
-            return e;
-        return experts_impl(h, x, T, r, out, W, ws, st);
-    }
-    if (T <= SKINNY_MAX_M) {
-        // Few tokens: the fork and join cost more than the overlap hides (measured at 64 tokens),
-        // so the call is the two calls' sequence on the caller's stream; the few-token x-side
-        // epilogue builds the tile lists alongside its own work, off the critical path.
-        if ((e = select_impl(h, T, ta, r, W, ws, st, false)) != MOE_OK)
-            return e;
-        if ((e = xside_impl(h, x, T, r, W, ws, st, true)) != MOE_OK)
-            return e;
-        return experts_impl(h, x, T, r, out, W, ws, st);
-    }
-    // fork after the router product (which wants the whole GPU): the x-side product then overlaps
-    // the top-K and grouping
-    if (hipEventRecord(h->fork, st) != hipSuccess || hipStreamWaitEvent(h->side, h->fork, 0) != hipSuccess)
-        return MOE_ERR_HIP;
-    const moe_status ex = xside_impl(h, x, T, r, W, ws, h->side, false);
-    const moe_status ro = select_impl(h, T, ta, r, W, ws, st, true);
-    // join: always, so that the side stream never runs past the call's stream, even after an error
-    const bool joined = hipEventRecord(h->join, h->side) == hipSuccess && hipStreamWaitEvent(st, h->join, 0) == hipSuccess;
-    if (ex != MOE_OK)
-        return ex;
-    if (ro != MOE_OK)
-        return ro;
-    if (!joined)
-        return MOE_ERR_HIP;
     return experts_impl(h, x, T, r, out, W, ws, st);
 }
 

@@ -27,9 +27,17 @@ struct GemmArgs {
     int64_t b_stride;        // bytes between consecutive groups' packed weights
     int M, N, K;             // M: dense row count (ignored with a tile list)
     const int32_t *tiles;    // nullable: [0] = tile count, from element 4: int4 (group, m0, m1, -)
-    int split;               // logical columns < split use `lo`, the rest `hi`
-    OutDesc lo, hi;
+    int split;               // logical columns < split use `lo`, the rest `hi` ...
+    int split2;              // ... and, when split2 > 0, columns >= split2 use `top`
+    OutDesc lo, hi, top;
 };
+
+// Output descriptor for the columns from logical column n on. Region boundaries (split, split2)
+// are multiples of the 64-column wave width, so n = a wave's first column picks one region.
+__device__ inline OutDesc out_region(const GemmArgs &g, int n)
+{
+    return n < g.split ? g.lo : (g.split2 > 0 && n >= g.split2) ? g.top : g.hi;
+}
 
 enum GemmShape {
     GEMM_SKINNY_N16 = 0,     // dense, 64 rows x 16 columns per workgroup, K split over 8 waves
@@ -60,6 +68,10 @@ hipError_t launch_pack_router(uint8_t *dst, const uint16_t *w, int64_t E, int64_
                               hipStream_t st);
 hipError_t launch_pack_xside(uint8_t *dst, const uint16_t *wdn, const uint16_t *sg, const uint16_t *su,
                              int64_t Lt, int64_t H, int64_t S, int64_t Is, hipStream_t st);
+// Router rows (zero-padded to E_pad) followed by the x-side rows, one packed [E_pad + Nx, H] matrix.
+hipError_t launch_pack_router_xside(uint8_t *dst, const uint16_t *wr, int64_t E, int64_t E_pad, const uint16_t *wdn,
+                                   const uint16_t *sg, const uint16_t *su, int64_t Lt, int64_t H, int64_t S, int64_t Is,
+                                   hipStream_t st);
 hipError_t launch_pack_outside(uint8_t *dst, const uint16_t *wup, const uint16_t *sd, int64_t Lt,
                                int64_t H, int64_t S, int64_t Is, hipStream_t st);
 hipError_t launch_pack_gateup(uint8_t *dst, const uint8_t *gc, const uint8_t *gs, const uint8_t *uc,

@@ -46,6 +46,13 @@ struct FetchXside {           // [Lt + 2 S Is, H]: down-projection rows, then pe
     }
 };
 
+struct FetchRouterXside {     // [E_pad + Lt + 2 S Is, H]: router rows (zero past E), then the x-side rows
+    FetchRouter r;
+    FetchXside x;
+    int64_t E_pad;
+    __device__ u32x4_t operator()(int64_t n, int64_t k) const { return n < E_pad ? r(n, k) : x(n - E_pad, k); }
+};
+
 struct FetchOutside {         // [H, Lt + S Is]: up-projection row n, then shared down rows n
     const uint16_t *wup, *sd;
     int64_t Lt, H, Is;
@@ -159,6 +166,17 @@ hipError_t launch_pack_xside(uint8_t *dst, const uint16_t *wdn, const uint16_t *
     const int64_t thr = (N / 16) * (H / BF16_STEP) * WAVE;
     hipLaunchKernelGGL(pack_bf16_kernel<FetchXside>, dim3(grid_for(thr, 256)), dim3(256), 0, st, dst, N,
                        H, FetchXside{wdn, sg, su, Lt, H, Is});
+    return hipGetLastError();
+}
+
+hipError_t launch_pack_router_xside(uint8_t *dst, const uint16_t *wr, int64_t E, int64_t E_pad, const uint16_t *wdn,
+                                   const uint16_t *sg, const uint16_t *su, int64_t Lt, int64_t H, int64_t S, int64_t Is,
+                                   hipStream_t st)
+{
+    const int64_t N = E_pad + Lt + 2 * S * Is;
+    const int64_t thr = (N / 16) * (H / BF16_STEP) * WAVE;
+    hipLaunchKernelGGL(pack_bf16_kernel<FetchRouterXside>, dim3(grid_for(thr, 256)), dim3(256), 0, st, dst, N, H,
+                       FetchRouterXside{FetchRouter{wr, E, H}, FetchXside{wdn, sg, su, Lt, H, Is}, E_pad});
     return hipGetLastError();
 }
 

@@ -221,7 +221,7 @@ __global__ __launch_bounds__(WAVE * 4) void tiled_kernel(const GemmArgs g, int g
     // ---- epilogue. The weights are the first MFMA operand, so lane (q = l / 16, c = l % 16) of
     // fragment (f, nf) holds token row f*16 + c and the four consecutive columns nf*16 + 4q + i:
     // one 8-byte (BF16) or 16-byte (FP32) store per fragment when the output is aligned for it.
-    const OutDesc d = (n0 < g.split) ? g.lo : g.hi;
+    const OutDesc d = out_region(g, n0);
     const int q = lane >> 4;
     const int rbase = m0 + wm * TL_WAVE_M + (lane & 15);
     const bool vec = (d.ld % 4 == 0) && (d.col0 % 4 == 0) &&
@@ -317,7 +317,7 @@ static hipError_t launch_tiled_t(const GemmArgs &g, int grid_m, hipStream_t st)
 // of B (the packed fragment blocks). Both are moved by direct global->LDS loads -- one wave instruction fills one
 // 1 KiB block, no register round trip -- issued RG_NBUF - 1 stages ahead; a wave waits for its own
 // loads of the next stage (vmcnt) and a barrier makes every wave's loads visible. K must be a
-// multiple of 32; the lo/hi output split must leave both parts a multiple of 128 columns.
+// multiple of 32; N and the output region boundaries must be multiples of 64 columns.
 constexpr int RG_BM = 256, RG_BN = 256, RG_WM = 128;
 constexpr int RG_MF = RG_WM / 16;                          // 8 row fragments per wave
 constexpr int RG_AF = RG_BM / 16, RG_BF = RG_BN / 16;      // 16 + 16 blocks per stage
@@ -419,7 +419,7 @@ __global__ __launch_bounds__(WAVE * 8) void ring_kernel(const GemmArgs g, int gx
     const int n0w = n0 + wn * RG_WN;
     if (n0w >= g.N)
         return;
-    const OutDesc d = (n0w < g.split) ? g.lo : g.hi;
+    const OutDesc d = out_region(g, n0w);
     const int q = lane >> 4;
     const int rbase = m0 + wm * RG_WM + (lane & 15);
     if (d.kind == OUT_GLU) {
@@ -489,9 +489,12 @@ bool ring_supported(const GemmArgs &g)
     auto out_ok = [](const OutDesc &d) {
         return d.ld % 4 == 0 && d.col0 % 4 == 0 && reinterpret_cast<uintptr_t>(d.ptr) % 16 == 0;
     };
-    return !g.tiles && !g.a_index && g.M >= RG_BM && g.N >= RG_BN && g.N % 16 == 0 && g.K > 0 && g.K % BF16_STEP == 0 &&
+    // every wave's 64 columns (the shifted last tile included) lie in one output region
+    const bool two = g.split < g.N, three = g.split2 > 0 && g.split2 < g.N;
+    return !g.tiles && !g.a_index && g.M >= RG_BM && g.N >= RG_BN && g.K > 0 && g.K % BF16_STEP == 0 &&
            g.lda % 8 == 0 && reinterpret_cast<uintptr_t>(g.A) % 16 == 0 && out_ok(g.lo) &&
-           (g.split >= g.N || (g.split % 128 == 0 && (g.N - g.split) % 128 == 0 && out_ok(g.hi)));
+           (g.N % 64 == 0 || (!two && !three && g.N % 16 == 0)) && (!two || (g.split % 64 == 0 && out_ok(g.hi))) &&
+           (!three || (two && g.split2 > g.split && g.split2 % 64 == 0 && out_ok(g.top)));
 }
 
 // Ring tiles fill the GPU (256 CUs) only from 256 tiles on; below that (e.g. the router's 896
@@ -671,6 +674,8 @@ hipError_t launch_tiled(const GemmArgs &g, bool mx, int max_tiles, hipStream_t s
 {
     if (g.N % 16 || g.N <= 0 || g.K % (mx ? MX_STEP : BF16_STEP) || g.K <= 0)
         return hipErrorInvalidValue;
+    if ((g.split < g.N && g.split % 64) || (g.split2 > 0 && (g.split2 % 64 || g.split2 <= g.split)))
+        return hipErrorInvalidValue;   // a wave's 64 columns must lie in one output region
     const int grid_m = g.tiles ? max_tiles : (g.M + TILED_BM - 1) / TILED_BM;
     if (grid_m <= 0)
         return hipSuccess;

@@ -44,8 +44,11 @@ def test_packed_size_matches_layout():
     pb, wb = abi.query(_cfg(), 64)
     E, H, Lt, I, S, Is = 896, 7168, 3584, 384, 2, 384
     mx = lambda n, k: (n // 16) * (k // 128) * 1088        # noqa: E731
-    expect = E * H * 2 + (Lt + 2 * S * Is) * H * 2 + H * (Lt + S * Is) * 2 + E * (mx(2 * I, Lt) + mx(Lt, I))
-    assert expect <= pb < expect + 5 * 256
+    # router, x-side, their combined copy (router rows padded to 64), output side, experts
+    E_rx = (E + 63) // 64 * 64
+    expect = (E * H * 2 + (Lt + 2 * S * Is) * H * 2 + (E_rx + Lt + 2 * S * Is) * H * 2 + H * (Lt + S * Is) * 2
+              + E * (mx(2 * I, Lt) + mx(Lt, I)))
+    assert expect <= pb < expect + 6 * 256
     # one expert's MXFP4 bytes: three 3584 x 384 matrices at 4.25 bits per value
     assert mx(2 * I, Lt) + mx(Lt, I) == 3 * 3584 * 384 * 17 // 32
     lay = abi.workspace_layout(_cfg(), 64)

@@ -507,9 +507,10 @@ moe_status xside_impl(moe_handle *h, const void *x, int32_t T, const moe_routing
 // moe_route_forward with the latent projections: the router and the x-side products as one
 // product over the combined [router rows (zero-padded to E_rx) | x-side rows] matrix, so that x is
 // read once and one launch streams both weight matrices; then top-K and grouping. Few tokens: the
-// product leaves split-K partials, the top-K kernel sums the router columns' and the x-side
-// epilogue (which also builds the tile lists) the rest. Many tokens: the product's epilogue writes
-// the logits (+bias), z and the shared GLU directly, and the grouping builds the tile lists.
+// product leaves split-K partials; one launch sums the router columns' for the top-K and runs the
+// x-side epilogue on the rest, and the grouping builds the tile lists. Many tokens: the product's
+// epilogue writes the logits (+bias), z and the shared GLU directly, and the grouping builds the
+// tile lists.
 // Every output element is computed in the same order as by the separate products.
 moe_status front_impl(moe_handle *h, const void *x, int32_t T, const float *logit_bias, float *logits_out,
                       const moe_routing *r, const WsLayout &W, uint8_t *ws, hipStream_t st)
@@ -542,13 +543,14 @@ moe_status front_impl(moe_handle *h, const void *x, int32_t T, const float *logi
         ta.splits = splits;
         ta.bias = logit_bias;
         ta.logits_out = logits_out;
-        moe_status e = select_impl(h, T, ta, r, W, ws, st, false);
-        if (e != MOE_OK)
-            return e;
+        // top-K and the x-side epilogue in one launch, then the grouping with the tile lists
         XsideEpiArgs ea{P + (int64_t)(Erx / 16) * SKINNY_TILE_FLOATS, pstride, splits, T, Nx, Lt, 2 * S * Is, Z,
-                        Acat, ldcat, r->offsets, E, bm, bm,
-                        reinterpret_cast<int32_t *>(ws + W.tiles1), reinterpret_cast<int32_t *>(ws + W.tiles2)};
-        MOE_LAUNCH(MOE_KERNEL_XSIDE_EPI, launch_xside_epilogue(ea, st));
+                        Acat, ldcat, nullptr, E, bm, bm, nullptr, nullptr};
+        MOE_LAUNCH(MOE_KERNEL_TOPK, launch_topk_xside(ta, ea, st));
+        MOE_LAUNCH(MOE_KERNEL_PERMUTE,
+                   launch_permute_small(r->topk_ids, T, K, E, r->counts, r->offsets, r->sorted_pairs, r->inv, st, bm,
+                                        reinterpret_cast<int32_t *>(ws + W.tiles1),
+                                        reinterpret_cast<int32_t *>(ws + W.tiles2)));
         return MOE_OK;
     }
     float *lg = logits_out ? logits_out : reinterpret_cast<float *>(ws + W.logits);

@@ -138,6 +138,8 @@ struct TopkArgs {
 constexpr int PERM_TOKENS_PER_BLOCK = 32;
 constexpr int PERM_SMALL_MAX_T = 256;
 hipError_t launch_topk(const TopkArgs &a, hipStream_t st);
+// Top-K from split-K partials together with the x-side epilogue (no tile lists) in one launch.
+hipError_t launch_topk_xside(const TopkArgs &a, const XsideEpiArgs &e, hipStream_t st);
 // Grouping for T <= PERM_SMALL_MAX_T in one workgroup; with tiles1 set it also writes the expert tile
 // list(s) of bm rows (tiles2 may be null).
 hipError_t launch_permute_small(const int32_t *ids, int T, int K, int E, int32_t *counts, int32_t *offsets,

@@ -1,6 +1,7 @@
 // route.hip -- deterministic top-K selection with sigmoid gate weights, and the grouping of
 // token/expert pairs by expert (histogram, per-expert scan, stable scatter).
 #include "kernels.hpp"
+#include "partials.hpp"
 
 
 namespace mxmoe {
@@ -156,14 +157,14 @@ __global__ __launch_bounds__(256) void topk_kernel(const TopkArgs a)
 // are added pairwise through LDS in a fixed tree (w += w + 4, w += w + 2, w += w + 1); waves 0..3
 // then select tokens 4 b .. 4 b + 3 from the totals.
 template <int SLOTS>
-__global__ __launch_bounds__(512) void topk_wide_kernel(const TopkArgs a)
+__device__ inline void topk_wide_block(const TopkArgs &a, int blk)
 {
     constexpr int WAVES = 8;
     __shared__ f32x4_t red[WAVES / 2 * SLOTS * WAVE];     // tree level buffer, then the totals
     __shared__ uint64_t scratch[4][WAVE];
     const int lane = threadIdx.x & (WAVE - 1);
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE);
-    const int t0 = blockIdx.x * 4;
+    const int t0 = blk * 4;
     const int mf = t0 / 16, quad = (t0 % 16) / 4;
 
     // expert e = lane + 64 j sits in partial tile e / 16 = lane / 16 + 4 j at column e % 16 = lane % 16
@@ -218,6 +219,41 @@ __global__ __launch_bounds__(512) void topk_wide_kernel(const TopkArgs a)
     uint32_t key[SLOTS];
     token_keys<SLOTS>(a, t, v, key);
     select_keys<SLOTS>(a, t, key, scratch[wv]);
+}
+
+template <int SLOTS>
+__global__ __launch_bounds__(512) void topk_wide_kernel(const TopkArgs a)
+{
+    topk_wide_block<SLOTS>(a, blockIdx.x);
+}
+
+// One launch for two independent consumers of the combined router + x-side partials: workgroups
+// 0 .. ntopk-1 select the top-K of four tokens each, the rest run the x-side epilogue (512 items
+// per workgroup), so the two overlap instead of running back to back.
+template <int SLOTS>
+__global__ __launch_bounds__(512) void topk_xside_kernel(const TopkArgs a, const XsideEpiArgs e, int ntopk)
+{
+    if ((int)blockIdx.x < ntopk)
+        topk_wide_block<SLOTS>(a, blockIdx.x);
+    else
+        xside_epi_item(e, (int64_t)(blockIdx.x - ntopk) * blockDim.x + threadIdx.x);
+}
+
+hipError_t launch_topk_xside(const TopkArgs &a, const XsideEpiArgs &e, hipStream_t st)
+{
+    if (!a.partials || a.T > SKINNY_MAX_M || a.K > WAVE || a.E > 16 * WAVE || e.tiles1)
+        return hipErrorInvalidValue;
+    const int ntopk = (a.T + 3) / 4;
+    const int64_t items = (int64_t)(e.Lt / 16 + e.shared_cols / 32) * 4 * WAVE;
+    const dim3 grid(ntopk + (unsigned)((items + 511) / 512));
+    const int slots = (a.E + WAVE - 1) / WAVE;
+    if (slots <= 4)
+        hipLaunchKernelGGL(topk_xside_kernel<4>, grid, dim3(512), 0, st, a, e, ntopk);
+    else if (slots <= 8)
+        hipLaunchKernelGGL(topk_xside_kernel<8>, grid, dim3(512), 0, st, a, e, ntopk);
+    else
+        hipLaunchKernelGGL(topk_xside_kernel<16>, grid, dim3(512), 0, st, a, e, ntopk);
+    return hipGetLastError();
 }
 
 hipError_t launch_topk(const TopkArgs &a, hipStream_t st)

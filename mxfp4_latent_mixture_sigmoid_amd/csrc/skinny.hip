@@ -10,6 +10,7 @@
 // and applies the epilogue: router logits (+bias) in the top-K kernel, z and the shared-expert GLU
 // in xside_epilogue_kernel, the final BF16 output in out_epilogue_kernel.
 #include "kernels.hpp"
+#include "partials.hpp"
 
 #include <algorithm>
 
@@ -101,18 +102,18 @@ __global__ __launch_bounds__(WAVE *WAVES) void skinny_kernel(const SkinnyArgs g)
 // groups = gridDim.x / splits. The activation chunk of its split is staged in LDS once; each wave
 // then streams its blocks as 16-step units (one contiguous 16 KiB range each), loading the next unit
 // while the current one is multiplied, and writes a block's partial tile after its last unit.
-template <int WAVES, int UNITS>
+template <int WAVES, int UNITS, int MT>
 __global__ __launch_bounds__(WAVE *WAVES) void skinny_persist_kernel(const SkinnyArgs g, int splits)
 {
     constexpr int STEPS = 16, CSTEPS = STEPS * UNITS;
     __shared__ u32x4_t lds_a[CSTEPS * 4 * WAVE];   // [steps][4 fragments][64 lanes]
-    const int lane = threadIdx.x & (WAVE - 1), wv = threadIdx.x / WAVE;
+    const int lane = threadIdx.x & (WAVE - 1);
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE);
     const int split = blockIdx.x % splits, grp = blockIdx.x / splits;
     const int groups = gridDim.x / splits;
     const int kc0 = split * CSTEPS * BF16_STEP;
     const int nsteps = min(CSTEPS * BF16_STEP, g.K - kc0) / BF16_STEP;
     const int nunits = (nsteps + STEPS - 1) / STEPS;
-    const int mt = (g.M + 15) / 16;
     const int nblocks = g.N / 16;
     const int stride = groups * WAVES;
     const int nb0 = grp * WAVES + wv;
@@ -146,7 +147,7 @@ __global__ __launch_bounds__(WAVE *WAVES) void skinny_persist_kernel(const Skinn
             const int slot = threadIdx.x + u * WAVE * WAVES;
             const int blk = slot / WAVE, sl = slot % WAVE;
             const int m = (blk % 4) * 16 + (sl & 15);
-            if (blk / 4 < nsteps && (blk % 4) < mt)
+            if (blk / 4 < nsteps && (blk % 4) < MT)
                 lds_a[slot] = m < g.M ? av[u] : u32x4_t{0u, 0u, 0u, 0u};
         }
     }
@@ -169,7 +170,7 @@ __global__ __launch_bounds__(WAVE *WAVES) void skinny_persist_kernel(const Skinn
                     a[mf] = lds_a[(step * 4 + mf) * WAVE + lane];
 #pragma unroll
                 for (int mf = 0; mf < 4; mf++)
-                    if (mf < mt)
+                    if (mf < MT)
                         acc[mf] = mfma16(as_bf16x8(a[mf]), as_bf16x8(b[s]), acc[mf]);
             }
         }
@@ -178,7 +179,7 @@ __global__ __launch_bounds__(WAVE *WAVES) void skinny_persist_kernel(const Skinn
             float *P = g.P + (int64_t)split * g.p_split_stride + (int64_t)blk * SKINNY_TILE_FLOATS;
 #pragma unroll
             for (int mf = 0; mf < 4; mf++)
-                if (mf < mt)
+                if (mf < MT)
                     *reinterpret_cast<f32x4_t *>(P + (mf * WAVE + lane) * 4) = acc[mf];
         }
     };
@@ -196,22 +197,23 @@ __global__ __launch_bounds__(WAVE *WAVES) void skinny_persist_kernel(const Skinn
     }
 }
 
-// chunk_steps (16 or 32) is the K range of a split in 32-wide steps.
+// chunk_steps is the K range of a split in 32-wide steps (16: one packed K chunk).
 hipError_t launch_skinny_persist(const SkinnyArgs &g, int waves, int groups, int chunk_steps, hipStream_t st)
 {
     if (g.M < 1 || g.M > SKINNY_MAX_M || g.N % 16 || g.K % BF16_STEP || groups < 1)
         return hipErrorInvalidValue;
     const int splits = skinny_splits(g.K, chunk_steps);
     const dim3 grid(splits * groups);
-#define MOE_PERSIST(W, U)                                                                                            \
-    if (waves == W && chunk_steps == 16 * U) {                                                                       \
-        hipLaunchKernelGGL((skinny_persist_kernel<W, U>), grid, dim3(WAVE * W), 0, st, g, splits);                   \
+    const int mt = (g.M + 15) / 16;
+#define MOE_PERSIST(W, U, MT)                                                                                        \
+    if (waves == W && chunk_steps == 16 * U && mt == MT) {                                                          \
+        hipLaunchKernelGGL((skinny_persist_kernel<W, U, MT>), grid, dim3(WAVE * W), 0, st, g, splits);               \
         return hipGetLastError();                                                                                    \
     }
-    MOE_PERSIST(8, 1)
-    MOE_PERSIST(8, 2)
-    MOE_PERSIST(4, 1)
-    MOE_PERSIST(4, 2)
+    MOE_PERSIST(8, 1, 1)
+    MOE_PERSIST(8, 1, 2)
+    MOE_PERSIST(8, 1, 3)
+    MOE_PERSIST(8, 1, 4)
 #undef MOE_PERSIST
     return hipErrorInvalidValue;
 }
@@ -244,46 +246,8 @@ hipError_t launch_skinny(const SkinnyArgs &g, int waves, int chunk_steps, hipStr
     return hipErrorInvalidValue;
 }
 
-// Sum of the K-chunk partials of one element, in chunk order; loads are issued in batches of
-// SUM_BATCH (addresses clamped, so every load is valid) before any of them is used.
-constexpr int SUM_BATCH = 8;
-__device__ inline float sum_partials(const float *P, int64_t split_stride, int splits, int64_t idx)
-{
-    float v = 0.f;
-    for (int s0 = 0; s0 < splits; s0 += SUM_BATCH) {
-        float t[SUM_BATCH];
-#pragma unroll
-        for (int u = 0; u < SUM_BATCH; u++)
-            t[u] = P[min(s0 + u, splits - 1) * split_stride + idx];
-#pragma unroll
-        for (int u = 0; u < SUM_BATCH; u++)
-            if (s0 + u < splits)
-                v += t[u];
-    }
-    return v;
-}
-
-// Sum over the splits of one lane's 16-byte partial slot (four rows of one column), split order.
-__device__ inline f32x4_t sum_slot(const float *slot, int64_t split_stride, int splits)
-{
-    f32x4_t v = {0.f, 0.f, 0.f, 0.f};
-    for (int s0 = 0; s0 < splits; s0 += SUM_BATCH) {
-        f32x4_t t[SUM_BATCH];
-#pragma unroll
-        for (int u = 0; u < SUM_BATCH; u++)
-            t[u] = *reinterpret_cast<const f32x4_t *>(slot + min(s0 + u, splits - 1) * split_stride);
-#pragma unroll
-        for (int u = 0; u < SUM_BATCH; u++)
-            if (s0 + u < splits)
-                v += t[u];
-    }
-    return v;
-}
-
-// x-side epilogue. Thread (nb, mf, lane) owns rows mf*16 + 4(lane/16) .. +3 of column
-// nb*16 + lane%16: z = bf16(sum) for the latent blocks; for a shared-expert pair of blocks (16
-// gate columns, then the matching 16 up columns) the thread of the gate block forms
-// h_s = bf16(silu(gate) * up). With tile lists requested, one extra (last) workgroup builds them.
+// x-side epilogue over the whole partials (per-item work: xside_epi_item). With tile lists
+// requested, one extra (last) workgroup builds them.
 __global__ __launch_bounds__(256) void xside_epilogue_kernel(const XsideEpiArgs e)
 {
     if (e.tiles1 && blockIdx.x == gridDim.x - 1) {
@@ -292,35 +256,7 @@ __global__ __launch_bounds__(256) void xside_epilogue_kernel(const XsideEpiArgs 
         write_tiles(e.offsets, e.E, e.bm2, e.tiles2, sh);
         return;
     }
-    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int lane = (int)(gid % WAVE);
-    const int64_t frag = gid / WAVE;
-    const int mf = (int)(frag % 4);
-    const int nbz = e.Lt / 16, npairs = e.shared_cols / 32;
-    const int64_t unit = frag / 4;                           // latent block, then shared pair
-    if (unit >= nbz + npairs || mf * 16 >= e.M)
-        return;
-    const int col16 = lane & 15, r0 = mf * 16 + 4 * (lane >> 4);
-    if (unit < nbz) {
-        const f32x4_t v = sum_slot(e.P + (unit * 4 + mf) * (int64_t)SKINNY_TILE_FLOATS / 4 + lane * 4,
-                                   e.p_split_stride, e.splits);
-#pragma unroll
-        for (int i = 0; i < 4; i++)
-            if (r0 + i < e.M)
-                e.z[(int64_t)(r0 + i) * e.Lt + unit * 16 + col16] = (uint16_t)f32_to_bf16_bits(v[i]);
-    } else {
-        const int pr = (int)(unit - nbz);
-        const int64_t gb = nbz + 2 * pr;                     // gate block; up block is gb + 1
-        const f32x4_t gv = sum_slot(e.P + (gb * 4 + mf) * (int64_t)SKINNY_TILE_FLOATS / 4 + lane * 4,
-                                    e.p_split_stride, e.splits);
-        const f32x4_t uv = sum_slot(e.P + ((gb + 1) * 4 + mf) * (int64_t)SKINNY_TILE_FLOATS / 4 + lane * 4,
-                                    e.p_split_stride, e.splits);
-#pragma unroll
-        for (int i = 0; i < 4; i++)
-            if (r0 + i < e.M)
-                e.acat[(int64_t)(r0 + i) * e.ldcat + e.Lt + pr * 16 + col16] =
-                    (uint16_t)f32_to_bf16_bits(silu_f32(gv[i]) * uv[i]);
-    }
+    xside_epi_item(e, (int64_t)blockIdx.x * blockDim.x + threadIdx.x);
 }
 
 hipError_t launch_xside_epilogue(const XsideEpiArgs &e, hipStream_t st)

@@ -52,60 +52,52 @@ __device__ inline bool tiled_item(const GemmArgs &g, int gx, int gy, int &bx, in
     return true;
 }
 
-template <int WM, int WN, bool MX>
-__global__ __launch_bounds__(WAVE * 4) void tiled_kernel(const GemmArgs g, int gx, int gy)
-{
-    static_assert(WM * WN == 4, "four waves");
-    constexpr int BM = TL_WAVE_M * WM, BN = TL_WAVE_N * WN;
-    constexpr int MFW = BM / 16;                                // 16-row fragments per workgroup
-    constexpr int SLOTS = TL_SUB * MFW * WAVE;                  // 16-byte slots per stage
-    constexpr int PER_THREAD = SLOTS / (WAVE * 4);
-    __shared__ u32x4_t lds[2][SLOTS];
+constexpr int TL_BM = TL_WAVE_M, TL_BN = TL_WAVE_N * 4;   // four waves side by side along N
+constexpr int TL_MFW = TL_BM / 16;                         // 16-row fragments per workgroup
+constexpr int TL_SLOTS = TL_SUB * TL_MFW * WAVE;           // 16-byte A slots per stage
 
+// One 128 x 256 output tile (rows m0 .. m1-1 valid) of which only the first NMF 16-row fragments
+// hold valid rows: the A staging, the MFMAs and the stores cover those fragments only, so a short
+// tile (an expert's last rows) costs in proportion to its rows plus its B stream.
+template <bool MX, int NMF>
+__device__ __attribute__((always_inline)) inline void tiled_tile(const GemmArgs &g, int bx, int group, int m0, int m1,
+                                                                 u32x4_t (*lds)[TL_SLOTS])
+{
+    static_assert(NMF == 2 || NMF == 4 || NMF == 8, "row fragments per tile");
     const int lane = threadIdx.x & (WAVE - 1);
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE);   // wave-uniform
-    const int wm = wv / WN, wn = wv % WN;
-
-    int bx, by;
-    if (!tiled_item(g, gx, gy, bx, by))
-        return;
-    int group = 0, m0, m1;
-    if (g.tiles) {
-        const int4 t = reinterpret_cast<const int4 *>(g.tiles + TILE_HEADER_INTS)[by];
-        group = t.x;
-        m0 = t.y;
-        m1 = t.z;
-    } else {
-        m0 = by * BM;
-        m1 = min(g.M, m0 + BM);
-    }
-    const int n0 = bx * BN + wn * TL_WAVE_N;                     // this wave's first column
+    const int n0 = bx * TL_BN + wv * TL_WAVE_N;                  // this wave's first column
     const int nblocks = g.N / 16;
     const uint8_t *Bg = g.B + (int64_t)group * g.b_stride;
 
-    // ---- A staging. Thread t fills slots t + 256 u: its lane slot (t % 64) is fixed, so its row
-    // within a fragment (t % 16) and its K quarter ((t % 64) / 16) are too; block t / 64 + 4 u runs
-    // over fragments f = wv + 4 (u % FR) (FR = MFW / 4 distinct rows) and sub-steps s = u / FR.
-    constexpr int FR = MFW / 4;
+    // ---- A staging. A stage holds TL_SUB x NMF 1 KiB blocks (sub-step s, fragment f at block
+    // s * TL_MFW + f, lane slot l = row f*16 + l%16, inputs s*32 + 8(l/16)). Thread t fills lane slot
+    // t % 64 of blocks b = wv + 4u (u < NMF), b -> (s, f) = (b / NMF, b % NMF): its fragment rows
+    // are f = wv % NMF + 4 (u % FR), FR = NMF / 4 (at least 1) distinct rows.
+    constexpr int FR = NMF >= 8 ? NMF / 4 : 1;
     const uint16_t *arow[FR];
 #pragma unroll
     for (int i = 0; i < FR; i++) {
-        const int r = min(m0 + (wv + 4 * i) * 16 + (lane & 15), m1 - 1);   // clamped valid row
+        const int f = wv % NMF + 4 * i;
+        const int r = min(m0 + f * 16 + (lane & 15), m1 - 1);   // clamped valid row
         const int64_t row = g.a_index ? (int64_t)(g.a_index[r] / g.a_div) : (int64_t)r;
         arow[i] = g.A + row * g.lda + 8 * (lane >> 4);
     }
     const int nstages = (g.K + TL_STAGE_K - 1) / TL_STAGE_K;
     auto load_a = [&](int stage, u32x4_t *v) {
 #pragma unroll
-        for (int u = 0; u < PER_THREAD; u++) {
-            const int k = min(stage * TL_STAGE_K + (u / FR) * 32, g.K - 32);
+        for (int u = 0; u < NMF; u++) {
+            const int sub = (wv + 4 * u) / NMF;
+            const int k = min(stage * TL_STAGE_K + sub * 32, g.K - 32);
             v[u] = load16(arow[u % FR] + k);
         }
     };
     auto store_a = [&](int buf, const u32x4_t *v) {
 #pragma unroll
-        for (int u = 0; u < PER_THREAD; u++)
-            lds[buf][threadIdx.x + u * WAVE * 4] = v[u];
+        for (int u = 0; u < NMF; u++) {
+            const int b = wv + 4 * u;
+            lds[buf][((b / NMF) * TL_MFW + b % NMF) * WAVE + lane] = v[u];
+        }
     };
 
     // ---- B fragments of this wave
@@ -114,15 +106,15 @@ __global__ __launch_bounds__(WAVE * 4) void tiled_kernel(const GemmArgs g, int g
     for (int nf = 0; nf < TL_NF; nf++)
         nval[nf] = (n0 / 16 + nf) < nblocks;
 
-    f32x4_t acc[TL_MF][TL_NF];
+    f32x4_t acc[NMF][TL_NF];
 #pragma unroll
-    for (int i = 0; i < TL_MF; i++)
+    for (int i = 0; i < NMF; i++)
 #pragma unroll
         for (int j = 0; j < TL_NF; j++)
             acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
     {
-        u32x4_t av[PER_THREAD];
+        u32x4_t av[NMF];
         load_a(0, av);
         store_a(0, av);
     }
@@ -160,7 +152,7 @@ __global__ __launch_bounds__(WAVE * 4) void tiled_kernel(const GemmArgs g, int g
 
     for (int st = 0; st < nstages; st++) {
         const int cur = st & 1;
-        u32x4_t an[PER_THREAD];
+        u32x4_t an[NMF];
         load_a(min(st + 1, nstages - 1), an);
 
         {
@@ -170,15 +162,15 @@ __global__ __launch_bounds__(WAVE * 4) void tiled_kernel(const GemmArgs g, int g
                 load_mx(st + 1, bnx, scnx);
 #pragma unroll
                 for (int s = 0; s < TL_SUB; s++) {
-                    u32x4_t a[TL_MF];
+                    u32x4_t a[NMF];
 #pragma unroll
-                    for (int f = 0; f < TL_MF; f++)
-                        a[f] = lds[cur][(s * MFW + wm * TL_MF + f) * WAVE + lane];
+                    for (int f = 0; f < NMF; f++)
+                        a[f] = lds[cur][(s * TL_MFW + f) * WAVE + lane];
 #pragma unroll
                     for (int nf = 0; nf < TL_NF; nf++) {
                         const bf16x8_t b = mx_dequant8(bcur[nf][s], e8m0_to_f32((sccur[nf] >> (8 * s)) & 0xFFu));
 #pragma unroll
-                        for (int f = 0; f < TL_MF; f++)
+                        for (int f = 0; f < NMF; f++)
                             acc[f][nf] = mfma16(b, as_bf16x8(a[f]), acc[f][nf]);
                     }
                     __builtin_amdgcn_sched_barrier(0);   // keep one sub-step's operands live at a time
@@ -195,14 +187,14 @@ __global__ __launch_bounds__(WAVE * 4) void tiled_kernel(const GemmArgs g, int g
                     u32x4_t bnx[TL_NF];
                     load_b(kstep + 1, bnx);
                     if (kstep < ks) {
-                        u32x4_t a[TL_MF];
+                        u32x4_t a[NMF];
 #pragma unroll
-                        for (int f = 0; f < TL_MF; f++)
-                            a[f] = lds[cur][(s * MFW + wm * TL_MF + f) * WAVE + lane];
+                        for (int f = 0; f < NMF; f++)
+                            a[f] = lds[cur][(s * TL_MFW + f) * WAVE + lane];
 #pragma unroll
                         for (int nf = 0; nf < TL_NF; nf++)
 #pragma unroll
-                            for (int f = 0; f < TL_MF; f++)
+                            for (int f = 0; f < NMF; f++)
                                 acc[f][nf] = mfma16(as_bf16x8(bcur[nf]), as_bf16x8(a[f]), acc[f][nf]);
                     }
 #pragma unroll
@@ -223,7 +215,7 @@ __global__ __launch_bounds__(WAVE * 4) void tiled_kernel(const GemmArgs g, int g
     // one 8-byte (BF16) or 16-byte (FP32) store per fragment when the output is aligned for it.
     const OutDesc d = out_region(g, n0);
     const int q = lane >> 4;
-    const int rbase = m0 + wm * TL_WAVE_M + (lane & 15);
+    const int rbase = m0 + (lane & 15);
     const bool vec = (d.ld % 4 == 0) && (d.col0 % 4 == 0) &&
                      (reinterpret_cast<uintptr_t>(d.ptr) % (d.kind == OUT_F32 ? 16 : 8) == 0);
     if (d.kind == OUT_GLU) {
@@ -235,7 +227,7 @@ __global__ __launch_bounds__(WAVE * 4) void tiled_kernel(const GemmArgs g, int g
                 continue;
             const int oc = (n0 - d.col0) / 2 + p * 16 + 4 * q;
 #pragma unroll
-            for (int f = 0; f < TL_MF; f++) {
+            for (int f = 0; f < NMF; f++) {
                 const int r = rbase + f * 16;
                 if (r >= m1)
                     continue;
@@ -266,7 +258,7 @@ __global__ __launch_bounds__(WAVE * 4) void tiled_kernel(const GemmArgs g, int g
                 for (int i = 0; i < 4; i++)
                     bias[i] = (n + i < d.n_valid) ? d.bias[n + i] : 0.f;
 #pragma unroll
-            for (int f = 0; f < TL_MF; f++) {
+            for (int f = 0; f < NMF; f++) {
                 const int r = rbase + f * 16;
                 if (r >= m1)
                     continue;
@@ -300,14 +292,40 @@ __global__ __launch_bounds__(WAVE * 4) void tiled_kernel(const GemmArgs g, int g
 }
 
 template <bool MX>
+__global__ __launch_bounds__(WAVE * 4) void tiled_kernel(const GemmArgs g, int gx, int gy)
+{
+    __shared__ u32x4_t lds[2][TL_SLOTS];
+    int bx, by;
+    if (!tiled_item(g, gx, gy, bx, by))
+        return;
+    int group = 0, m0, m1;
+    if (g.tiles) {
+        const int4 t = reinterpret_cast<const int4 *>(g.tiles + TILE_HEADER_INTS)[by];
+        group = t.x;
+        m0 = t.y;
+        m1 = t.z;
+    } else {
+        m0 = by * TL_BM;
+        m1 = min(g.M, m0 + TL_BM);
+    }
+    // one code path per workgroup, chosen by the tile's row count
+    const int nmf = __builtin_amdgcn_readfirstlane((m1 - m0 + 15) / 16);
+    if (nmf <= 2)
+        tiled_tile<MX, 2>(g, bx, group, m0, m1, lds);
+    else if (nmf <= 4)
+        tiled_tile<MX, 4>(g, bx, group, m0, m1, lds);
+    else
+        tiled_tile<MX, 8>(g, bx, group, m0, m1, lds);
+}
+
+template <bool MX>
 static hipError_t launch_tiled_t(const GemmArgs &g, int grid_m, hipStream_t st)
 {
-    constexpr int BN = TL_WAVE_N * 4;
-    const int gx = (g.N + BN - 1) / BN;
+    const int gx = (g.N + TL_BN - 1) / TL_BN;
     const int64_t grid = ((int64_t)gx * grid_m + TL_XCDS - 1) / TL_XCDS * TL_XCDS;
     if (grid > INT32_MAX)
         return hipErrorInvalidValue;
-    hipLaunchKernelGGL((tiled_kernel<1, 4, MX>), dim3((unsigned)grid), dim3(WAVE * 4), 0, st, g, gx, grid_m);
+    hipLaunchKernelGGL((tiled_kernel<MX>), dim3((unsigned)grid), dim3(WAVE * 4), 0, st, g, gx, grid_m);
     return hipGetLastError();
 }
 
@@ -526,38 +544,27 @@ hipError_t launch_ring(const GemmArgs &g, hipStream_t st)
 // counted on the device, so the tiles of one expert share an L2.
 constexpr int AS_BM = 128, AS_BN = 256, AS_MF = 8, AS_NF = 4, AS_XCDS = 8;
 
-template <int KB>
-__global__ __launch_bounds__(WAVE * 4) void astat_kernel(const GemmArgs g, int nsplit)
+// One (tile, N-run) item whose rows need only the first NMF 16-row fragments.
+template <int KB, int NMF>
+__device__ __attribute__((always_inline)) inline void astat_item(const GemmArgs &g, int group, int m0, int m1, int j0,
+                                                                 int j1, u32x4_t *lds)
 {
     constexpr int KS = KB * TL_SUB;                              // 32-wide sub-steps
-    __shared__ u32x4_t lds[KS * AS_MF * WAVE];
     const int lane = threadIdx.x & (WAVE - 1);
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE);
 
-    const int total = g.tiles[0] * nsplit;
-    const int per = (total + AS_XCDS - 1) / AS_XCDS;
-    const int slot = blockIdx.x / AS_XCDS;
-    const int item = (blockIdx.x % AS_XCDS) * per + slot;
-    if (slot >= per || item >= total)
-        return;
-    const int4 t = reinterpret_cast<const int4 *>(g.tiles + TILE_HEADER_INTS)[item / nsplit];
-    const int part = item % nsplit;
-    const int m0 = t.y, m1 = t.z;
-    const int nbn = (g.N + AS_BN - 1) / AS_BN;
-    const int j0 = part * nbn / nsplit, j1 = (part + 1) * nbn / nsplit;
-    if (j0 >= j1)
-        return;
-
-    // A tile -> LDS: block b = (s, f) holds lane l's operand (row f*16 + l%16, k = 32 s + 8 (l/16)).
-    for (int b = wv; b < KS * AS_MF; b += 4) {
-        const int s = b / AS_MF, f = b % AS_MF;
+    // A tile -> LDS: block (s, f) at s * AS_MF + f holds lane l's operand (row f*16 + l%16,
+    // k = 32 s + 8 (l/16)); only the NMF fragments that hold valid rows are loaded.
+    for (int b = wv; b < KS * NMF; b += 4) {
+        const int s = b / NMF, f = b % NMF;
         const int r = min(m0 + f * 16 + (lane & 15), m1 - 1);   // clamped valid row, never stored
         const int64_t row = g.a_index ? (int64_t)(g.a_index[r] / g.a_div) : (int64_t)r;
         __builtin_amdgcn_global_load_lds(g.A + row * g.lda + s * 32 + 8 * (lane >> 4),
-                                         (__attribute__((address_space(3))) void *)&lds[b * WAVE], 16, 0, 0);
+                                         (__attribute__((address_space(3))) void *)&lds[(s * AS_MF + f) * WAVE], 16,
+                                         0, 0);
     }
 
-    const uint8_t *Bg = g.B + (int64_t)t.x * g.b_stride;
+    const uint8_t *Bg = g.B + (int64_t)group * g.b_stride;
     const int nbmax = g.N / 16 - 1;
     auto load_block = [&](int j, u32x4_t (&codes)[AS_NF][KB], uint32_t (&sc)[AS_NF][KB]) {
 #pragma unroll
@@ -584,9 +591,9 @@ __global__ __launch_bounds__(WAVE * 4) void astat_kernel(const GemmArgs g, int n
         u32x4_t bn[AS_NF][KB];
         uint32_t bsn[AS_NF][KB];
         load_block(min(j + 1, j1 - 1), bn, bsn);
-        f32x4_t acc[AS_MF][AS_NF];
+        f32x4_t acc[NMF][AS_NF];
 #pragma unroll
-        for (int f = 0; f < AS_MF; f++)
+        for (int f = 0; f < NMF; f++)
 #pragma unroll
             for (int nf = 0; nf < AS_NF; nf++)
                 acc[f][nf] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -594,15 +601,15 @@ __global__ __launch_bounds__(WAVE * 4) void astat_kernel(const GemmArgs g, int n
         for (int kb = 0; kb < KB; kb++)
 #pragma unroll
             for (int s = 0; s < TL_SUB; s++) {
-                u32x4_t a[AS_MF];
+                u32x4_t a[NMF];
 #pragma unroll
-                for (int f = 0; f < AS_MF; f++)
+                for (int f = 0; f < NMF; f++)
                     a[f] = lds[((kb * TL_SUB + s) * AS_MF + f) * WAVE + lane];
 #pragma unroll
                 for (int nf = 0; nf < AS_NF; nf++) {
                     const bf16x8_t b = mx_dequant8(bc[nf][kb][s], e8m0_to_f32((bs[nf][kb] >> (8 * s)) & 0xFFu));
 #pragma unroll
-                    for (int f = 0; f < AS_MF; f++)
+                    for (int f = 0; f < NMF; f++)
                         acc[f][nf] = mfma16(b, as_bf16x8(a[f]), acc[f][nf]);
                 }
                 __builtin_amdgcn_sched_barrier(0);
@@ -614,7 +621,7 @@ __global__ __launch_bounds__(WAVE * 4) void astat_kernel(const GemmArgs g, int n
             if (n >= d.n_valid)
                 continue;
 #pragma unroll
-            for (int f = 0; f < AS_MF; f++) {
+            for (int f = 0; f < NMF; f++) {
                 const int r = m0 + f * 16 + (lane & 15);
                 if (r < m1)
                     *reinterpret_cast<uint2 *>(out + (int64_t)r * d.ld + n) =
@@ -630,6 +637,32 @@ __global__ __launch_bounds__(WAVE * 4) void astat_kernel(const GemmArgs g, int n
                 bs[nf][kb] = bsn[nf][kb];
             }
     }
+}
+
+template <int KB>
+__global__ __launch_bounds__(WAVE * 4) void astat_kernel(const GemmArgs g, int nsplit)
+{
+    __shared__ u32x4_t lds[KB * TL_SUB * AS_MF * WAVE];
+    const int total = g.tiles[0] * nsplit;
+    const int per = (total + AS_XCDS - 1) / AS_XCDS;
+    const int slot = blockIdx.x / AS_XCDS;
+    const int item = (blockIdx.x % AS_XCDS) * per + slot;
+    if (slot >= per || item >= total)
+        return;
+    const int4 t = reinterpret_cast<const int4 *>(g.tiles + TILE_HEADER_INTS)[item / nsplit];
+    const int part = item % nsplit;
+    const int nbn = (g.N + AS_BN - 1) / AS_BN;
+    const int j0 = part * nbn / nsplit, j1 = (part + 1) * nbn / nsplit;
+    if (j0 >= j1)
+        return;
+    // one code path per workgroup, chosen by the tile's row count
+    const int nmf = __builtin_amdgcn_readfirstlane((t.z - t.y + 15) / 16);
+    if (nmf <= 2)
+        astat_item<KB, 2>(g, t.x, t.y, t.z, j0, j1, lds);
+    else if (nmf <= 4)
+        astat_item<KB, 4>(g, t.x, t.y, t.z, j0, j1, lds);
+    else
+        astat_item<KB, 8>(g, t.x, t.y, t.z, j0, j1, lds);
 }
 
 template <int KB>

@@ -104,9 +104,9 @@ moe_status moe_query(const moe_config *cfg, int32_t T_max, size_t *packed_bytes,
                      size_t *workspace_bytes);
 
 /* Test hook: byte offsets inside the workspace for T tokens, in this order: FP32 logits [T,E],
- * per-block expert histogram, the two expert tile lists, z [T,Lt], [zc | h_s] [T, Lt + S Is],
+ * per-block expert histogram, the expert tile list, z [T,Lt], [zc | h_s] [T, Lt + S Is],
  * h [T K, I] and y [T K, Lt] (expert-sorted rows, BF16), FP32 split-K partials, then the total
- * size. `offsets` is a host array of 10 entries. Host-only. */
+ * size. `offsets` is a host array of 9 entries. Host-only. */
 moe_status moe_query_workspace_layout(const moe_config *cfg, int32_t T, size_t *offsets);
 
 /* Validate the config and weights, then enqueue the packing of every weight into `packed`

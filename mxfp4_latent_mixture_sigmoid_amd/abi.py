@@ -120,7 +120,7 @@ def query(cfg: MoeConfig, T_max: int):
     return pb.value, wb.value
 
 
-WS_REGIONS = ("logits", "hist", "tiles1", "tiles2", "z", "acat", "h", "y", "partials", "total")
+WS_REGIONS = ("logits", "hist", "tiles", "z", "acat", "h", "y", "partials", "total")
 
 
 def workspace_layout(cfg: MoeConfig, T: int) -> dict:

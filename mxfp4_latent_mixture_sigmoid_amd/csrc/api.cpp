@@ -108,9 +108,9 @@ PackedLayout packed_layout(const moe_config *c)
 }
 
 struct WsLayout {
-    int64_t logits, hist, tiles1, tiles2, z, acat, h, y, partials, total;
+    int64_t logits, hist, tiles, z, acat, h, y, partials, total;
     int64_t rpartials;                  // router partials (inside the partials region, before the dense ones)
-    int64_t max_tiles1, max_tiles2;
+    int64_t max_tiles;                  // capacity of the expert tile list (shared by both expert products)
 };
 
 int64_t max_tiles(int64_t T, int64_t K, int64_t E, int bm)
@@ -125,17 +125,14 @@ WsLayout ws_layout(const moe_config *c, int64_t T)
     const int64_t E = c->n_experts, K = c->top_k, Lt = c->latent, I = c->inter;
     const int64_t S = c->n_shared, Is = c->shared_inter;
     const int64_t nb = (T + PERM_TOKENS_PER_BLOCK - 1) / PERM_TOKENS_PER_BLOCK;
-    L.max_tiles1 = max_tiles(T, K, E, expert_bm(c, T));
-    L.max_tiles2 = max_tiles(T, K, E, expert_bm(c, T));
+    L.max_tiles = max_tiles(T, K, E, expert_bm(c, T));
     int64_t off = 0;
     L.logits = off;
     off = align_up(off + T * E * 4);
     L.hist = off;
     off = align_up(off + E * nb * 4);
-    L.tiles1 = off;
-    off = align_up(off + (TILE_HEADER_INTS + 4 * L.max_tiles1) * 4);
-    L.tiles2 = off;
-    off = align_up(off + (TILE_HEADER_INTS + 4 * L.max_tiles2) * 4);
+    L.tiles = off;
+    off = align_up(off + (TILE_HEADER_INTS + 4 * L.max_tiles) * 4);
     L.z = off;
     if (c->has_latent_proj)
         off = align_up(off + T * Lt * 2);
@@ -249,8 +246,8 @@ moe_status moe_query_workspace_layout(const moe_config *cfg, int32_t T, size_t *
     if (!valid_config(cfg) || T < 0 || !sizes_fit_int32(cfg, T) || !offsets)
         return MOE_ERR_INVALID_ARG;
     const WsLayout W = ws_layout(cfg, T);
-    const int64_t v[10] = {W.logits, W.hist, W.tiles1, W.tiles2, W.z, W.acat, W.h, W.y, W.rpartials, W.total};
-    for (int i = 0; i < 10; i++)
+    const int64_t v[9] = {W.logits, W.hist, W.tiles, W.z, W.acat, W.h, W.y, W.rpartials, W.total};
+    for (int i = 0; i < 9; i++)
         offsets[i] = (size_t)v[i];
     return MOE_OK;
 }
@@ -444,18 +441,16 @@ moe_status select_impl(moe_handle *h, int32_t T, const TopkArgs &ta, const moe_r
     const moe_config *c = &h->cfg;
     const int E = c->n_experts, K = c->top_k;
     MOE_LAUNCH(MOE_KERNEL_TOPK, launch_topk(ta, st));
-    int32_t *tiles1 = reinterpret_cast<int32_t *>(ws + W.tiles1);
-    int32_t *tiles2 = reinterpret_cast<int32_t *>(ws + W.tiles2);
+    int32_t *tl = reinterpret_cast<int32_t *>(ws + W.tiles);
     const int bm = expert_bm(c, T);
     if (T <= PERM_SMALL_MAX_T) {
         MOE_LAUNCH(MOE_KERNEL_PERMUTE, launch_permute_small(r->topk_ids, T, K, E, r->counts, r->offsets,
-                                                            r->sorted_pairs, r->inv, st, bm,
-                                                            tiles ? tiles1 : nullptr, tiles ? tiles2 : nullptr));
+                                                            r->sorted_pairs, r->inv, st, bm, tiles ? tl : nullptr));
     } else {
         MOE_LAUNCH(MOE_KERNEL_PERMUTE, launch_permute(r->topk_ids, T, K, E, reinterpret_cast<int32_t *>(ws + W.hist),
                                                       r->counts, r->offsets, r->sorted_pairs, r->inv, st));
         if (tiles)
-            MOE_LAUNCH(MOE_KERNEL_TILEMAP, launch_tilemap(r->offsets, E, bm, tiles1, bm, tiles2, st));
+            MOE_LAUNCH(MOE_KERNEL_TILEMAP, launch_tilemap(r->offsets, E, bm, tl, st));
     }
     return MOE_OK;
 }
@@ -474,15 +469,14 @@ moe_status xside_impl(moe_handle *h, const void *x, int32_t T, const moe_routing
     const int bm = expert_bm(c, T);
     uint16_t *Z = reinterpret_cast<uint16_t *>(ws + W.z);
     uint16_t *Acat = reinterpret_cast<uint16_t *>(ws + W.acat);
-    int32_t *tiles1 = reinterpret_cast<int32_t *>(ws + W.tiles1);
-    int32_t *tiles2 = reinterpret_cast<int32_t *>(ws + W.tiles2);
+    int32_t *tl = reinterpret_cast<int32_t *>(ws + W.tiles);
     if (lat && T <= SKINNY_MAX_M) {   // z and h_s from split-K partials, summed by the epilogue
         float *partials = reinterpret_cast<float *>(ws + W.partials);
         const int64_t pstride = (int64_t)(Nx / 16) * SKINNY_TILE_FLOATS;
         SkinnyArgs g{static_cast<const uint16_t *>(x), H, T, h->packed + h->off_xside, Nx, H, partials, pstride};
         MOE_LAUNCH(MOE_KERNEL_XSIDE, launch_skinny_persist(g, 8, XSIDE_GROUPS, SKINNY_XSTEPS, st));
         XsideEpiArgs ea{partials, pstride, skinny_splits(H, SKINNY_XSTEPS), T, Nx, Lt, 2 * S * Is, Z, Acat, ldcat,
-                        r->offsets, E, bm, bm, tiles ? tiles1 : nullptr, tiles ? tiles2 : nullptr};
+                        r->offsets, E, bm, tiles ? tl : nullptr};
         MOE_LAUNCH(MOE_KERNEL_XSIDE_EPI, launch_xside_epilogue(ea, st));
         return MOE_OK;
     }
@@ -500,7 +494,7 @@ moe_status xside_impl(moe_handle *h, const void *x, int32_t T, const moe_routing
         MOE_LAUNCH(MOE_KERNEL_XSIDE, (ring_preferred(g) ? launch_ring(g, st) : launch_tiled(g, false, 0, st)));
     }
     if (tiles)
-        MOE_LAUNCH(MOE_KERNEL_TILEMAP, launch_tilemap(r->offsets, E, bm, tiles1, bm, tiles2, st));
+        MOE_LAUNCH(MOE_KERNEL_TILEMAP, launch_tilemap(r->offsets, E, bm, tl, st));
     return MOE_OK;
 }
 
@@ -545,12 +539,11 @@ moe_status front_impl(moe_handle *h, const void *x, int32_t T, const float *logi
         ta.logits_out = logits_out;
         // top-K and the x-side epilogue in one launch, then the grouping with the tile lists
         XsideEpiArgs ea{P + (int64_t)(Erx / 16) * SKINNY_TILE_FLOATS, pstride, splits, T, Nx, Lt, 2 * S * Is, Z,
-                        Acat, ldcat, nullptr, E, bm, bm, nullptr, nullptr};
+                        Acat, ldcat, nullptr, E, bm, nullptr};
         MOE_LAUNCH(MOE_KERNEL_TOPK, launch_topk_xside(ta, ea, st));
         MOE_LAUNCH(MOE_KERNEL_PERMUTE,
                    launch_permute_small(r->topk_ids, T, K, E, r->counts, r->offsets, r->sorted_pairs, r->inv, st, bm,
-                                        reinterpret_cast<int32_t *>(ws + W.tiles1),
-                                        reinterpret_cast<int32_t *>(ws + W.tiles2)));
+                                        reinterpret_cast<int32_t *>(ws + W.tiles)));
         return MOE_OK;
     }
     float *lg = logits_out ? logits_out : reinterpret_cast<float *>(ws + W.logits);
@@ -586,8 +579,7 @@ moe_status experts_impl(moe_handle *h, const void *x, int32_t T, const moe_routi
     uint16_t *Acat = reinterpret_cast<uint16_t *>(ws + W.acat);
     uint16_t *Hb = reinterpret_cast<uint16_t *>(ws + W.h);
     uint16_t *Yb = reinterpret_cast<uint16_t *>(ws + W.y);
-    int32_t *tiles1 = reinterpret_cast<int32_t *>(ws + W.tiles1);
-    int32_t *tiles2 = reinterpret_cast<int32_t *>(ws + W.tiles2);
+    int32_t *tl = reinterpret_cast<int32_t *>(ws + W.tiles);
     const bool tiled = tiled_experts(c, T);
     {   // h = bf16(silu(z Wg_e^T) (z Wu_e^T)) for every pair, rows in expert-sorted order
         GemmArgs g{};
@@ -599,12 +591,12 @@ moe_status experts_impl(moe_handle *h, const void *x, int32_t T, const moe_routi
         g.b_stride = h->gateup_stride;
         g.N = 2 * I;
         g.K = Lt;
-        g.tiles = tiles1;
+        g.tiles = tl;
         g.split = INT_MAX;
         g.lo = OutDesc{OUT_GLU, Hb, I, 0, INT_MAX, nullptr};
-        MOE_LAUNCH(MOE_KERNEL_GATEUP, tiled ? launch_tiled(g, true, (int)W.max_tiles1, st)
+        MOE_LAUNCH(MOE_KERNEL_GATEUP, tiled ? launch_tiled(g, true, (int)W.max_tiles, st)
                                             : launch_gemm_grouped(g, (2 * I) % 64 ? GEMM_MX_GLU_M16 : GEMM_MX_GLU_M16_N64,
-                                                                  (int)W.max_tiles1, st));
+                                                                  (int)W.max_tiles, st));
     }
     {   // y = bf16(h Wd_e^T), unweighted, expert-sorted rows
         GemmArgs g{};
@@ -614,12 +606,12 @@ moe_status experts_impl(moe_handle *h, const void *x, int32_t T, const moe_routi
         g.b_stride = h->down_stride;
         g.N = Lt;
         g.K = I;
-        g.tiles = tiles2;
+        g.tiles = tl;
         g.split = INT_MAX;
         g.lo = OutDesc{OUT_BF16, Yb, Lt, 0, Lt, nullptr};
-        MOE_LAUNCH(MOE_KERNEL_DOWN, !tiled ? launch_gemm_grouped(g, GEMM_MX_M16_N64, (int)W.max_tiles2, st)
-                                    : astat_supported(g) ? launch_astat(g, (int)W.max_tiles2, st)
-                                                         : launch_tiled(g, true, (int)W.max_tiles2, st));
+        MOE_LAUNCH(MOE_KERNEL_DOWN, !tiled ? launch_gemm_grouped(g, GEMM_MX_M16_N64, (int)W.max_tiles, st)
+                                    : astat_supported(g) ? launch_astat(g, (int)W.max_tiles, st)
+                                                         : launch_tiled(g, true, (int)W.max_tiles, st));
     }
     // zc = bf16(sum_j w_j y_j) in slot order: into the first Lt columns of [zc | h_s], or the output
     MOE_LAUNCH(MOE_KERNEL_COMBINE, launch_combine(Yb, Lt, r->inv, r->topk_w, T, K, lat ? Acat : static_cast<uint16_t *>(out),

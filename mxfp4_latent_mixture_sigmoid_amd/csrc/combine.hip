@@ -4,20 +4,16 @@
 
 namespace mxmoe {
 
-__global__ __launch_bounds__(1024) void tilemap_kernel(const int32_t *__restrict__ offsets, int E, int bm1,
-                                                       int32_t *__restrict__ tiles1, int bm2,
-                                                       int32_t *__restrict__ tiles2)
+__global__ __launch_bounds__(1024) void tilemap_kernel(const int32_t *__restrict__ offsets, int E, int bm,
+                                                       int32_t *__restrict__ tiles)
 {
     __shared__ int sh[16];
-    write_tiles(offsets, E, bm1, tiles1, sh);
-    if (bm2 > 0)
-        write_tiles(offsets, E, bm2, tiles2, sh);
+    write_tiles(offsets, E, bm, tiles, sh);
 }
 
-hipError_t launch_tilemap(const int32_t *offsets, int E, int bm1, int32_t *tiles1, int bm2, int32_t *tiles2,
-                          hipStream_t st)
+hipError_t launch_tilemap(const int32_t *offsets, int E, int bm, int32_t *tiles, hipStream_t st)
 {
-    hipLaunchKernelGGL(tilemap_kernel, dim3(1), dim3(1024), 0, st, offsets, E, bm1, tiles1, bm2, tiles2);
+    hipLaunchKernelGGL(tilemap_kernel, dim3(1), dim3(1024), 0, st, offsets, E, bm, tiles);
     return hipGetLastError();
 }
 

@@ -113,9 +113,9 @@ struct XsideEpiArgs {
     uint16_t *z;                         // [M, Lt]
     uint16_t *acat;                      // [M, ldcat]; h_s written at columns Lt..
     int64_t ldcat;
-    const int32_t *offsets;              // tile lists (extra last workgroup; none if tiles1 is null)
-    int E, bm1, bm2;
-    int32_t *tiles1, *tiles2;
+    const int32_t *offsets;              // expert tile list (extra last workgroup; none if tiles is null)
+    int E, bm;
+    int32_t *tiles;
 };
 hipError_t launch_xside_epilogue(const XsideEpiArgs &e, hipStream_t st);
 hipError_t launch_out_epilogue(const float *P, int64_t split_stride, int splits, int M, int N, uint16_t *out,
@@ -140,17 +140,16 @@ constexpr int PERM_SMALL_MAX_T = 256;
 hipError_t launch_topk(const TopkArgs &a, hipStream_t st);
 // Top-K from split-K partials together with the x-side epilogue (no tile lists) in one launch.
 hipError_t launch_topk_xside(const TopkArgs &a, const XsideEpiArgs &e, hipStream_t st);
-// Grouping for T <= PERM_SMALL_MAX_T in one workgroup; with tiles1 set it also writes the expert tile
-// list(s) of bm rows (tiles2 may be null).
+// Grouping for T <= PERM_SMALL_MAX_T in one workgroup; with `tiles` set it also writes the expert tile
+// list of bm rows.
 hipError_t launch_permute_small(const int32_t *ids, int T, int K, int E, int32_t *counts, int32_t *offsets,
                                 int32_t *sorted_pairs, int32_t *inv, hipStream_t st, int bm = 0,
-                                int32_t *tiles1 = nullptr, int32_t *tiles2 = nullptr);
+                                int32_t *tiles = nullptr);
 hipError_t launch_permute(const int32_t *ids, int T, int K, int E, int32_t *hist, int32_t *counts,
                           int32_t *offsets, int32_t *sorted_pairs, int32_t *inv, hipStream_t st);
 
 // Forward helpers.
-hipError_t launch_tilemap(const int32_t *offsets, int E, int bm1, int32_t *tiles1, int bm2, int32_t *tiles2,
-                          hipStream_t st);
+hipError_t launch_tilemap(const int32_t *offsets, int E, int bm, int32_t *tiles, hipStream_t st);
 hipError_t launch_combine(const uint16_t *Y, int Lt, const int32_t *inv, const float *w, int T, int K,
                           uint16_t *out, int64_t ldo, hipStream_t st);
 

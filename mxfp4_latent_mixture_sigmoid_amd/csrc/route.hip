@@ -241,7 +241,7 @@ __global__ __launch_bounds__(512) void topk_xside_kernel(const TopkArgs a, const
 
 hipError_t launch_topk_xside(const TopkArgs &a, const XsideEpiArgs &e, hipStream_t st)
 {
-    if (!a.partials || a.T > SKINNY_MAX_M || a.K > WAVE || a.E > 16 * WAVE || e.tiles1)
+    if (!a.partials || a.T > SKINNY_MAX_M || a.K > WAVE || a.E > 16 * WAVE || e.tiles)
         return hipErrorInvalidValue;
     const int ntopk = (a.T + 3) / 4;
     const int64_t items = (int64_t)(e.Lt / 16 + e.shared_cols / 32) * 4 * WAVE;
@@ -285,8 +285,7 @@ hipError_t launch_topk(const TopkArgs &a, hipStream_t st)
 __global__ __launch_bounds__(1024) void perm_small_kernel(const int32_t *__restrict__ ids, int T, int K, int E,
                                                           int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
                                                           int32_t *__restrict__ sorted_pairs, int32_t *__restrict__ inv,
-                                                          int bm, int32_t *__restrict__ tiles1,
-                                                          int32_t *__restrict__ tiles2)
+                                                          int bm, int32_t *__restrict__ tiles)
 {
     extern __shared__ uint32_t masks[];               // [E][W] then off[E + 1]
     __shared__ int sh[16];
@@ -327,22 +326,18 @@ __global__ __launch_bounds__(1024) void perm_small_kernel(const int32_t *__restr
         sorted_pairs[pos] = p;
         inv[p] = pos;
     }
-    if (tiles1) {
-        write_tiles(off, E, bm, tiles1, sh);
-        if (tiles2)
-            write_tiles(off, E, bm, tiles2, sh);
-    }
+    if (tiles)
+        write_tiles(off, E, bm, tiles, sh);
 }
 
 hipError_t launch_permute_small(const int32_t *ids, int T, int K, int E, int32_t *counts, int32_t *offsets,
-                                int32_t *sorted_pairs, int32_t *inv, hipStream_t st, int bm, int32_t *tiles1,
-                                int32_t *tiles2)
+                                int32_t *sorted_pairs, int32_t *inv, hipStream_t st, int bm, int32_t *tiles)
 {
-    if (T > PERM_SMALL_MAX_T || E > 1024 || (tiles1 && bm < 1))
+    if (T > PERM_SMALL_MAX_T || E > 1024 || (tiles && bm < 1))
         return hipErrorInvalidValue;
     const size_t lds = ((size_t)E * ((T + 31) / 32) + E + 1) * sizeof(uint32_t);
     hipLaunchKernelGGL(perm_small_kernel, dim3(1), dim3(1024), lds, st, ids, T, K, E, counts, offsets, sorted_pairs,
-                       inv, bm, tiles1, tiles2);
+                       inv, bm, tiles);
     return hipGetLastError();
 }
 

@@ -250,10 +250,9 @@ hipError_t launch_skinny(const SkinnyArgs &g, int waves, int chunk_steps, hipStr
 // requested, one extra (last) workgroup builds them.
 __global__ __launch_bounds__(256) void xside_epilogue_kernel(const XsideEpiArgs e)
 {
-    if (e.tiles1 && blockIdx.x == gridDim.x - 1) {
+    if (e.tiles && blockIdx.x == gridDim.x - 1) {
         __shared__ int sh[16];
-        write_tiles(e.offsets, e.E, e.bm1, e.tiles1, sh);
-        write_tiles(e.offsets, e.E, e.bm2, e.tiles2, sh);
+        write_tiles(e.offsets, e.E, e.bm, e.tiles, sh);
         return;
     }
     xside_epi_item(e, (int64_t)blockIdx.x * blockDim.x + threadIdx.x);
@@ -262,7 +261,7 @@ __global__ __launch_bounds__(256) void xside_epilogue_kernel(const XsideEpiArgs 
 hipError_t launch_xside_epilogue(const XsideEpiArgs &e, hipStream_t st)
 {
     const int64_t threads = (int64_t)(e.Lt / 16 + e.shared_cols / 32) * 4 * WAVE;
-    const unsigned blocks = (e.tiles1 ? 1 : 0) + (unsigned)((threads + 255) / 256);
+    const unsigned blocks = (e.tiles ? 1 : 0) + (unsigned)((threads + 255) / 256);
     hipLaunchKernelGGL(xside_epilogue_kernel, dim3(blocks), dim3(256), 0, st, e);
     return hipGetLastError();
 }

@@ -38,56 +38,38 @@ __device__ inline void token_keys(const TopkArgs &a, int t, float *v, uint32_t *
     }
 }
 
-__device__ inline uint64_t shfl_xor_u64(uint64_t v, int mask)
-{
-    const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, mask, WAVE);
-    const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), mask, WAVE);
-    return ((uint64_t)hi << 32) | lo;
-}
-
-// Bitonic sort of one 64-bit value per lane into descending lane order (lane 0 the largest).
-__device__ inline uint64_t wave_sort_desc_u64(uint64_t v)
-{
-    const int lane = threadIdx.x & (WAVE - 1);
-#pragma unroll
-    for (int k = 2; k <= WAVE; k <<= 1)
-#pragma unroll
-        for (int j = k >> 1; j > 0; j >>= 1) {
-            const uint64_t p = shfl_xor_u64(v, j);
-            const bool keep_max = ((lane & j) == 0) == ((lane & k) == 0);
-            v = keep_max ? (p > v ? p : v) : (p < v ? p : v);
-        }
-    return v;
-}
-
 // Top-K of one token by one wave from the order keys (0 = no expert), ties to the lower expert, and
 // the gate weights: sigmoid of the selected logits over their sum. Writes ids and w of token t.
 // Every candidate becomes one 64-bit value, key above the complemented expert index, so the order
-// (key descending, expert ascending) is plain unsigned order and all values differ. The K-th largest
-// of the 64 lane maxima bounds the K-th largest value from below (K lanes hold a value at least that
-// large), so only values at or above it can be selected; at most K lanes hold such values. When they
-// number at most 64 (the usual case), they are gathered through `scratch` (64 entries of this wave)
-// and sorted across the wave: lanes 0 .. K-1 then hold the selection in rank order. Otherwise K
-// rounds of wave-wide maxima select directly.
+// (key descending, expert ascending) is plain unsigned order and all values differ.
+//  1. bound: the K-th largest of the 64 lane maxima (keys only), built bit by bit from the top with
+//     one ballot per bit. At least K lanes hold a key >= bound, so every selected key is >= bound.
+//  2. The candidates (keys >= bound; K or a few more in practice) are gathered into `scratch` (64
+//     entries of this wave); each ranks itself against all of them by broadcast reads, and the K
+//     best are placed at their ranks, so lane k then holds the rank-k expert.
+//  3. With more than 64 candidates (heavy ties), K rounds of wave-wide maxima select directly.
 template <int SLOTS>
 __device__ inline void select_keys(const TopkArgs &a, int t, const uint32_t *key, uint64_t *scratch)
 {
     const int lane = threadIdx.x & (WAVE - 1);
+    const int K = a.K;
     uint64_t c[SLOTS];
-    uint64_t m = 0;
+    uint32_t mk = 0u;
 #pragma unroll
     for (int j = 0; j < SLOTS; j++) {
         c[j] = key[j] ? ((uint64_t)key[j] << 32) | (uint32_t)~(uint32_t)(lane + WAVE * j) : 0;
-        m = c[j] > m ? c[j] : m;
+        mk = key[j] > mk ? key[j] : mk;
     }
-    const uint64_t lane_max_sorted = wave_sort_desc_u64(m);
-    const uint32_t th_lo = (uint32_t)__shfl((int)(uint32_t)lane_max_sorted, a.K - 1, WAVE);
-    const uint32_t th_hi = (uint32_t)__shfl((int)(uint32_t)(lane_max_sorted >> 32), a.K - 1, WAVE);
-    const uint64_t th = ((uint64_t)th_hi << 32) | th_lo;
+    uint32_t bound = 0u;
+    for (int b = 31; b >= 0; b--) {
+        const uint32_t cand = bound | (1u << b);
+        if ((int)__popcll(__ballot(mk >= cand)) >= K)
+            bound = cand;
+    }
     int n = 0;
 #pragma unroll
     for (int j = 0; j < SLOTS; j++)
-        n += (c[j] >= th && c[j] != 0) ? 1 : 0;
+        n += (key[j] != 0u && key[j] >= bound) ? 1 : 0;
     const int incl = wave_incl_scan(n);
     const int total = __shfl(incl, WAVE - 1, WAVE);
     uint32_t my_key = 0u;
@@ -96,10 +78,15 @@ __device__ inline void select_keys(const TopkArgs &a, int t, const uint32_t *key
         int pos = incl - n;
 #pragma unroll
         for (int j = 0; j < SLOTS; j++)
-            if (c[j] >= th && c[j] != 0)
+            if (key[j] != 0u && key[j] >= bound)
                 scratch[pos++] = c[j];
         const uint64_t mine = lane < total ? scratch[lane] : 0;
-        const uint64_t r = wave_sort_desc_u64(mine);
+        int rank = 0;
+        for (int m = 0; m < total; m++)
+            rank += scratch[m] > mine ? 1 : 0;
+        if (lane < total && rank < K)
+            scratch[rank] = mine;
+        const uint64_t r = lane < K ? scratch[lane] : 0;
         my_key = (uint32_t)(r >> 32);
         my_id = (int)~(uint32_t)r;
     } else {
@@ -107,7 +94,7 @@ __device__ inline void select_keys(const TopkArgs &a, int t, const uint32_t *key
 #pragma unroll
         for (int j = 0; j < SLOTS; j++)
             left[j] = c[j];
-        for (int k = 0; k < a.K; k++) {
+        for (int k = 0; k < K; k++) {
             uint64_t bm = left[0];
 #pragma unroll
             for (int j = 1; j < SLOTS; j++)
@@ -125,11 +112,11 @@ __device__ inline void select_keys(const TopkArgs &a, int t, const uint32_t *key
                     left[j] = 0;
         }
     }
-    const float s = lane < a.K ? 1.0f / (1.0f + expf(-key_value(my_key))) : 0.0f;
+    const float s = lane < K ? 1.0f / (1.0f + expf(-key_value(my_key))) : 0.0f;
     const float sum = wave_sum_f32(s);
-    if (lane < a.K) {
-        a.ids[(int64_t)t * a.K + lane] = my_id;
-        a.w[(int64_t)t * a.K + lane] = s / sum;
+    if (lane < K) {
+        a.ids[(int64_t)t * K + lane] = my_id;
+        a.w[(int64_t)t * K + lane] = s / sum;
     }
 }
 

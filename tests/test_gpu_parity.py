@@ -190,6 +190,20 @@ def test_planted_ties_select_lower_index():
     G.check_forward(shape, inp, tied, oracle_logits_in=lg)
 
 
+@pytest.mark.parametrize("grid", [4.0, 0.25])
+def test_heavy_ties_select_lower_index(grid):
+    """Logits rounded to a coarse grid tie most of the 96 experts: with grid 4 nearly all of them
+    share the top value (more than 64 candidates for the last places), with 0.25 a few do. Either
+    way the selection must equal the oracle's (logit descending, lower expert first), bit for bit."""
+    shape, inp, layer = _setup("mid_zipf")
+    run = G.GpuRun(layer, shape, inp)
+    lg = (np.round(run.logits / grid) * grid).astype(np.float32)
+    top = np.sort(lg, 1)[:, ::-1]
+    assert np.any(top[:, shape.K - 1] == top[:, shape.K])        # ties straddle rank K
+    tied = G.GpuRun(layer, shape, dict(inp), logits_in=lg)
+    G.check_forward(shape, inp, tied, oracle_logits_in=lg)
+
+
 def test_bad_arguments_raise():
     from mxfp4_latent_mixture_sigmoid_amd import abi
     shape, inp, layer = _setup("tiny")

@@ -24,6 +24,12 @@ constexpr int TL_MF = TL_WAVE_M / 16, TL_NF = TL_WAVE_N / 16;   // 8 x 4 fragmen
 constexpr int TL_STAGE_K = 128;                                 // K per LDS stage
 constexpr int TL_SUB = TL_STAGE_K / 32;                         // 32-wide sub-steps per stage
 
+// s_waitcnt immediates: at most n vector-memory operations outstanding (the other counters free),
+// and no LDS (lgkm) operation outstanding (the others free).
+constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | (((n >> 4) & 3) << 14); }
+constexpr int LGKM_ZERO = 15 | (7 << 4) | (0 << 8) | (3 << 14);
+constexpr int vmcnt_lgkm_imm(int n) { return (n & 15) | (7 << 4) | (0 << 8) | (((n >> 4) & 3) << 14); }
+
 constexpr int TL_XCDS = 8;      // workgroups are dealt to the XCDs round-robin by linear id
 constexpr int TL_GROUP_M = 8;   // dense products: M tiles per group, walked M-fastest
 
@@ -99,6 +105,21 @@ __device__ __attribute__((always_inline)) inline void tiled_tile(const GemmArgs 
             lds[buf][((b / NMF) * TL_MFW + b % NMF) * WAVE + lane] = v[u];
         }
     };
+    // MXFP4 products stage A by direct global->LDS loads instead: one wave instruction fills one
+    // 1 KiB block (its LDS base is wave-uniform, lane l lands at slot l), with no register round
+    // trip. The compiler does not track these loads into LDS, so the stage loop waits for them
+    // itself (vmcnt) before the barrier that publishes the stage.
+    auto issue_a = [&](int stage, int buf) {
+#pragma unroll
+        for (int u = 0; u < NMF; u++) {
+            const int b = wv + 4 * u;
+            const int k = min(stage * TL_STAGE_K + (b / NMF) * 32, g.K - 32);
+            __builtin_amdgcn_global_load_lds(arow[u % FR] + k,
+                                             (__attribute__((address_space(3))) void *)&lds[buf][((b / NMF) * TL_MFW +
+                                                                                                 b % NMF) * WAVE],
+                                             16, 0, 0);
+        }
+    };
 
     // ---- B fragments of this wave
     bool nval[TL_NF];
@@ -113,12 +134,17 @@ __device__ __attribute__((always_inline)) inline void tiled_tile(const GemmArgs 
         for (int j = 0; j < TL_NF; j++)
             acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    {
+    if constexpr (MX) {
+        issue_a(0, 0);
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+    } else {
         u32x4_t av[NMF];
         load_a(0, av);
         store_a(0, av);
+        __syncthreads();
     }
-    __syncthreads();
 
     const bool wave_active = n0 < g.N;
     // B of this wave, prefetched ahead of use: MXFP4 one stage (128 inputs) ahead, BF16 one 32-wide
@@ -152,8 +178,11 @@ __device__ __attribute__((always_inline)) inline void tiled_tile(const GemmArgs 
 
     for (int st = 0; st < nstages; st++) {
         const int cur = st & 1;
-        u32x4_t an[NMF];
-        load_a(min(st + 1, nstages - 1), an);
+        u32x4_t an[MX ? 1 : NMF];
+        if constexpr (MX)
+            issue_a(min(st + 1, nstages - 1), cur ^ 1);   // before this stage's B prefetch (vmcnt order)
+        else
+            load_a(min(st + 1, nstages - 1), an);
 
         {
             if constexpr (MX) {
@@ -204,9 +233,22 @@ __device__ __attribute__((always_inline)) inline void tiled_tile(const GemmArgs 
                 }
             }
         }
-        store_a(cur ^ 1, an);
-        __syncthreads();
+        // This wave's part of the next stage's A is in LDS and its reads of this stage's are done,
+        // then the waves meet. The wait leaves the next stage's B prefetch (issued after the A loads:
+        // 2 TL_NF MXFP4 loads) in flight; a __syncthreads would wait for every outstanding global
+        // load and expose that latency once per stage.
+        asm volatile("" ::: "memory");
+        if constexpr (MX) {
+            __builtin_amdgcn_s_waitcnt(vmcnt_lgkm_imm(2 * TL_NF));
+        } else {
+            store_a(cur ^ 1, an);
+            __builtin_amdgcn_s_waitcnt(LGKM_ZERO);
+        }
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
     }
+    if constexpr (MX)
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // the last (repeated) A stage has landed before exit
 
     if (!wave_active)
         return;
@@ -292,7 +334,7 @@ __device__ __attribute__((always_inline)) inline void tiled_tile(const GemmArgs 
 }
 
 template <bool MX>
-__global__ __launch_bounds__(WAVE * 4) void tiled_kernel(const GemmArgs g, int gx, int gy)
+__global__ __launch_bounds__(WAVE * 4) __attribute__((amdgpu_waves_per_eu(2, 2))) void tiled_kernel(const GemmArgs g, int gx, int gy)
 {
     __shared__ u32x4_t lds[2][TL_SLOTS];
     int bx, by;
@@ -341,8 +383,6 @@ constexpr int RG_MF = RG_WM / 16;                          // 8 row fragments pe
 constexpr int RG_AF = RG_BM / 16, RG_BF = RG_BN / 16;      // 16 + 16 blocks per stage
 constexpr int RG_NBUF = 4;
 
-// s_waitcnt immediate that waits until at most n vector-memory operations are outstanding
-constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | (((n >> 4) & 3) << 14); }
 
 // Eight waves, 2 x 4, each 128 x 64 outputs (128 accumulators): two waves per SIMD, which cover
 // each other's waits (measured 1.07 PFLOP/s against 0.82 for four waves of 128 x 128 at one wave per

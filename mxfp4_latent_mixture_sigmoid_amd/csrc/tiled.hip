@@ -578,11 +578,13 @@ hipError_t launch_ring(const GemmArgs &g, hipStream_t st)
 // The workgroup stages its whole 128-row A tile (gathered rows, 128 x K BF16, at most 128 KiB) into
 // LDS once, in the operand order above, with direct global->LDS loads (one wave instruction fills
 // one 1 KiB block), then walks its run of 256-column N blocks. Each wave owns 128 x 64 outputs per
-// block; its MXFP4 B for the next block is loaded while this block multiplies, and the block's
-// outputs leave as 8-byte stores (four consecutive columns per lane) before the next block starts.
+// block; its MXFP4 B is loaded one 128-input block ahead (across N blocks too) while the current
+// one multiplies, and a block's outputs leave as 8-byte stores (four consecutive columns per lane)
+// before the next N block starts. (Eight waves over 512 columns, two per SIMD, spill at 256 VGPRs
+// and were slower; the 96 KiB A tile allows one workgroup per CU.)
 // Work is mapped XCD-major: the eight XCDs each take a contiguous run of the (tile, N-run) items
 // counted on the device, so the tiles of one expert share an L2.
-constexpr int AS_BM = 128, AS_BN = 256, AS_MF = 8, AS_NF = 4, AS_XCDS = 8;
+constexpr int AS_WAVES = 4, AS_BM = 128, AS_BN = AS_WAVES * TL_WAVE_N, AS_MF = 8, AS_NF = 4, AS_XCDS = 8;
 
 // One (tile, N-run) item whose rows need only the first NMF 16-row fragments.
 template <int KB, int NMF>
@@ -595,7 +597,7 @@ __device__ __attribute__((always_inline)) inline void astat_item(const GemmArgs 
 
     // A tile -> LDS: block (s, f) at s * AS_MF + f holds lane l's operand (row f*16 + l%16,
     // k = 32 s + 8 (l/16)); only the NMF fragments that hold valid rows are loaded.
-    for (int b = wv; b < KS * NMF; b += 4) {
+    for (int b = wv; b < KS * NMF; b += AS_WAVES) {
         const int s = b / NMF, f = b % NMF;
         const int r = min(m0 + f * 16 + (lane & 15), m1 - 1);   // clamped valid row, never stored
         const int64_t row = g.a_index ? (int64_t)(g.a_index[r] / g.a_div) : (int64_t)r;
@@ -606,21 +608,20 @@ __device__ __attribute__((always_inline)) inline void astat_item(const GemmArgs 
 
     const uint8_t *Bg = g.B + (int64_t)group * g.b_stride;
     const int nbmax = g.N / 16 - 1;
-    auto load_block = [&](int j, u32x4_t (&codes)[AS_NF][KB], uint32_t (&sc)[AS_NF][KB]) {
+    // B is prefetched one 128-input block ahead (the next block of this N block, or the first of the
+    // next N block), so a wave holds two blocks of B at a time.
+    auto load_kb = [&](int j, int kb, u32x4_t *codes, uint32_t *sc) {
 #pragma unroll
         for (int nf = 0; nf < AS_NF; nf++) {
             const int nb = min((j * AS_BN + wv * TL_WAVE_N) / 16 + nf, nbmax);
-#pragma unroll
-            for (int kb = 0; kb < KB; kb++) {
-                const uint8_t *p = Bg + ((int64_t)nb * KB + kb) * MX_BLOCK_BYTES;
-                codes[nf][kb] = load16_nt(p + lane * 16);
-                sc[nf][kb] = load4_nt(p + MX_CODE_BYTES + 4 * (lane & 15));
-            }
+            const uint8_t *p = Bg + ((int64_t)nb * KB + kb) * MX_BLOCK_BYTES;
+            codes[nf] = load16_nt(p + lane * 16);
+            sc[nf] = load4_nt(p + MX_CODE_BYTES + 4 * (lane & 15));
         }
     };
-    u32x4_t bc[AS_NF][KB];
-    uint32_t bs[AS_NF][KB];
-    load_block(j0, bc, bs);
+    u32x4_t bc[AS_NF];
+    uint32_t bs[AS_NF];
+    load_kb(j0, 0, bc, bs);
     __builtin_amdgcn_s_waitcnt(0);                               // A tile (and first B) have landed
     __syncthreads();
 
@@ -628,9 +629,6 @@ __device__ __attribute__((always_inline)) inline void astat_item(const GemmArgs 
     const int q = lane >> 4;
     uint16_t *out = reinterpret_cast<uint16_t *>(d.ptr);
     for (int j = j0; j < j1; j++) {
-        u32x4_t bn[AS_NF][KB];
-        uint32_t bsn[AS_NF][KB];
-        load_block(min(j + 1, j1 - 1), bn, bsn);
         f32x4_t acc[NMF][AS_NF];
 #pragma unroll
         for (int f = 0; f < NMF; f++)
@@ -638,7 +636,13 @@ __device__ __attribute__((always_inline)) inline void astat_item(const GemmArgs 
             for (int nf = 0; nf < AS_NF; nf++)
                 acc[f][nf] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kb = 0; kb < KB; kb++)
+        for (int kb = 0; kb < KB; kb++) {
+            u32x4_t bn[AS_NF];
+            uint32_t bsn[AS_NF];
+            if (kb + 1 < KB)
+                load_kb(j, kb + 1, bn, bsn);
+            else
+                load_kb(min(j + 1, j1 - 1), 0, bn, bsn);
 #pragma unroll
             for (int s = 0; s < TL_SUB; s++) {
                 u32x4_t a[NMF];
@@ -647,13 +651,19 @@ __device__ __attribute__((always_inline)) inline void astat_item(const GemmArgs 
                     a[f] = lds[((kb * TL_SUB + s) * AS_MF + f) * WAVE + lane];
 #pragma unroll
                 for (int nf = 0; nf < AS_NF; nf++) {
-                    const bf16x8_t b = mx_dequant8(bc[nf][kb][s], e8m0_to_f32((bs[nf][kb] >> (8 * s)) & 0xFFu));
+                    const bf16x8_t b = mx_dequant8(bc[nf][s], e8m0_to_f32((bs[nf] >> (8 * s)) & 0xFFu));
 #pragma unroll
                     for (int f = 0; f < NMF; f++)
                         acc[f][nf] = mfma16(b, as_bf16x8(a[f]), acc[f][nf]);
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
+#pragma unroll
+            for (int nf = 0; nf < AS_NF; nf++) {
+                bc[nf] = bn[nf];
+                bs[nf] = bsn[nf];
+            }
+        }
         // lane (q, c) of fragment (f, nf): row f*16 + c, columns nf*16 + 4q .. +3
 #pragma unroll
         for (int nf = 0; nf < AS_NF; nf++) {
@@ -669,18 +679,11 @@ __device__ __attribute__((always_inline)) inline void astat_item(const GemmArgs 
                                    f32_to_bf16_bits(acc[f][nf][2]) | (f32_to_bf16_bits(acc[f][nf][3]) << 16));
             }
         }
-#pragma unroll
-        for (int nf = 0; nf < AS_NF; nf++)
-#pragma unroll
-            for (int kb = 0; kb < KB; kb++) {
-                bc[nf][kb] = bn[nf][kb];
-                bs[nf][kb] = bsn[nf][kb];
-            }
     }
 }
 
 template <int KB>
-__global__ __launch_bounds__(WAVE * 4) void astat_kernel(const GemmArgs g, int nsplit)
+__global__ __launch_bounds__(WAVE * AS_WAVES) void astat_kernel(const GemmArgs g, int nsplit)
 {
     __shared__ u32x4_t lds[KB * TL_SUB * AS_MF * WAVE];
     const int total = g.tiles[0] * nsplit;
@@ -715,7 +718,7 @@ static hipError_t launch_astat_t(const GemmArgs &g, int max_tiles, hipStream_t s
     const int64_t grid = (items + AS_XCDS - 1) / AS_XCDS * AS_XCDS;
     if (grid > INT32_MAX)
         return hipErrorInvalidValue;
-    hipLaunchKernelGGL((astat_kernel<KB>), dim3((unsigned)grid), dim3(WAVE * 4), 0, st, g, nsplit);
+    hipLaunchKernelGGL((astat_kernel<KB>), dim3((unsigned)grid), dim3(WAVE * AS_WAVES), 0, st, g, nsplit);
     return hipGetLastError();
 }
 

@@ -26,8 +26,8 @@ __global__ __launch_bounds__(64) void combine_kernel(const uint16_t *__restrict_
                                                      const int32_t *__restrict__ inv, const float *__restrict__ w,
                                                      int K, uint16_t *__restrict__ out, int64_t ldo)
 {
-    const int t = blockIdx.x;
-    const int c8 = blockIdx.y * 64 + threadIdx.x;
+    const int t = blockIdx.y;
+    const int c8 = blockIdx.x * 64 + threadIdx.x;
     if (c8 * 8 >= Lt)
         return;
     const int32_t *it = inv + (int64_t)t * K;
@@ -69,7 +69,10 @@ __global__ __launch_bounds__(64) void combine_kernel(const uint16_t *__restrict_
 hipError_t launch_combine(const uint16_t *Y, int Lt, const int32_t *inv, const float *w, int T, int K,
                           uint16_t *out, int64_t ldo, hipStream_t st)
 {
-    const dim3 grid(T, (Lt / 8 + 63) / 64);
+    // column chunks fastest: the chunks of one token (its K rows of y read whole) run back to back
+    if (T > 65535)
+        return hipErrorInvalidValue;
+    const dim3 grid((Lt / 8 + 63) / 64, T);
     hipLaunchKernelGGL(combine_kernel, grid, dim3(64), 0, st, Y, Lt, inv, w, K, out, ldo);
     return hipGetLastError();
 }

@@ -1,40 +1,33 @@
-// gemm.hip -- BF16 matrix-core GEMMs C = A . B^T for the layer's dense and grouped products.
+// gemm.hip -- grouped MXFP4 expert products for few rows per expert (decode), where the time is
+// the HBM stream of the expert weights.
 //
-// A is a row-major BF16 activation matrix, optionally gathered row by row; B is a packed weight
-// matrix (BF16 or MXFP4, see common.hpp) streamed from HBM in fragment order so that every
-// 16-byte lane load is exactly one matrix-core operand and a wave's load covers 1 KiB of
-// contiguous memory. MXFP4 codes are converted to BF16 in registers with their E8M0 scale
-// (gfx950's scaled FP4 conversion) right before the 16x16x32 BF16 instruction; accumulation is
-// FP32. The waves of a workgroup split the K axis; their partial tiles are summed in LDS in a
-// fixed order, so the result does not depend on timing. The epilogue writes FP32 logits (+bias),
-// BF16, or the GLU h = bf16(silu(gate) * up) from gate/up column pairs.
+// A is a row-major BF16 activation matrix, gathered row by row through the expert-sorted order; B
+// is an expert's packed MXFP4 matrix (see common.hpp) streamed from HBM in fragment order so that
+// every 16-byte lane load holds four matrix-core operands and a wave's load covers 1 KiB of
+// contiguous memory. MXFP4 codes are converted to BF16 in registers with their E8M0 scale (gfx950's
+// scaled FP4 conversion) right before the 16x16x32 BF16 instruction; accumulation is FP32. The
+// waves of a workgroup split the K axis; their partial tiles are summed in LDS in a fixed order, so
+// the result does not depend on timing. The epilogue writes BF16, or the GLU
+// h = bf16(silu(gate) * up) from gate/up column pairs.
 #include "kernels.hpp"
 
 namespace mxmoe {
 
-template <int MT, int NT, int WK, bool MX>
+template <int MT, int NT, int WK>
 __global__ __launch_bounds__(WAVE *WK) void gemm_kernel(const GemmArgs g)
 {
     constexpr int BM = 16 * MT, BN = 16 * NT;
-    constexpr int STEP = MX ? MX_STEP : BF16_STEP;
+    constexpr int STEP = MX_STEP;
     __shared__ float red[WK * BM * BN];
 
     const int lane = threadIdx.x & (WAVE - 1);
     const int wv = threadIdx.x / WAVE;
 
     // Column block fastest in the launch order: neighbouring workgroups stream neighbouring weights.
-    int group = 0, m0, m1;
-    if (g.tiles) {
-        if ((int)blockIdx.y >= g.tiles[0])
-            return;
-        const int4 t = reinterpret_cast<const int4 *>(g.tiles + TILE_HEADER_INTS)[blockIdx.y];
-        group = t.x;
-        m0 = t.y;
-        m1 = t.z;
-    } else {
-        m0 = blockIdx.y * BM;
-        m1 = min(g.M, m0 + BM);
-    }
+    if ((int)blockIdx.y >= g.tiles[0])
+        return;
+    const int4 t = reinterpret_cast<const int4 *>(g.tiles + TILE_HEADER_INTS)[blockIdx.y];
+    const int group = t.x, m0 = t.y, m1 = t.z;
     const int n0 = blockIdx.x * BN;
 
     // Activation rows of this lane for each 16-row fragment (gathered when a_index is set).
@@ -62,7 +55,7 @@ __global__ __launch_bounds__(WAVE *WK) void gemm_kernel(const GemmArgs g)
             acc[mf][nf] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
     const u32x4_t zero4 = {0u, 0u, 0u, 0u};
-    if constexpr (MX) {
+    {
 #pragma unroll 2
         for (int s = s0; s < s1; s++) {
             u32x4_t codes[NT];
@@ -92,21 +85,6 @@ __global__ __launch_bounds__(WAVE *WK) void gemm_kernel(const GemmArgs g)
                         acc[mf][nf] = mfma16(as_bf16x8(a[mf][j]), b[nf], acc[mf][nf]);
             }
         }
-    } else {
-#pragma unroll 4
-        for (int s = s0; s < s1; s++) {
-            u32x4_t b[NT];
-#pragma unroll
-            for (int nf = 0; nf < NT; nf++)
-                b[nf] = load16_nt(Bg + bf16_block_index(n0 / 16 + nf, s, g.N, g.K) * BF16_BLOCK_BYTES + lane * 16);
-#pragma unroll
-            for (int mf = 0; mf < MT; mf++) {
-                const u32x4_t a = aval[mf] ? load16(arow[mf] + s * STEP) : zero4;
-#pragma unroll
-                for (int nf = 0; nf < NT; nf++)
-                    acc[mf][nf] = mfma16(as_bf16x8(a), as_bf16x8(b[nf]), acc[mf][nf]);
-            }
-        }
     }
 
     // Partial tiles to LDS: lane l holds rows 4 (l/16) + i, column l % 16 of each fragment.
@@ -121,7 +99,7 @@ __global__ __launch_bounds__(WAVE *WK) void gemm_kernel(const GemmArgs g)
             }
     __syncthreads();
 
-    const OutDesc d = (n0 < g.split) ? g.lo : g.hi;
+    const OutDesc d = g.lo;
     const int nthr = WAVE * WK;
     if (d.kind == OUT_GLU) {
         // Column pairs: within each 32 columns, 16 gate columns then the 16 matching up columns.
@@ -152,14 +130,7 @@ __global__ __launch_bounds__(WAVE *WK) void gemm_kernel(const GemmArgs g)
 #pragma unroll
             for (int w = 0; w < WK; w++)
                 v += red[(w * BM + row) * BN + col];
-            if (d.kind == OUT_F32) {
-                if (d.bias)
-                    v += d.bias[n];
-                reinterpret_cast<float *>(d.ptr)[(int64_t)r * d.ld + (n - d.col0)] = v;
-            } else {
-                reinterpret_cast<uint16_t *>(d.ptr)[(int64_t)r * d.ld + (n - d.col0)] =
-                    (uint16_t)f32_to_bf16_bits(v);
-            }
+            reinterpret_cast<uint16_t *>(d.ptr)[(int64_t)r * d.ld + (n - d.col0)] = (uint16_t)f32_to_bf16_bits(v);
         }
     }
 }
@@ -297,31 +268,18 @@ static hipError_t launch_stream(const GemmArgs &g, int max_tiles, hipStream_t st
     return hipGetLastError();
 }
 
-template <int MT, int NT, int WK, bool MX>
+template <int MT, int NT, int WK>
 static hipError_t launch(const GemmArgs &g, int grid_m, hipStream_t st)
 {
     constexpr int BN = 16 * NT;
-    if (g.N % BN != 0 || g.K % (MX ? MX_STEP : BF16_STEP) != 0)
+    if (g.N % BN != 0 || g.K % MX_STEP != 0 || !g.tiles || g.lo.kind == OUT_F32 || g.split < g.N)
         return hipErrorInvalidValue;
     if (grid_m <= 0)
         return hipSuccess;
     if (grid_m > 65535)
         return hipErrorInvalidValue;
-    hipLaunchKernelGGL((gemm_kernel<MT, NT, WK, MX>), dim3(g.N / BN, grid_m), dim3(WAVE * WK), 0, st, g);
+    hipLaunchKernelGGL((gemm_kernel<MT, NT, WK>), dim3(g.N / BN, grid_m), dim3(WAVE * WK), 0, st, g);
     return hipGetLastError();
-}
-
-// Dense products (row count M known on the host).
-hipError_t launch_gemm_dense(const GemmArgs &g, GemmShape shape, hipStream_t st)
-{
-    switch (shape) {
-    case GEMM_SKINNY_N16:
-        return launch<4, 1, 8, false>(g, (g.M + 63) / 64, st);
-    case GEMM_SKINNY_N32:
-        return launch<4, 2, 8, false>(g, (g.M + 63) / 64, st);
-    default:
-        return hipErrorInvalidValue;
-    }
 }
 
 // Grouped MXFP4 products over the tile list (upper bound `max_tiles` workgroup rows).
@@ -329,11 +287,11 @@ hipError_t launch_gemm_grouped(const GemmArgs &g, GemmShape shape, int max_tiles
 {
     switch (shape) {
     case GEMM_MX_GLU_M16:
-        return launch<1, 2, 4, true>(g, max_tiles, st);
+        return launch<1, 2, 4>(g, max_tiles, st);
     case GEMM_MX_M16_N64:
         return launch_stream<4, 1, 1, 3>(g, max_tiles, st);
     case GEMM_MX_GLU_M16_N64:
-        return launch<1, 4, 4, true>(g, max_tiles, st);
+        return launch<1, 4, 4>(g, max_tiles, st);
     default:
         return hipErrorInvalidValue;
     }

@@ -40,14 +40,10 @@ __device__ inline OutDesc out_region(const GemmArgs &g, int n)
 }
 
 enum GemmShape {
-    GEMM_SKINNY_N16 = 0,     // dense, 64 rows x 16 columns per workgroup, K split over 8 waves
-    GEMM_SKINNY_N32 = 1,     // dense, 64 rows x 32 columns (one GLU pair), K over 8 waves
-    GEMM_MX_GLU_M16 = 2,     // grouped MXFP4, 16 rows x one (16 gate + 16 up) pair, K over 4 waves
-    GEMM_MX_M16_N64 = 3,     // grouped MXFP4 stream, 16 rows x 64 columns, one wave
-    GEMM_MX_GLU_M16_N64 = 4, // grouped MXFP4, 16 rows x two (gate, up) pairs, K over 4 waves, per-step loads
+    GEMM_MX_GLU_M16 = 0,     // grouped MXFP4, 16 rows x one (16 gate + 16 up) pair, K over 4 waves
+    GEMM_MX_M16_N64 = 1,     // grouped MXFP4 stream, 16 rows x 64 columns, one wave
+    GEMM_MX_GLU_M16_N64 = 2, // grouped MXFP4, 16 rows x two (gate, up) pairs, K over 4 waves, per-step loads
 };
-
-hipError_t launch_gemm_dense(const GemmArgs &g, GemmShape shape, hipStream_t st);
 
 // Tiled matrix-core product for many rows: 128 x 256 outputs per workgroup.
 // Dense (g.tiles null: rows 0..M-1) or grouped (tile list, at most `max_tiles` entries).

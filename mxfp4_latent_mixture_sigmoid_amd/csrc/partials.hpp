@@ -7,25 +7,9 @@
 
 namespace mxmoe {
 
-// Sum of the K-chunk partials of one element, in chunk order; loads are issued in batches of
-// SUM_BATCH (addresses clamped, so every load is valid) before any of them is used.
+// Partial sums load SUM_BATCH splits at a time (addresses clamped, so every load is valid) before
+// any of them is used.
 constexpr int SUM_BATCH = 8;
-__device__ inline float sum_partials(const float *P, int64_t split_stride, int splits, int64_t idx)
-{
-    float v = 0.f;
-    for (int s0 = 0; s0 < splits; s0 += SUM_BATCH) {
-        float t[SUM_BATCH];
-#pragma unroll
-        for (int u = 0; u < SUM_BATCH; u++)
-            t[u] = P[min(s0 + u, splits - 1) * split_stride + idx];
-#pragma unroll
-        for (int u = 0; u < SUM_BATCH; u++)
-            if (s0 + u < splits)
-                v += t[u];
-    }
-    return v;
-}
-
 // Sum over the splits of one lane's 16-byte partial slot (four rows of one column), split order.
 __device__ inline f32x4_t sum_slot(const float *slot, int64_t split_stride, int splits)
 {

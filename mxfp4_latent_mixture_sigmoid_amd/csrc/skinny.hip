@@ -224,8 +224,8 @@ int skinny_splits(int K, int chunk_steps)
     return (K + chunk - 1) / chunk;
 }
 
-// chunk_steps (8 or 16) sets the K range of a split: a half packed chunk keeps the weight range of a
-// workgroup contiguous and halves its LDS, letting more workgroups share a CU.
+// One workgroup per (K split, group of `waves` 16-row blocks); chunk_steps (16: one packed K chunk)
+// sets the K range of a split. Only (4 waves, 16 steps) is built: the router product alone.
 hipError_t launch_skinny(const SkinnyArgs &g, int waves, int chunk_steps, hipStream_t st)
 {
     if (g.M < 1 || g.M > SKINNY_MAX_M || g.N % 16 || g.K % BF16_STEP)
@@ -239,9 +239,6 @@ hipError_t launch_skinny(const SkinnyArgs &g, int waves, int chunk_steps, hipStr
         return hipGetLastError();                                                                                     \
     }
     MOE_SKINNY(4, 16)
-    MOE_SKINNY(8, 16)
-    MOE_SKINNY(4, 8)
-    MOE_SKINNY(8, 8)
 #undef MOE_SKINNY
     return hipErrorInvalidValue;
 }

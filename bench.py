@@ -4,9 +4,9 @@
 One step = moe_route_forward over one batch of seeded synthetic tokens (router, top-K, grouping by
 expert, latent down-projection and shared gate/up, MXFP4 gate/up and down expert products,
 gate-weighted combine, up-projection plus shared down-projection) with the inputs already resident
-in HBM; the x-side products run on the library's second stream, concurrently with the routing, and
-the step is timed on the caller's stream, which waits for both. The same work as two calls
-(moe_route, then moe_forward, one stream) is timed too and reported beside it. Prints one JSON line.
+in HBM; the router and the x-side products run as one product over a combined weight copy, and
+the step is timed on the caller's stream. The same work as two calls (moe_route, then moe_forward,
+one stream) is timed too and reported beside it. Prints one JSON line.
 
 Default workload: one GPU's TP8 share of a Kimi K3 layer at decode size (64 tokens, hidden 7168,
 latent 3584, 896 experts top-16, expert intermediate 384, 2 shared experts).

@@ -151,9 +151,9 @@ class GpuRun:
 
 
 def check_fused_identical(layer, shape, inp: dict, run: GpuRun) -> None:
-    """moe_route_forward (x-side products on the handle's second stream, concurrent with the
-    routing) must reproduce the separate moe_route + moe_forward run bit for bit: the same kernels
-    and fixed-order sums, only the scheduling differs."""
+    """moe_route_forward (router and x-side products as one product over a combined weight copy,
+    top-K and x-side epilogue in one launch) must reproduce the separate moe_route + moe_forward run
+    bit for bit: every output element is summed in the same fixed order."""
     T = inp["x"].shape[0]
     x = dev(inp["x"])
     bias = None if inp.get("router_bias") is None else dev(inp["router_bias"])

@@ -20,9 +20,8 @@
  *  - Every pointer argument except the handle, the config and the structs themselves is DEVICE
  *    memory owned by the caller. The library never allocates device memory (no hipMalloc).
  *  - BF16 tensors are passed as 16-bit bit patterns, row-major, innermost dimension contiguous.
- *  - `stream` is a hipStream_t (NULL = the null stream). All device work is enqueued on it (the
- *    x-side products of moe_route_forward may run on the handle's second stream, ordered between
- *    the call's earlier and later work on `stream`) and the call returns without synchronising. Argument errors are reported synchronously before
+ *  - `stream` is a hipStream_t (NULL = the null stream). All device work is enqueued on it and the
+ *    call returns without synchronising. Argument errors are reported synchronously before
  *    anything is enqueued; launch failures return MOE_ERR_HIP; device faults surface at the
  *    caller's next synchronisation. No C++ exception crosses this boundary.
  *  - Results are deterministic: identical inputs give bitwise-identical outputs (no

@@ -204,6 +204,56 @@ def test_heavy_ties_select_lower_index(grid):
     G.check_forward(shape, inp, tied, oracle_logits_in=lg)
 
 
+def test_power_of_two_down_scales_double_the_output_bitwise():
+    """Raising every down-matrix E8M0 scale by one doubles each expert output exactly; with the
+    shared experts zeroed, zc and the output then double bit for bit too (every step is a product
+    or an FP32 sum of doubled terms, and BF16 rounding commutes with doubling). Routing is
+    untouched."""
+    shape = replace(MID, name="pow2", seed=23)
+    inp = make_inputs(shape)
+    inp0 = dict(inp, **{k: np.zeros_like(inp[k]) for k in ("sh_gate", "sh_up", "sh_down")})
+    inp1 = dict(inp0, down_scales=(inp0["down_scales"] + 1).astype(np.uint8))
+    runs = []
+    for d in (inp0, inp1):
+        layer = G.make_layer(shape, d, T_max=shape.T)
+        run = G.GpuRun(layer, shape, d)
+        runs.append((run, run.rows()))
+        layer.close()
+    (a, ra), (b, rb) = runs
+    assert np.array_equal(a.ids, b.ids) and np.array_equal(a.w, b.w)
+    for k in ("y", "zc", "out"):
+        assert np.array_equal(G.bf16_f64(rb[k]), 2.0 * G.bf16_f64(ra[k])), k
+    assert np.any(G.bf16_f64(ra["out"]) != 0.0)
+
+
+def test_expert_relabelling_leaves_the_output_unchanged_bitwise():
+    """Relabelling the experts consistently (router rows and every expert matrix moved to the new
+    index) selects the relabelled experts in the same rank order with the same weights, and every
+    expert row is computed from the same data in the same order: the output is bit-identical."""
+    shape = replace(MID, name="relabel", seed=29)
+    inp = make_inputs(shape)
+    perm = np.random.default_rng(5).permutation(shape.E)     # expert e becomes perm[e]
+    moved = dict(inp)
+    for k in ("w_router", "gate_codes", "gate_scales", "up_codes", "up_scales", "down_codes", "down_scales"):
+        a = np.empty_like(inp[k])
+        a[perm] = inp[k]
+        moved[k] = a
+    if inp.get("router_bias") is not None:
+        b = np.empty_like(inp["router_bias"])
+        b[perm] = inp["router_bias"]
+        moved["router_bias"] = b
+    runs = []
+    for d in (inp, moved):
+        layer = G.make_layer(shape, d, T_max=shape.T)
+        run = G.GpuRun(layer, shape, d)
+        runs.append((run, run.rows()))
+        layer.close()
+    (a, ra), (b, rb) = runs
+    assert np.array_equal(b.ids, perm[a.ids]) and np.array_equal(a.w, b.w)
+    for k in ("z", "y", "zc", "hs", "out"):
+        assert np.array_equal(ra[k], rb[k]), k
+
+
 def test_bad_arguments_raise():
     from mxfp4_latent_mixture_sigmoid_amd import abi
     shape, inp, layer = _setup("tiny")

@@ -335,6 +335,106 @@ void or_expert_down(const uint16_t *h, int64_t T, int64_t K, int64_t I, int64_t 
     }
 }
 
+/* ---------------------------------------------------- FP8 second stage (opt-in mode) ---------
+ * [K31-opt] ("Kimi K3.1 Pro on AMD Instinct GPUs", section "What we optimized", and its
+ * "Appendix: environment variables") runs the routed experts' second stage -- the down
+ * product -- in FP8. The pages fix neither the FP8 format nor the scale granularity; reading F1:
+ *  F1  h is quantised per pair row in blocks of 32 consecutive values along I (the down
+ *      product's input axis, the same blocks as the weights' scales) to OCP MX FP8: E4M3
+ *      elements with one E8M0 block scale 2^X. X follows the OCP MX v1.0 conversion rule,
+ *      X = floor(log2(max |h| over the block)) - 8 (8 = exponent of E4M3's largest normal),
+ *      clamped to [-127, 127]; an all-zero block takes X = -127. Each element h / 2^X is
+ *      rounded to nearest even at E4M3's precision (4 significant bits, subnormal quantum 2^-9)
+ *      and saturates at +-448; its sign bit is kept (also for zero).
+ *  F2  The down product then reads the dequantised values: y_p = bf16(sum_j q_j 2^X_j . Wd[n][j]).
+ */
+
+/* O10a. E4M3 (OCP, "FN": no infinities) value of an 8-bit code: bit 7 sign, bits 6..3 exponent
+ * (bias 7), bits 2..0 mantissa; exponent field 0 is subnormal (m/8 . 2^-6); S.1111.111 is NaN. */
+double or_e4m3(int code)
+{
+    int sign = (code >> 7) & 1, e = (code >> 3) & 15, m = code & 7;
+    if (e == 15 && m == 7)
+        return NAN;
+    double mag = (e == 0) ? ldexp((double)m, -9) : ldexp(1.0 + m / 8.0, e - 7);
+    return sign ? -mag : mag;
+}
+
+/* E4M3 code of |a| (a >= 0, finite) rounded to nearest even, saturating at 448; sign added by caller. */
+static int e4m3_round(double a)
+{
+    if (a == 0.0)
+        return 0;
+    int ex;
+    frexp(a, &ex);                       /* a = m 2^ex, 0.5 <= m < 1: leading bit at 2^(ex-1) */
+    int q = ex - 1 - 3;                  /* quantum for 4 significant bits */
+    if (q < -9)
+        q = -9;                          /* subnormal range */
+    double r = ldexp(nearbyint(ldexp(a, -q)), q);
+    if (r > 448.0)
+        r = 448.0;
+    /* encode r: find the code whose value is r (codes are monotone in magnitude) */
+    for (int c = 0; c <= 0x7E; c++)
+        if (or_e4m3(c) == r)
+            return c;
+    return -1;                           /* unreachable: r is an E4M3 value */
+}
+
+/* O10b. MX FP8 quantisation of h [R, I] bf16 (I a multiple of 32) per F1: codes u8 [R, I] and
+ * scale bytes u8 [R, I/32] (E8M0, 2^(code-127)). */
+void or_fp8_quant(const uint16_t *h, int64_t R, int64_t I, uint8_t *codes, uint8_t *scales)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < R; r++)
+        for (int64_t b = 0; b < I / 32; b++) {
+            const uint16_t *v = h + r * I + b * 32;
+            double amax = 0.0;
+            for (int i = 0; i < 32; i++) {
+                double a = fabs(or_bf16_to_double(v[i]));
+                if (a > amax)
+                    amax = a;
+            }
+            int X = -127;
+            if (amax > 0.0) {
+                int ex;
+                frexp(amax, &ex);        /* floor(log2 amax) = ex - 1 */
+                X = ex - 1 - 8;
+                if (X < -127)
+                    X = -127;
+                if (X > 127)
+                    X = 127;
+            }
+            scales[r * (I / 32) + b] = (uint8_t)(X + 127);
+            for (int i = 0; i < 32; i++) {
+                double x = or_bf16_to_double(v[i]);
+                int c = e4m3_round(ldexp(fabs(x), -X));
+                codes[r * I + b * 32 + i] = (uint8_t)(c | ((v[i] & 0x8000) ? 0x80 : 0));
+            }
+        }
+}
+
+/* O10c. The FP8 second stage on given quantised h (F2): y_p = bf16(sum_j q_pj 2^X . Wd_e[n][j]) for
+ * every pair p with e = ids[p]. codes [T*K, I], scales [T*K, I/32] by pair id; y [T*K, Lt]. */
+void or_expert_down_fp8(const uint8_t *hq, const uint8_t *hs, int64_t T, int64_t K, int64_t I, int64_t Lt,
+                        const int32_t *ids, const uint8_t *down_codes, const uint8_t *down_scales, uint16_t *y_out)
+{
+    const int64_t dcb = Lt * (I / 2), dsb = Lt * (I / 32);
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t p = 0; p < T * K; p++) {
+        const int64_t e = ids[p];
+        double *hv = (double *)malloc((size_t)I * sizeof(double));
+        for (int64_t j = 0; j < I; j++)
+            hv[j] = or_e4m3(hq[p * I + j]) * or_e8m0(hs[p * (I / 32) + j / 32]);
+        for (int64_t n = 0; n < Lt; n++) {
+            double acc = 0.0;
+            for (int64_t j = 0; j < I; j++)
+                acc += hv[j] * mx_elem(down_codes + e * dcb, down_scales + e * dsb, I, n, j);
+            y_out[p * Lt + n] = or_double_to_bf16(acc);
+        }
+        free(hv);
+    }
+}
+
 /* O9b. The down half of O9 on given h_s: ys[t] = sum_s h_s[t] . Wd_s^T (FP64, not rounded).
  * hs [T, S*Is] bf16; sd [S,H,Is]; ys [T,H]. */
 void or_shared_down(const uint16_t *hs, int64_t T, int64_t S, int64_t Is, const uint16_t *sd, int64_t H, double *ys)

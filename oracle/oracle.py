@@ -58,6 +58,9 @@ def lib():
             "or_output": (None, [P, I64, I64, P, I64, P, P]),
             "or_experts": (None, [P, I64, I64, P, I64, I64, P, P, P, P, P, P, P, P]),
             "or_combine": (None, [P, P, I64, I64, I64, P]),
+            "or_e4m3": (ctypes.c_double, [ctypes.c_int]),
+            "or_fp8_quant": (None, [P, I64, I64, P, P]),
+            "or_expert_down_fp8": (None, [P, P, I64, I64, I64, I64, P, P, P, P]),
             "or_num_threads": (ctypes.c_int, []),
             "or_expert_down": (None, [P, I64, I64, I64, I64, P, P, P, P]),
             "or_shared_down": (None, [P, I64, I64, I64, P, I64, P]),
@@ -225,6 +228,43 @@ def expert_down(h, ids, down_codes, down_scales) -> np.ndarray:
     return y
 
 
+def e4m3(code: int) -> float:
+    """Value of an OCP E4M3 code (NaN for S.1111.111)."""
+    return lib().or_e4m3(int(code))
+
+
+def fp8_quant(h) -> tuple[np.ndarray, np.ndarray]:
+    """MX FP8 quantisation of BF16 rows [R, I]: (E4M3 codes [R, I], E8M0 scale bytes [R, I/32])."""
+    h = _c(h, np.uint16)
+    R, I = h.shape
+    codes = np.empty((R, I), np.uint8)
+    scales = np.empty((R, I // 32), np.uint8)
+    lib().or_fp8_quant(_p(h), R, I, _p(codes), _p(scales))
+    return codes, scales
+
+
+def fp8_dequant(codes, scales) -> np.ndarray:
+    """Values of MX FP8 rows: code value times its block's scale (FP64)."""
+    codes = _c(codes, np.uint8)
+    scales = _c(scales, np.uint8)
+    table = np.array([e4m3(c) for c in range(256)], np.float64)
+    return table[codes] * np.repeat(np.ldexp(1.0, scales.astype(np.int64) - 127), 32, axis=1)
+
+
+def expert_down_fp8(hq, hs, ids, down_codes, down_scales) -> np.ndarray:
+    """y by pair id from quantised h (pair order) -- the FP8 second stage."""
+    hq = _c(hq, np.uint8)
+    hs = _c(hs, np.uint8)
+    ids = _c(ids, np.int32)
+    T, K = ids.shape
+    I = hq.shape[1]
+    Lt = down_codes.shape[1]
+    dc, ds = _c(down_codes, np.uint8), _c(down_scales, np.uint8)
+    y = np.empty((T * K, Lt), np.uint16)
+    lib().or_expert_down_fp8(_p(hq), _p(hs), T, K, I, Lt, _p(ids), _p(dc), _p(ds), _p(y))
+    return y
+
+
 def shared_down(hs, sh_down) -> np.ndarray:
     """sum over shared experts of h_s . Wd_s^T (FP64) from given h_s -- the down half of `shared`."""
     hs = _c(hs, np.uint16)
@@ -248,13 +288,16 @@ def combine(y, w) -> np.ndarray:
 
 # ------------------------------------------------------------------ whole layer
 
-def forward(inp: dict, K: int, logits_in=None, ids_in=None, want_intermediates=True) -> dict:
+def forward(inp: dict, K: int, logits_in=None, ids_in=None, want_intermediates=True,
+            stage2_fp8: bool = False) -> dict:
     """Whole routed-expert forward on the tokens of ``inp["x"]``.
 
     ``logits_in`` replaces the router product (as the library's logits input does);
     ``ids_in`` forces the expert selection (the floating-point parity protocol uses the
     selection that was already checked bit-exactly, so a near-tie cannot mask a numeric
-    comparison). Returns logits, ids, w, perm, z, h, y (pair order), zc, hs, ys, out.
+    comparison). ``stage2_fp8`` runs the down product on MX FP8 h (oracle.c, O10).
+    Returns logits, ids, w, perm, z, h, hq / hs8 (FP8 codes and scales, or None), y (pair
+    order), zc, hs, ys, out.
     """
     x = inp["x"]
     has_latent = "w_down" in inp
@@ -267,7 +310,11 @@ def forward(inp: dict, K: int, logits_in=None, ids_in=None, want_intermediates=T
     z = latent_down(x, inp["w_down"]) if has_latent else _c(x, np.uint16)
     h, y = experts(z, ids, inp["gate_codes"], inp["gate_scales"], inp["up_codes"],
                    inp["up_scales"], inp["down_codes"], inp["down_scales"],
-                   want_h=want_intermediates)
+                   want_h=want_intermediates or stage2_fp8)
+    hq = hs8 = None
+    if stage2_fp8:   # second stage on MX FP8 h instead of BF16 h
+        hq, hs8 = fp8_quant(h)
+        y = expert_down_fp8(hq, hs8, ids, inp["down_codes"], inp["down_scales"])
     zc = combine(y, w)
     hs = ys = None
     if has_latent:
@@ -276,4 +323,5 @@ def forward(inp: dict, K: int, logits_in=None, ids_in=None, want_intermediates=T
         out = output(zc, inp["w_up"], ys)
     else:
         out = zc
-    return dict(logits=lg, ids=ids, w=w, perm=perm, z=z, h=h, y=y, zc=zc, hs=hs, ys=ys, out=out)
+    return dict(logits=lg, ids=ids, w=w, perm=perm, z=z, h=h, hq=hq, hs8=hs8, y=y, zc=zc, hs=hs, ys=ys,
+                out=out)

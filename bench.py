@@ -9,7 +9,8 @@ the step is timed on the caller's stream. The same work as two calls (moe_route,
 one stream) is timed too and reported beside it. Prints one JSON line.
 
 Default workload: one GPU's TP8 share of a Kimi K3 layer at decode size (64 tokens, hidden 7168,
-latent 3584, 896 experts top-16, expert intermediate 384, 2 shared experts).
+latent 3584, 896 experts top-16, expert intermediate 384, 2 shared experts). `--stage2 fp8` times
+the layer with its FP8 second stage (h quantised to MX FP8 for the down product) instead.
 """
 from __future__ import annotations
 
@@ -26,6 +27,7 @@ sys.path.insert(0, ROOT)
 METRIC = "routed-MoE tokens/s per MI355X; HBM GB/s (decode), MFMA TFLOPS (prefill)"
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0       # MI355X dense BF16 matrix cores
+FP8_PEAK_TFLOPS = 5000.0        # MI355X dense FP8 matrix cores (the FP8 x FP4 down product's rate)
 MX_BYTES_PER_VALUE = 17 / 32    # E2M1 nibble + one E8M0 byte per 32 values
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
@@ -92,6 +94,9 @@ def main() -> int:
     ap.add_argument("--cpu-sample", type=int, default=16, help="tokens the CPU oracle evaluates")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES")
+    ap.add_argument("--stage2", choices=("bf16", "fp8"), default="bf16",
+                    help="arithmetic of the experts' down product: BF16 h (the layer as defined), or h "
+                         "quantised to MX FP8 on the scaled FP8 x FP4 matrix-core instruction")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -125,8 +130,9 @@ def main() -> int:
         return torch.from_numpy(a).cuda()
 
     weights = {k: dev(v) for k, v in inp.items() if k in abi.WEIGHT_FIELDS and v is not None}
+    fp8 = args.stage2 == "fp8"
     layer = MoELayer(shape.H, shape.Lt, shape.E, shape.K, shape.I, shape.S, shape.Is, shape.has_latent,
-                     weights, T_max=T)
+                     weights, T_max=T, stage2_fp8=fp8)
     torch.cuda.synchronize()
     del weights
     x = dev(inp["x"])
@@ -196,6 +202,19 @@ def main() -> int:
                     frac=round(achieved / BF16_PEAK_TFLOPS, 4))
     roof["kernel"] = "gateup"
     roof["traffic"] = read_traffic(shape.name, "gateup")
+    down_roof = None
+    if fp8:   # the FP8 x FP4 down product against its own roof
+        down_s = kernels_us["down"] * 1e-6
+        P = T * shape.K
+        if decode:
+            b = n_active * shape.Lt * shape.I * MX_BYTES_PER_VALUE + P * shape.I * 33 / 32 + P * shape.Lt * 2
+            down_roof = dict(bound="hbm", achieved=round(b / down_s / 1e9, 1), peak=HBM_PEAK_GBPS, unit="GB/s")
+        else:
+            f = 2 * P * shape.I * shape.Lt
+            down_roof = dict(bound="mfma", achieved=round(f / down_s / 1e12, 2), peak=FP8_PEAK_TFLOPS,
+                             unit="TFLOP/s")
+        down_roof["frac"] = round(down_roof["achieved"] / down_roof["peak"], 4)
+        down_roof["kernel"] = "down"
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -204,7 +223,7 @@ def main() -> int:
         sub = dict(inp, x=inp["x"][tok])
         print(f"[bench] CPU oracle on {len(tok)} tokens", file=sys.stderr, flush=True)
         c0 = time.perf_counter()
-        O.forward(sub, shape.K, want_intermediates=False)
+        O.forward(sub, shape.K, want_intermediates=False, stage2_fp8=fp8)
         csec = time.perf_counter() - c0
         cpu = dict(value=round(len(tok) / csec, 3), unit="tokens/s", cores=O.num_threads(), kind="oracle",
                    sample=f"{len(tok)} seeded tokens of {shape.name}, full forward in FP64 ({csec:.1f} s)")
@@ -221,11 +240,12 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "bf16+fp8" if fp8 else "bf16",
         "data": "synthetic",
         "config": {"workload": shape.name, "tokens": T, "hidden": shape.H, "latent": shape.Lt,
                    "experts": shape.E, "top_k": shape.K, "inter": shape.I, "shared_experts": shape.S,
-                   "shared_inter": shape.Is, "routing": shape.routing, "active_experts": n_active},
+                   "shared_inter": shape.Is, "routing": shape.routing, "active_experts": n_active,
+                   "stage2": args.stage2},
         "roofline": roof,
         "cpu_baseline": cpu,
         "gpu_ms_per_step": round(gpu_ms / args.steps, 5),
@@ -234,6 +254,8 @@ def main() -> int:
         "step_tflops": round(alg["step_flops"] / step_s / 1e12, 2),
         "kernels_us": kernels_us,
     }
+    if down_roof:
+        line["roofline_down"] = down_roof
     print(json.dumps(line), flush=True)
     layer.close()
     return 0

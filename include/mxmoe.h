@@ -51,6 +51,20 @@ typedef enum {
  * implemented reads it as the SiLU-gated GLU h = silu(g) * u, silu(g) = g * sigmoid(g). */
 typedef enum { MOE_ACT_SILU_GLU = 0 } moe_act;
 
+/* Arithmetic of the routed experts' second stage (the down product y = h . Wd_e^T).
+ * MOE_STAGE2_BF16: h is the BF16 GLU output (the layer as defined above).
+ * MOE_STAGE2_FP8:  h is first quantised to MX FP8 and the down product reads the quantised
+ *   values, as the reference engine's FP8 second stage does (page "Kimi K3.1 Pro on AMD Instinct
+ *   GPUs", section "What we optimized" and its appendix of environment variables). The pages fix
+ *   neither the FP8 format nor the scale granularity; this build takes the OCP MX FP8 reading:
+ *   per pair row, blocks of 32 consecutive h values along I share one E8M0 scale 2^X with
+ *   X = floor(log2(max |h| in the block)) - 8 (clamped to [-127, 127]; -127 for an all-zero
+ *   block), and each element h / 2^X is rounded to nearest even to an E4M3 code (4 significant
+ *   bits, subnormal quantum 2^-9, no infinities) that saturates at +-448 and keeps the sign of h.
+ *   The packed buffer then also holds the down weights in the layout of gfx950's scaled MX
+ *   matrix-core instruction. */
+typedef enum { MOE_STAGE2_BF16 = 0, MOE_STAGE2_FP8 = 1 } moe_stage2;
+
 typedef struct {
     int32_t hidden;          /* H: width of x and out (multiple of 128); unused without latent  */
     int32_t latent;          /* Lt: latent width (multiple of 128)                               */
@@ -61,6 +75,7 @@ typedef struct {
     int32_t shared_inter;    /* Is: shared-expert intermediate (multiple of 32 when S > 0)       */
     int32_t has_latent_proj; /* 1: x is the hidden state (down/up projections, shared experts)   */
     int32_t act;             /* moe_act                                                          */
+    int32_t stage2;          /* moe_stage2                                                       */
 } moe_config;
 
 /* Canonical weights (device, caller-owned; only read by moe_create's packing kernels, so they
@@ -104,8 +119,10 @@ moe_status moe_query(const moe_config *cfg, int32_t T_max, size_t *packed_bytes,
 
 /* Test hook: byte offsets inside the workspace for T tokens, in this order: FP32 logits [T,E],
  * per-block expert histogram, the expert tile list, z [T,Lt], [zc | h_s] [T, Lt + S Is],
- * h [T K, I] and y [T K, Lt] (expert-sorted rows, BF16), FP32 split-K partials, then the total
- * size. `offsets` is a host array of 9 entries. Host-only. */
+ * h [T K, I] and y [T K, Lt] (expert-sorted rows, BF16), the MX FP8 h of MOE_STAGE2_FP8 (E4M3
+ * codes [T K, I], then from byte offset T K I the E8M0 scales [T K, I/32]; empty otherwise),
+ * FP32 split-K partials, then the total size. `offsets` is a host array of 10 entries.
+ * Host-only. */
 moe_status moe_query_workspace_layout(const moe_config *cfg, int32_t T, size_t *offsets);
 
 /* Validate the config and weights, then enqueue the packing of every weight into `packed`
@@ -160,7 +177,8 @@ typedef enum {
     MOE_KERNEL_OUT = 8,      /* up-projection + shared down-projection              */
     MOE_KERNEL_XSIDE_EPI = 9,/* few-token x-side partial sums, GLU and tile lists   */
     MOE_KERNEL_OUT_EPI = 10, /* few-token output partial sums                       */
-    MOE_KERNEL_ROUTER_XSIDE = 11 /* router + x-side product as one (moe_route_forward) */
+    MOE_KERNEL_ROUTER_XSIDE = 11,/* router + x-side product as one (moe_route_forward) */
+    MOE_KERNEL_H_QUANT = 12  /* MX FP8 quantisation of h (MOE_STAGE2_FP8)           */
 } moe_kernel;
 
 /* Profiling hook (benchmarks, tests): after moe_profile_begin, every kernel launch of moe_route

@@ -17,7 +17,7 @@ struct moe_handle {
     int E_pad;           // router rows padded to 16
     int E_rx;            // router rows padded to 64 in the combined router + x-side matrix
     uint8_t *packed;
-    int64_t off_router, off_xside, off_rx, off_outside, off_gateup, off_down;
+    int64_t off_router, off_xside, off_rx, off_outside, off_gateup, off_down, off_down8;
     int64_t gateup_stride, down_stride;   // packed bytes per expert
     // profiling hook state
     bool prof = false;
@@ -55,6 +55,11 @@ bool valid_config(const moe_config *c)
         return false;
     if (c->act != MOE_ACT_SILU_GLU || (c->has_latent_proj != 0 && c->has_latent_proj != 1))
         return false;
+    if (c->stage2 != MOE_STAGE2_BF16 && c->stage2 != MOE_STAGE2_FP8)
+        return false;
+    // the FP8 down product keeps a whole 128-row tile of h (inter bytes per row) in LDS
+    if (c->stage2 == MOE_STAGE2_FP8 && (c->inter > FP8_DOWN_MAX_K || c->latent % 64))
+        return false;
     if (c->latent <= 0 || c->latent % 128 || c->inter <= 0 || c->inter % 128)
         return false;
     if (c->n_experts < 1 || c->n_experts > 1024 || c->top_k < 1 || c->top_k > 32 || c->top_k > c->n_experts)
@@ -75,7 +80,7 @@ bool valid_config(const moe_config *c)
 }
 
 struct PackedLayout {
-    int64_t router, xside, rx, outside, gateup, down, total, gateup_stride, down_stride;
+    int64_t router, xside, rx, outside, gateup, down, down8, total, gateup_stride, down_stride;
 };
 
 PackedLayout packed_layout(const moe_config *c)
@@ -103,12 +108,16 @@ PackedLayout packed_layout(const moe_config *c)
     off = align_up(off + c->n_experts * L.gateup_stride);
     L.down = off;
     off = align_up(off + c->n_experts * L.down_stride);
+    // FP8 second stage: the down weights once more, in the scaled instruction's operand layout
+    L.down8 = off;
+    if (c->stage2 == MOE_STAGE2_FP8)
+        off = align_up(off + c->n_experts * L.down_stride);
     L.total = off;
     return L;
 }
 
 struct WsLayout {
-    int64_t logits, hist, tiles, z, acat, h, y, partials, total;
+    int64_t logits, hist, tiles, z, acat, h, y, h8, partials, total;
     int64_t rpartials;                  // router partials (inside the partials region, before the dense ones)
     int64_t max_tiles;                  // capacity of the expert tile list (shared by both expert products)
 };
@@ -143,6 +152,9 @@ WsLayout ws_layout(const moe_config *c, int64_t T)
     off = align_up(off + T * K * I * 2);
     L.y = off;
     off = align_up(off + T * K * Lt * 2);
+    L.h8 = off;   // MX FP8 h: E4M3 codes [T K, I], then E8M0 scales [T K, I / 32]
+    if (c->stage2 == MOE_STAGE2_FP8)
+        off = align_up(off + T * K * I + T * K * (I / 32));
     L.partials = off;
     L.rpartials = off;
     if (T <= SKINNY_MAX_M) {   // split-K partial tiles of the few-token dense products
@@ -246,8 +258,8 @@ moe_status moe_query_workspace_layout(const moe_config *cfg, int32_t T, size_t *
     if (!valid_config(cfg) || T < 0 || !sizes_fit_int32(cfg, T) || !offsets)
         return MOE_ERR_INVALID_ARG;
     const WsLayout W = ws_layout(cfg, T);
-    const int64_t v[9] = {W.logits, W.hist, W.tiles, W.z, W.acat, W.h, W.y, W.rpartials, W.total};
-    for (int i = 0; i < 9; i++)
+    const int64_t v[10] = {W.logits, W.hist, W.tiles, W.z, W.acat, W.h, W.y, W.h8, W.rpartials, W.total};
+    for (int i = 0; i < 10; i++)
         offsets[i] = (size_t)v[i];
     return MOE_OK;
 }
@@ -292,6 +304,7 @@ moe_status moe_create(const moe_config *cfg, const moe_weights *w, void *packed,
     h->off_outside = L.outside;
     h->off_gateup = L.gateup;
     h->off_down = L.down;
+    h->off_down8 = L.down8;
     h->gateup_stride = L.gateup_stride;
     h->down_stride = L.down_stride;
 
@@ -318,6 +331,9 @@ moe_status moe_create(const moe_config *cfg, const moe_weights *w, void *packed,
     if (e == hipSuccess)
         e = launch_pack_down(h->packed + L.down, static_cast<const uint8_t *>(w->down_codes),
                              static_cast<const uint8_t *>(w->down_scales), E, I, Lt, st);
+    if (e == hipSuccess && cfg->stage2 == MOE_STAGE2_FP8)
+        e = launch_pack_down8(h->packed + L.down8, static_cast<const uint8_t *>(w->down_codes),
+                              static_cast<const uint8_t *>(w->down_scales), E, I, Lt, st);
     if (e != hipSuccess) {
         moe_destroy(h);
         return MOE_ERR_HIP;
@@ -598,7 +614,13 @@ moe_status experts_impl(moe_handle *h, const void *x, int32_t T, const moe_routi
                                             : launch_gemm_grouped(g, (2 * I) % 64 ? GEMM_MX_GLU_M16 : GEMM_MX_GLU_M16_N64,
                                                                   (int)W.max_tiles, st));
     }
-    {   // y = bf16(h Wd_e^T), unweighted, expert-sorted rows
+    if (c->stage2 == MOE_STAGE2_FP8) {   // h -> MX FP8, then y = bf16(h8 Wd_e^T) on the scaled instruction
+        const int64_t P = (int64_t)T * K;
+        uint8_t *h8 = ws + W.h8, *h8s = ws + W.h8 + P * I;
+        MOE_LAUNCH(MOE_KERNEL_H_QUANT, launch_fp8_quant(Hb, P, I, h8, h8s, st));
+        Fp8DownArgs g{h8, h8s, h->packed + h->off_down8, h->down_stride, Lt, I, tl, Yb, Lt};
+        MOE_LAUNCH(MOE_KERNEL_DOWN, launch_down_fp8(g, tiled, (int)W.max_tiles, st));
+    } else {   // y = bf16(h Wd_e^T), unweighted, expert-sorted rows
         GemmArgs g{};
         g.A = Hb;
         g.lda = I;

@@ -59,6 +59,25 @@ bool astat_supported(const GemmArgs &g);
 hipError_t launch_astat(const GemmArgs &g, int max_tiles, hipStream_t st);
 hipError_t launch_gemm_grouped(const GemmArgs &g, GemmShape shape, int max_tiles, hipStream_t st);
 
+// FP8 second stage: h -> MX FP8 (E4M3 codes [rows, I], E8M0 scales [rows, I/32]), and the down
+// product y = bf16(h8 . Wd_e^T) over the expert tile list on MX8-packed weights (fp8.hip).
+constexpr int FP8_DOWN_MAX_K = 512;
+struct Fp8DownArgs {
+    const uint8_t *codes;    // E4M3 h [rows, K], expert-sorted rows
+    const uint8_t *scales;   // E8M0 [rows, K / 32]
+    const uint8_t *B;        // MX8-packed weights of expert 0
+    int64_t b_stride;        // bytes between experts
+    int N, K;                // N = output columns (multiple of 64), K = I (multiple of 128, <= 512)
+    const int32_t *tiles;    // expert tile list
+    uint16_t *out;           // BF16 [rows, ldo]
+    int64_t ldo;
+};
+hipError_t launch_fp8_quant(const uint16_t *h, int64_t rows, int64_t I, uint8_t *codes, uint8_t *scales,
+                            hipStream_t st);
+hipError_t launch_down_fp8(const Fp8DownArgs &g, bool many_rows, int max_tiles, hipStream_t st);
+hipError_t launch_pack_down8(uint8_t *dst, const uint8_t *dc, const uint8_t *ds, int64_t E, int64_t I, int64_t Lt,
+                             hipStream_t st);
+
 // Packing (moe_create) and unpacking (test hook).
 hipError_t launch_pack_router(uint8_t *dst, const uint16_t *w, int64_t E, int64_t E_pad, int64_t Hin,
                               hipStream_t st);

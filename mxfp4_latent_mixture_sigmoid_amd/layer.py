@@ -16,9 +16,10 @@ class MoELayer:
     """
 
     def __init__(self, hidden, latent, n_experts, top_k, inter, n_shared, shared_inter,
-                 has_latent_proj, weights: dict, T_max: int, device="cuda", stream=None):
+                 has_latent_proj, weights: dict, T_max: int, device="cuda", stream=None,
+                 stage2_fp8: bool = False):
         self.cfg = abi.make_config(hidden, latent, n_experts, top_k, inter, n_shared, shared_inter,
-                                   has_latent_proj)
+                                   has_latent_proj, stage2_fp8)
         self.E, self.K, self.Lt = n_experts, top_k, latent
         self.H = hidden if has_latent_proj else latent
         self.T_max = T_max
@@ -52,7 +53,7 @@ class MoELayer:
         return out
 
     def route_forward(self, x, T, routing, out=None, logit_bias=None, logits_out=None, stream=None):
-        """route + forward in one call (x-side products concurrent with the routing)."""
+        """route + forward in one call, bitwise identical to the two calls."""
         self._check_T(T)
         if out is None:
             out = torch.empty(max(T, 1), self.H, dtype=torch.bfloat16, device=self.device)

@@ -87,3 +87,28 @@ def test_create_route_forward_reject_null_arguments_without_gpu_work():
     assert L.moe_forward(None, None, 4, ctypes.byref(r), None, None, 0, None) == abi.Status.INVALID_ARG
     assert L.moe_unpack_expert(None, 0, 0, None, None) == abi.Status.INVALID_ARG
     L.moe_destroy(None)
+
+
+def test_fp8_second_stage_sizes():
+    """MOE_STAGE2_FP8 adds one MX8 copy of the down weights and the FP8 h (codes + scales)."""
+    T, E, Lt, I, K = 64, 896, 3584, 384, 16
+    pb0, wb0 = abi.query(_cfg(), T)
+    pb1, wb1 = abi.query(_cfg(stage2_fp8=True), T)
+    mx_down = (Lt // 16) * (I // 128) * 1088
+    assert pb1 - pb0 == E * mx_down
+    lay0, lay1 = abi.workspace_layout(_cfg(), T), abi.workspace_layout(_cfg(stage2_fp8=True), T)
+    assert lay0["partials"] == lay0["h8"]                    # empty region in the BF16 mode
+    assert lay1["partials"] - lay1["h8"] == -(-(T * K * I + T * K * I // 32) // 256) * 256
+    assert wb1 - wb0 == lay1["partials"] - lay1["h8"]
+
+
+@pytest.mark.parametrize("kw", [dict(stage2_fp8=True, inter=640)])
+def test_fp8_second_stage_rejects_unsupported_shapes(kw):
+    c = _cfg(**kw)
+    assert abi.lib().moe_query(ctypes.byref(c), 64, None, None) == abi.Status.INVALID_ARG
+
+
+def test_unknown_second_stage_is_rejected():
+    c = _cfg()
+    c.stage2 = 2
+    assert abi.lib().moe_query(ctypes.byref(c), 64, None, None) == abi.Status.INVALID_ARG

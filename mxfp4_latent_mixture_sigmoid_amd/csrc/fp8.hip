@@ -248,17 +248,22 @@ __global__ __launch_bounds__(WAVE) void down8_stream_kernel(const Fp8DownArgs g)
 // run of 256-column N blocks; each of the four waves owns 128 x 64 outputs per N block. The
 // weights are operand A of the scaled instruction (FP4, rows = output columns) and h operand B
 // (FP8, columns = rows of h), so lane (q, c) of a fragment holds four consecutive output columns
-// 4q .. 4q+3 of row c and stores them as one 8-byte write. Weights are loaded one 128-input
-// block ahead (across N blocks too).
+// 4q .. 4q+3 of row c. The outputs leave through a 2 KiB LDS staging area per wave, one 16-row
+// fragment at a time, so that every store instruction writes whole 128-byte row segments (stores
+// of 32-byte pieces at the 7 KiB row stride ran at a quarter of the rate). Weights are loaded one
+// 128-input block ahead (across N blocks too).
 constexpr int A8_WAVES = 4, A8_BN = A8_WAVES * 64, A8_MF = 8, A8_NF = 4, A8_XCDS = 8;
+constexpr int A8_STAGE_PITCH = 144;                      // bytes per staged row (128 + 16 padding)
+constexpr int A8_STAGE_BYTES = 16 * A8_STAGE_PITCH;       // one 16-row fragment of one wave
 
 template <int KB, int NMF>
 __device__ __attribute__((always_inline)) inline void astat8_item(const Fp8DownArgs &g, int group, int m0, int m1,
-                                                                  int j0, int j1, u32x4_t *lds)
+                                                                  int j0, int j1, u32x4_t *lds, uint8_t *stage_all)
 {
     const int lane = threadIdx.x & (WAVE - 1);
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE);
     const int q = lane >> 4;
+    uint8_t *stage = stage_all + wv * A8_STAGE_BYTES;
 
     for (int b = wv; b < KB * 2 * NMF; b += A8_WAVES) {
         const int kb = b / (2 * NMF), s = (b / NMF) % 2, f = b % NMF;
@@ -334,18 +339,28 @@ __device__ __attribute__((always_inline)) inline void astat8_item(const Fp8DownA
                 bs[nf] = bsn[nf];
             }
         }
-#pragma unroll
-        for (int nf = 0; nf < A8_NF; nf++) {
-            const int n = j * A8_BN + wv * 64 + nf * 16 + 4 * q;
-            if (n >= g.N)
-                continue;
+        // Output through this wave's LDS staging area, one 16-row fragment at a time: lane (q, c)
+        // puts row c, columns nf*16 + 4q .. +3 in; then each lane takes 8 consecutive columns of
+        // one row, so a store instruction writes eight whole 128-byte row segments.
+        const int n0w = j * A8_BN + wv * 64;
+        if (n0w < g.N) {
 #pragma unroll
             for (int f = 0; f < NMF; f++) {
-                const int r = m0 + f * 16 + (lane & 15);
-                if (r < m1)
-                    *reinterpret_cast<uint2 *>(out + (int64_t)r * g.ldo + n) =
+#pragma unroll
+                for (int nf = 0; nf < A8_NF; nf++)
+                    *reinterpret_cast<uint2 *>(stage + (lane & 15) * A8_STAGE_PITCH + nf * 32 + 8 * q) =
                         make_uint2(f32_to_bf16_bits(acc[f][nf][0]) | (f32_to_bf16_bits(acc[f][nf][1]) << 16),
                                    f32_to_bf16_bits(acc[f][nf][2]) | (f32_to_bf16_bits(acc[f][nf][3]) << 16));
+                __builtin_amdgcn_wave_barrier();
+#pragma unroll
+                for (int h = 0; h < 2; h++) {
+                    const int rr = h * 8 + (lane >> 3);
+                    const u32x4_t v = *reinterpret_cast<const u32x4_t *>(stage + rr * A8_STAGE_PITCH + (lane & 7) * 16);
+                    const int r = m0 + f * 16 + rr;
+                    if (r < m1)
+                        *reinterpret_cast<u32x4_t *>(out + (int64_t)r * g.ldo + n0w + (lane & 7) * 8) = v;
+                }
+                __builtin_amdgcn_wave_barrier();
             }
         }
     }
@@ -356,6 +371,7 @@ __global__ __launch_bounds__(WAVE * A8_WAVES) __attribute__((amdgpu_waves_per_eu
 void astat8_kernel(const Fp8DownArgs g, int nsplit)
 {
     __shared__ u32x4_t lds[KB * 2 * A8_MF * WAVE];
+    __shared__ __attribute__((aligned(16))) uint8_t stage[A8_WAVES * A8_STAGE_BYTES];
     const int total = g.tiles[0] * nsplit;
     const int per = (total + A8_XCDS - 1) / A8_XCDS;
     const int slot = blockIdx.x / A8_XCDS;
@@ -370,11 +386,11 @@ void astat8_kernel(const Fp8DownArgs g, int nsplit)
         return;
     const int nmf = __builtin_amdgcn_readfirstlane((t.z - t.y + 15) / 16);
     if (nmf <= 2)
-        astat8_item<KB, 2>(g, t.x, t.y, t.z, j0, j1, lds);
+        astat8_item<KB, 2>(g, t.x, t.y, t.z, j0, j1, lds, stage);
     else if (nmf <= 4)
-        astat8_item<KB, 4>(g, t.x, t.y, t.z, j0, j1, lds);
+        astat8_item<KB, 4>(g, t.x, t.y, t.z, j0, j1, lds, stage);
     else
-        astat8_item<KB, 8>(g, t.x, t.y, t.z, j0, j1, lds);
+        astat8_item<KB, 8>(g, t.x, t.y, t.z, j0, j1, lds, stage);
 }
 
 template <int KB>
@@ -393,8 +409,8 @@ static hipError_t launch_astat8_t(const Fp8DownArgs &g, int max_tiles, hipStream
 hipError_t launch_down_fp8(const Fp8DownArgs &g, bool many_rows, int max_tiles, hipStream_t st)
 {
     if (!g.tiles || !g.codes || !g.scales || !g.B || !g.out || g.N <= 0 || g.N % 64 || g.K < MX_STEP ||
-        g.K % MX_STEP || g.K > FP8_DOWN_MAX_K || g.K % 16 || g.ldo < g.N || g.ldo % 4 ||
-        reinterpret_cast<uintptr_t>(g.codes) % 16 || reinterpret_cast<uintptr_t>(g.out) % 8)
+        g.K % MX_STEP || g.K > FP8_DOWN_MAX_K || g.ldo < g.N || g.ldo % 8 ||
+        reinterpret_cast<uintptr_t>(g.codes) % 16 || reinterpret_cast<uintptr_t>(g.out) % 16)
         return hipErrorInvalidValue;
     if (max_tiles <= 0)
         return hipSuccess;

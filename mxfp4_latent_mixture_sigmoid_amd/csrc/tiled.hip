@@ -585,15 +585,18 @@ hipError_t launch_ring(const GemmArgs &g, hipStream_t st)
 // Work is mapped XCD-major: the eight XCDs each take a contiguous run of the (tile, N-run) items
 // counted on the device, so the tiles of one expert share an L2.
 constexpr int AS_WAVES = 4, AS_BM = 128, AS_BN = AS_WAVES * TL_WAVE_N, AS_MF = 8, AS_NF = 4, AS_XCDS = 8;
+constexpr int AS_STAGE_PITCH = 144;                     // bytes per staged output row (128 + 16 padding)
+constexpr int AS_STAGE_BYTES = 16 * AS_STAGE_PITCH;      // one 16-row fragment of one wave
 
 // One (tile, N-run) item whose rows need only the first NMF 16-row fragments.
 template <int KB, int NMF>
 __device__ __attribute__((always_inline)) inline void astat_item(const GemmArgs &g, int group, int m0, int m1, int j0,
-                                                                 int j1, u32x4_t *lds)
+                                                                 int j1, u32x4_t *lds, uint8_t *stage_all)
 {
     constexpr int KS = KB * TL_SUB;                              // 32-wide sub-steps
     const int lane = threadIdx.x & (WAVE - 1);
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE);
+    uint8_t *stage = stage_all + wv * AS_STAGE_BYTES;
 
     // A tile -> LDS: block (s, f) at s * AS_MF + f holds lane l's operand (row f*16 + l%16,
     // k = 32 s + 8 (l/16)); only the NMF fragments that hold valid rows are loaded.
@@ -664,19 +667,29 @@ __device__ __attribute__((always_inline)) inline void astat_item(const GemmArgs 
                 bs[nf] = bsn[nf];
             }
         }
-        // lane (q, c) of fragment (f, nf): row f*16 + c, columns nf*16 + 4q .. +3
-#pragma unroll
-        for (int nf = 0; nf < AS_NF; nf++) {
-            const int n = j * AS_BN + wv * TL_WAVE_N + nf * 16 + 4 * q;
-            if (n >= d.n_valid)
-                continue;
+        // lane (q, c) of fragment (f, nf) holds row f*16 + c, columns nf*16 + 4q .. +3. The
+        // outputs leave through this wave's LDS staging area, one 16-row fragment at a time, so
+        // that each store instruction writes eight whole 128-byte row segments (32-byte pieces at
+        // the 7 KiB row stride stored at a quarter of the rate).
+        const int n0w = j * AS_BN + wv * TL_WAVE_N;
+        if (n0w < d.n_valid) {
 #pragma unroll
             for (int f = 0; f < NMF; f++) {
-                const int r = m0 + f * 16 + (lane & 15);
-                if (r < m1)
-                    *reinterpret_cast<uint2 *>(out + (int64_t)r * d.ld + n) =
+#pragma unroll
+                for (int nf = 0; nf < AS_NF; nf++)
+                    *reinterpret_cast<uint2 *>(stage + (lane & 15) * AS_STAGE_PITCH + nf * 32 + 8 * q) =
                         make_uint2(f32_to_bf16_bits(acc[f][nf][0]) | (f32_to_bf16_bits(acc[f][nf][1]) << 16),
                                    f32_to_bf16_bits(acc[f][nf][2]) | (f32_to_bf16_bits(acc[f][nf][3]) << 16));
+                __builtin_amdgcn_wave_barrier();
+#pragma unroll
+                for (int h = 0; h < 2; h++) {
+                    const int rr = h * 8 + (lane >> 3);
+                    const u32x4_t v = *reinterpret_cast<const u32x4_t *>(stage + rr * AS_STAGE_PITCH + (lane & 7) * 16);
+                    const int r = m0 + f * 16 + rr;
+                    if (r < m1)
+                        *reinterpret_cast<u32x4_t *>(out + (int64_t)r * d.ld + n0w + (lane & 7) * 8) = v;
+                }
+                __builtin_amdgcn_wave_barrier();
             }
         }
     }
@@ -686,6 +699,7 @@ template <int KB>
 __global__ __launch_bounds__(WAVE * AS_WAVES) void astat_kernel(const GemmArgs g, int nsplit)
 {
     __shared__ u32x4_t lds[KB * TL_SUB * AS_MF * WAVE];
+    __shared__ __attribute__((aligned(16))) uint8_t stage[AS_WAVES * AS_STAGE_BYTES];
     const int total = g.tiles[0] * nsplit;
     const int per = (total + AS_XCDS - 1) / AS_XCDS;
     const int slot = blockIdx.x / AS_XCDS;
@@ -701,11 +715,11 @@ __global__ __launch_bounds__(WAVE * AS_WAVES) void astat_kernel(const GemmArgs g
     // one code path per workgroup, chosen by the tile's row count
     const int nmf = __builtin_amdgcn_readfirstlane((t.z - t.y + 15) / 16);
     if (nmf <= 2)
-        astat_item<KB, 2>(g, t.x, t.y, t.z, j0, j1, lds);
+        astat_item<KB, 2>(g, t.x, t.y, t.z, j0, j1, lds, stage);
     else if (nmf <= 4)
-        astat_item<KB, 4>(g, t.x, t.y, t.z, j0, j1, lds);
+        astat_item<KB, 4>(g, t.x, t.y, t.z, j0, j1, lds, stage);
     else
-        astat_item<KB, 8>(g, t.x, t.y, t.z, j0, j1, lds);
+        astat_item<KB, 8>(g, t.x, t.y, t.z, j0, j1, lds, stage);
 }
 
 template <int KB>
@@ -725,9 +739,10 @@ static hipError_t launch_astat_t(const GemmArgs &g, int max_tiles, hipStream_t s
 bool astat_supported(const GemmArgs &g)
 {
     const OutDesc &d = g.lo;
-    return g.tiles && g.K % MX_STEP == 0 && g.K >= MX_STEP && g.K <= AS_MAX_K && g.N % 16 == 0 && g.N > 0 &&
-           g.split >= g.N && d.kind == OUT_BF16 && d.col0 == 0 && d.n_valid <= g.N && d.n_valid % 4 == 0 &&
-           d.ld % 4 == 0 && reinterpret_cast<uintptr_t>(d.ptr) % 8 == 0 && g.lda % 8 == 0 &&
+    // whole 64-column wave slices are stored with 16-byte writes
+    return g.tiles && g.K % MX_STEP == 0 && g.K >= MX_STEP && g.K <= AS_MAX_K && g.N % 64 == 0 && g.N > 0 &&
+           g.split >= g.N && d.kind == OUT_BF16 && d.col0 == 0 && d.n_valid == g.N && d.ld % 8 == 0 &&
+           d.ld >= g.N && reinterpret_cast<uintptr_t>(d.ptr) % 16 == 0 && g.lda % 8 == 0 &&
            reinterpret_cast<uintptr_t>(g.A) % 16 == 0;
 }
 

@@ -130,4 +130,20 @@ __device__ inline uint32_t load4_nt(const void *p)
     return __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(p));
 }
 
+// Stores into a window of `rows` rows of `ld` BF16 values that starts at `base`, through a raw
+// buffer resource: a store whose byte offset lies past the window is dropped by the hardware's
+// range check, so tile epilogues issue every store instruction unconditionally (the same number
+// on every path, which lets the wait counts for loads issued before the stores stay exact instead
+// of also waiting for the stores). rows = 0 makes every store a no-op. The last dword is the
+// gfx9-family resource word (32-bit data format, no swizzle).
+typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
+__device__ inline __amdgpu_buffer_rsrc_t row_window(void *base, int rows, int ld)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, rows * ld * 2, 0x00020000);
+}
+__device__ inline void store16_window(u32x4_t v, __amdgpu_buffer_rsrc_t w, int byte_offset)
+{
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4_t, v), w, byte_offset, 0, 0);
+}
+
 } // namespace mxmoe

@@ -342,26 +342,25 @@ __device__ __attribute__((always_inline)) inline void astat8_item(const Fp8DownA
         // Output through this wave's LDS staging area, one 16-row fragment at a time: lane (q, c)
         // puts row c, columns nf*16 + 4q .. +3 in; then each lane takes 8 consecutive columns of
         // one row, so a store instruction writes eight whole 128-byte row segments.
+        // Rows past the tile end, and a column slice past N, fall outside the store window.
         const int n0w = j * A8_BN + wv * 64;
-        if (n0w < g.N) {
+        const int wrows = n0w < g.N ? min(m1 - m0, NMF * 16) : 0;
+        const auto win = row_window(wrows > 0 ? out + (int64_t)m0 * g.ldo + n0w : out, wrows, g.ldo);
 #pragma unroll
-            for (int f = 0; f < NMF; f++) {
+        for (int f = 0; f < NMF; f++) {
 #pragma unroll
-                for (int nf = 0; nf < A8_NF; nf++)
-                    *reinterpret_cast<uint2 *>(stage + (lane & 15) * A8_STAGE_PITCH + nf * 32 + 8 * q) =
-                        make_uint2(f32_to_bf16_bits(acc[f][nf][0]) | (f32_to_bf16_bits(acc[f][nf][1]) << 16),
-                                   f32_to_bf16_bits(acc[f][nf][2]) | (f32_to_bf16_bits(acc[f][nf][3]) << 16));
-                __builtin_amdgcn_wave_barrier();
+            for (int nf = 0; nf < A8_NF; nf++)
+                *reinterpret_cast<uint2 *>(stage + (lane & 15) * A8_STAGE_PITCH + nf * 32 + 8 * q) =
+                    make_uint2(f32_to_bf16_bits(acc[f][nf][0]) | (f32_to_bf16_bits(acc[f][nf][1]) << 16),
+                               f32_to_bf16_bits(acc[f][nf][2]) | (f32_to_bf16_bits(acc[f][nf][3]) << 16));
+            __builtin_amdgcn_wave_barrier();
 #pragma unroll
-                for (int h = 0; h < 2; h++) {
-                    const int rr = h * 8 + (lane >> 3);
-                    const u32x4_t v = *reinterpret_cast<const u32x4_t *>(stage + rr * A8_STAGE_PITCH + (lane & 7) * 16);
-                    const int r = m0 + f * 16 + rr;
-                    if (r < m1)
-                        *reinterpret_cast<u32x4_t *>(out + (int64_t)r * g.ldo + n0w + (lane & 7) * 8) = v;
-                }
-                __builtin_amdgcn_wave_barrier();
+            for (int h = 0; h < 2; h++) {
+                const int rr = h * 8 + (lane >> 3);
+                const u32x4_t v = *reinterpret_cast<const u32x4_t *>(stage + rr * A8_STAGE_PITCH + (lane & 7) * 16);
+                store16_window(v, win, ((f * 16 + rr) * g.ldo + (lane & 7) * 8) * 2);
             }
+            __builtin_amdgcn_wave_barrier();
         }
     }
 }

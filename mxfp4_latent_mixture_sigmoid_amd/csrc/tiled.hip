@@ -577,14 +577,16 @@ hipError_t launch_ring(const GemmArgs &g, hipStream_t st)
 // ---- A-stationary grouped MXFP4 product for short K (the down projection, K = I <= 512).
 // The workgroup stages its whole 128-row A tile (gathered rows, 128 x K BF16, at most 128 KiB) into
 // LDS once, in the operand order above, with direct global->LDS loads (one wave instruction fills
-// one 1 KiB block), then walks its run of 256-column N blocks. Each wave owns 128 x 64 outputs per
-// block; its MXFP4 B is loaded one 128-input block ahead (across N blocks too) while the current
-// one multiplies, and a block's outputs leave as 8-byte stores (four consecutive columns per lane)
-// before the next N block starts. (Eight waves over 512 columns, two per SIMD, spill at 256 VGPRs
-// and were slower; the 96 KiB A tile allows one workgroup per CU.)
+// one 1 KiB block), then walks its run of 256-column N blocks. Eight waves, two per SIMD so that one
+// wave's output stores and B waits overlap the other's matrix-core work: wave (mh, wn) owns rows
+// 64 mh .. 64 mh + 63 and columns 64 wn .. 64 wn + 63 of every N block (4 x 4 fragments, 64
+// accumulators per lane). When every valid row lies in the first 64 (an expert's short last tile),
+// the two row halves take alternate N blocks instead. Each wave's MXFP4 B is loaded one 128-input
+// block ahead (across N blocks too) while the current one multiplies. (At one wave per SIMD -- four
+// waves of 128 x 64 -- the kernel ran at half the rate; eight waves of 128 x 64 spill.)
 // Work is mapped XCD-major: the eight XCDs each take a contiguous run of the (tile, N-run) items
 // counted on the device, so the tiles of one expert share an L2.
-constexpr int AS_WAVES = 4, AS_BM = 128, AS_BN = AS_WAVES * TL_WAVE_N, AS_MF = 8, AS_NF = 4, AS_XCDS = 8;
+constexpr int AS_WAVES = 8, AS_WN = 4, AS_BM = 128, AS_BN = AS_WN * TL_WAVE_N, AS_MF = 8, AS_NF = 4, AS_XCDS = 8;
 constexpr int AS_STAGE_PITCH = 144;                     // bytes per staged output row (128 + 16 padding)
 constexpr int AS_STAGE_BYTES = 16 * AS_STAGE_PITCH;      // one 16-row fragment of one wave
 
@@ -594,8 +596,13 @@ __device__ __attribute__((always_inline)) inline void astat_item(const GemmArgs 
                                                                  int j1, u32x4_t *lds, uint8_t *stage_all)
 {
     constexpr int KS = KB * TL_SUB;                              // 32-wide sub-steps
+    constexpr int WF = NMF > 4 ? 4 : NMF;                        // row fragments per wave
+    constexpr int JSTEP = NMF > 4 ? 1 : 2;                       // N blocks are split between row halves
     const int lane = threadIdx.x & (WAVE - 1);
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE);
+    const int wn = wv % AS_WN, mh = wv / AS_WN;
+    const int fb = NMF > 4 ? mh * 4 : 0;                         // this wave's first row fragment
+    const int jb = NMF > 4 ? j0 : j0 + mh;                       // this wave's first N block
     uint8_t *stage = stage_all + wv * AS_STAGE_BYTES;
 
     // A tile -> LDS: block (s, f) at s * AS_MF + f holds lane l's operand (row f*16 + l%16,
@@ -612,11 +619,11 @@ __device__ __attribute__((always_inline)) inline void astat_item(const GemmArgs 
     const uint8_t *Bg = g.B + (int64_t)group * g.b_stride;
     const int nbmax = g.N / 16 - 1;
     // B is prefetched one 128-input block ahead (the next block of this N block, or the first of the
-    // next N block), so a wave holds two blocks of B at a time.
+    // wave's next N block), so a wave holds two blocks of B at a time.
     auto load_kb = [&](int j, int kb, u32x4_t *codes, uint32_t *sc) {
 #pragma unroll
         for (int nf = 0; nf < AS_NF; nf++) {
-            const int nb = min((j * AS_BN + wv * TL_WAVE_N) / 16 + nf, nbmax);
+            const int nb = min((j * AS_BN + wn * TL_WAVE_N) / 16 + nf, nbmax);
             const uint8_t *p = Bg + ((int64_t)nb * KB + kb) * MX_BLOCK_BYTES;
             codes[nf] = load16_nt(p + lane * 16);
             sc[nf] = load4_nt(p + MX_CODE_BYTES + 4 * (lane & 15));
@@ -624,17 +631,17 @@ __device__ __attribute__((always_inline)) inline void astat_item(const GemmArgs 
     };
     u32x4_t bc[AS_NF];
     uint32_t bs[AS_NF];
-    load_kb(j0, 0, bc, bs);
+    load_kb(min(jb, j1 - 1), 0, bc, bs);
     __builtin_amdgcn_s_waitcnt(0);                               // A tile (and first B) have landed
     __syncthreads();
 
     const OutDesc d = g.lo;
     const int q = lane >> 4;
     uint16_t *out = reinterpret_cast<uint16_t *>(d.ptr);
-    for (int j = j0; j < j1; j++) {
-        f32x4_t acc[NMF][AS_NF];
+    for (int j = jb; j < j1; j += JSTEP) {
+        f32x4_t acc[WF][AS_NF];
 #pragma unroll
-        for (int f = 0; f < NMF; f++)
+        for (int f = 0; f < WF; f++)
 #pragma unroll
             for (int nf = 0; nf < AS_NF; nf++)
                 acc[f][nf] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -645,18 +652,18 @@ __device__ __attribute__((always_inline)) inline void astat_item(const GemmArgs 
             if (kb + 1 < KB)
                 load_kb(j, kb + 1, bn, bsn);
             else
-                load_kb(min(j + 1, j1 - 1), 0, bn, bsn);
+                load_kb(min(j + JSTEP, j1 - 1), 0, bn, bsn);
 #pragma unroll
             for (int s = 0; s < TL_SUB; s++) {
-                u32x4_t a[NMF];
+                u32x4_t a[WF];
 #pragma unroll
-                for (int f = 0; f < NMF; f++)
-                    a[f] = lds[((kb * TL_SUB + s) * AS_MF + f) * WAVE + lane];
+                for (int f = 0; f < WF; f++)
+                    a[f] = lds[((kb * TL_SUB + s) * AS_MF + fb + f) * WAVE + lane];
 #pragma unroll
                 for (int nf = 0; nf < AS_NF; nf++) {
                     const bf16x8_t b = mx_dequant8(bc[nf][s], e8m0_to_f32((bs[nf] >> (8 * s)) & 0xFFu));
 #pragma unroll
-                    for (int f = 0; f < NMF; f++)
+                    for (int f = 0; f < WF; f++)
                         acc[f][nf] = mfma16(b, as_bf16x8(a[f]), acc[f][nf]);
                 }
                 __builtin_amdgcn_sched_barrier(0);
@@ -667,30 +674,30 @@ __device__ __attribute__((always_inline)) inline void astat_item(const GemmArgs 
                 bs[nf] = bsn[nf];
             }
         }
-        // lane (q, c) of fragment (f, nf) holds row f*16 + c, columns nf*16 + 4q .. +3. The
+        // lane (q, c) of fragment (f, nf) holds row (fb + f)*16 + c, columns nf*16 + 4q .. +3. The
         // outputs leave through this wave's LDS staging area, one 16-row fragment at a time, so
         // that each store instruction writes eight whole 128-byte row segments (32-byte pieces at
         // the 7 KiB row stride stored at a quarter of the rate).
-        const int n0w = j * AS_BN + wv * TL_WAVE_N;
-        if (n0w < d.n_valid) {
+        // Rows past the tile end, and a column slice past N, fall outside the store window.
+        const int n0w = j * AS_BN + wn * TL_WAVE_N;
+        const int rbase = m0 + fb * 16;
+        const int wrows = n0w < d.n_valid ? max(0, min(m1 - rbase, WF * 16)) : 0;
+        const auto win = row_window(wrows > 0 ? out + (int64_t)rbase * d.ld + n0w : out, wrows, d.ld);
 #pragma unroll
-            for (int f = 0; f < NMF; f++) {
+        for (int f = 0; f < WF; f++) {
 #pragma unroll
-                for (int nf = 0; nf < AS_NF; nf++)
-                    *reinterpret_cast<uint2 *>(stage + (lane & 15) * AS_STAGE_PITCH + nf * 32 + 8 * q) =
-                        make_uint2(f32_to_bf16_bits(acc[f][nf][0]) | (f32_to_bf16_bits(acc[f][nf][1]) << 16),
-                                   f32_to_bf16_bits(acc[f][nf][2]) | (f32_to_bf16_bits(acc[f][nf][3]) << 16));
-                __builtin_amdgcn_wave_barrier();
+            for (int nf = 0; nf < AS_NF; nf++)
+                *reinterpret_cast<uint2 *>(stage + (lane & 15) * AS_STAGE_PITCH + nf * 32 + 8 * q) =
+                    make_uint2(f32_to_bf16_bits(acc[f][nf][0]) | (f32_to_bf16_bits(acc[f][nf][1]) << 16),
+                               f32_to_bf16_bits(acc[f][nf][2]) | (f32_to_bf16_bits(acc[f][nf][3]) << 16));
+            __builtin_amdgcn_wave_barrier();
 #pragma unroll
-                for (int h = 0; h < 2; h++) {
-                    const int rr = h * 8 + (lane >> 3);
-                    const u32x4_t v = *reinterpret_cast<const u32x4_t *>(stage + rr * AS_STAGE_PITCH + (lane & 7) * 16);
-                    const int r = m0 + f * 16 + rr;
-                    if (r < m1)
-                        *reinterpret_cast<u32x4_t *>(out + (int64_t)r * d.ld + n0w + (lane & 7) * 8) = v;
-                }
-                __builtin_amdgcn_wave_barrier();
+            for (int h = 0; h < 2; h++) {
+                const int rr = h * 8 + (lane >> 3);
+                const u32x4_t v = *reinterpret_cast<const u32x4_t *>(stage + rr * AS_STAGE_PITCH + (lane & 7) * 16);
+                store16_window(v, win, ((f * 16 + rr) * d.ld + (lane & 7) * 8) * 2);
             }
+            __builtin_amdgcn_wave_barrier();
         }
     }
 }

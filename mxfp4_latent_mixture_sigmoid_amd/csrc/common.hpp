@@ -62,20 +62,16 @@ __host__ __device__ inline int64_t mx_packed_bytes(int64_t N, int64_t K)
 // ---------------------------------------------------------------------------------------------
 __device__ inline float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
-// float -> BF16 bits, round to nearest even (NaN kept quiet).
-__device__ inline uint32_t f32_to_bf16_bits(float f)
-{
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7FFFFFFFu) > 0x7F800000u)
-        return ((u >> 16) | 0x40u) & 0xFFFFu;
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return u >> 16;
-}
-
+// Two floats -> packed BF16 bits (lo in bits 0..15), rounded to nearest even by gfx950's packed
+// conversion instruction (NaN stays a quiet NaN).
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 __device__ inline uint32_t pack_bf16x2(float lo, float hi)
 {
-    return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
+
+// float -> BF16 bits, round to nearest even.
+__device__ inline uint32_t f32_to_bf16_bits(float f) { return pack_bf16x2(f, 0.0f) & 0xFFFFu; }
 
 // E8M0 byte -> the float 2^(e-127) used as the conversion scale (255 -> NaN).
 __device__ inline float e8m0_to_f32(uint32_t e)

@@ -351,8 +351,8 @@ __device__ __attribute__((always_inline)) inline void astat8_item(const Fp8DownA
 #pragma unroll
             for (int nf = 0; nf < A8_NF; nf++)
                 *reinterpret_cast<uint2 *>(stage + (lane & 15) * A8_STAGE_PITCH + nf * 32 + 8 * q) =
-                    make_uint2(f32_to_bf16_bits(acc[f][nf][0]) | (f32_to_bf16_bits(acc[f][nf][1]) << 16),
-                               f32_to_bf16_bits(acc[f][nf][2]) | (f32_to_bf16_bits(acc[f][nf][3]) << 16));
+                    make_uint2(pack_bf16x2(acc[f][nf][0], acc[f][nf][1]),
+                               pack_bf16x2(acc[f][nf][2], acc[f][nf][3]));
             __builtin_amdgcn_wave_barrier();
 #pragma unroll
             for (int h = 0; h < 2; h++) {

@@ -273,17 +273,19 @@ __device__ __attribute__((always_inline)) inline void tiled_tile(const GemmArgs 
                 const int r = rbase + f * 16;
                 if (r >= m1)
                     continue;
-                uint32_t hv[4];
+                float hf[4];
 #pragma unroll
                 for (int i = 0; i < 4; i++)
-                    hv[i] = f32_to_bf16_bits(silu_f32(acc[f][2 * p][i]) * acc[f][2 * p + 1][i]);
+                    hf[i] = silu_f32(acc[f][2 * p][i]) * acc[f][2 * p + 1][i];
+                const uint2 hv = make_uint2(pack_bf16x2(hf[0], hf[1]), pack_bf16x2(hf[2], hf[3]));
                 uint16_t *dst = o + (int64_t)r * d.ld + oc;
                 if (vec) {
-                    *reinterpret_cast<uint2 *>(dst) = make_uint2(hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16));
+                    *reinterpret_cast<uint2 *>(dst) = hv;
                 } else {
-#pragma unroll
-                    for (int i = 0; i < 4; i++)
-                        dst[i] = (uint16_t)hv[i];
+                    dst[0] = (uint16_t)hv.x;
+                    dst[1] = (uint16_t)(hv.x >> 16);
+                    dst[2] = (uint16_t)hv.y;
+                    dst[3] = (uint16_t)(hv.y >> 16);
                 }
             }
         }
@@ -319,8 +321,8 @@ __device__ __attribute__((always_inline)) inline void tiled_tile(const GemmArgs 
                     uint16_t *dst = reinterpret_cast<uint16_t *>(d.ptr) + (int64_t)r * d.ld + (n - d.col0);
                     if (full) {
                         *reinterpret_cast<uint2 *>(dst) =
-                            make_uint2(f32_to_bf16_bits(acc[f][nf][0]) | (f32_to_bf16_bits(acc[f][nf][1]) << 16),
-                                       f32_to_bf16_bits(acc[f][nf][2]) | (f32_to_bf16_bits(acc[f][nf][3]) << 16));
+                            make_uint2(pack_bf16x2(acc[f][nf][0], acc[f][nf][1]),
+                                       pack_bf16x2(acc[f][nf][2], acc[f][nf][3]));
                     } else {
 #pragma unroll
                         for (int i = 0; i < 4; i++)
@@ -490,12 +492,12 @@ __global__ __launch_bounds__(WAVE * 8) void ring_kernel(const GemmArgs g, int gx
 #pragma unroll
             for (int f = 0; f < RG_MF; f++) {
                 const int r = rbase + f * 16;
-                uint32_t hv[4];
+                float hf[4];
 #pragma unroll
                 for (int i = 0; i < 4; i++)
-                    hv[i] = f32_to_bf16_bits(silu_f32(acc[f][2 * p][i]) * acc[f][2 * p + 1][i]);
+                    hf[i] = silu_f32(acc[f][2 * p][i]) * acc[f][2 * p + 1][i];
                 *reinterpret_cast<uint2 *>(o + (int64_t)r * d.ld + oc) =
-                    make_uint2(hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16));
+                    make_uint2(pack_bf16x2(hf[0], hf[1]), pack_bf16x2(hf[2], hf[3]));
             }
         }
         return;
@@ -529,8 +531,8 @@ __global__ __launch_bounds__(WAVE * 8) void ring_kernel(const GemmArgs g, int gx
                 uint16_t *dst = reinterpret_cast<uint16_t *>(d.ptr) + (int64_t)r * d.ld + (n - d.col0);
                 if (full) {
                     *reinterpret_cast<uint2 *>(dst) =
-                        make_uint2(f32_to_bf16_bits(acc[f][j][0]) | (f32_to_bf16_bits(acc[f][j][1]) << 16),
-                                   f32_to_bf16_bits(acc[f][j][2]) | (f32_to_bf16_bits(acc[f][j][3]) << 16));
+                        make_uint2(pack_bf16x2(acc[f][j][0], acc[f][j][1]),
+                                   pack_bf16x2(acc[f][j][2], acc[f][j][3]));
                 } else {
 #pragma unroll
                     for (int i = 0; i < 4; i++)
@@ -688,8 +690,8 @@ __device__ __attribute__((always_inline)) inline void astat_item(const GemmArgs 
 #pragma unroll
             for (int nf = 0; nf < AS_NF; nf++)
                 *reinterpret_cast<uint2 *>(stage + (lane & 15) * AS_STAGE_PITCH + nf * 32 + 8 * q) =
-                    make_uint2(f32_to_bf16_bits(acc[f][nf][0]) | (f32_to_bf16_bits(acc[f][nf][1]) << 16),
-                               f32_to_bf16_bits(acc[f][nf][2]) | (f32_to_bf16_bits(acc[f][nf][3]) << 16));
+                    make_uint2(pack_bf16x2(acc[f][nf][0], acc[f][nf][1]),
+                               pack_bf16x2(acc[f][nf][2], acc[f][nf][3]));
             __builtin_amdgcn_wave_barrier();
 #pragma unroll
             for (int h = 0; h < 2; h++) {

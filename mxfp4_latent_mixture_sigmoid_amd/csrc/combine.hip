@@ -20,7 +20,8 @@ hipError_t launch_tilemap(const int32_t *offsets, int E, int bm, int32_t *tiles,
 // zc[t, c] = bf16(sum over slots j = 0..K-1, in order, of w[t, j] * Y[inv[t K + j], c]).
 // Each thread owns 8 consecutive columns of one token (16-byte loads and store); FP32 sums. Slots
 // go in batches of CB: the batch's rows and weights, then all its row loads, are issued before any
-// is used, so a wave keeps CB loads in flight; the sums still run in slot order.
+// is used, so a wave keeps CB loads in flight; the sums still run in slot order. The rows of y are
+// read once, with non-temporal loads (at 8192 tokens, 940 MB: 236 -> 178 us against cached loads).
 constexpr int CB = 8;
 __global__ __launch_bounds__(64) void combine_kernel(const uint16_t *__restrict__ Y, int Lt,
                                                      const int32_t *__restrict__ inv, const float *__restrict__ w,
@@ -52,13 +53,13 @@ __global__ __launch_bounds__(64) void combine_kernel(const uint16_t *__restrict_
         u32x4_t y[CB];
 #pragma unroll
         for (int u = 0; u < CB; u++)
-            y[u] = load16(Y + r[u] * Lt + c8 * 8);
+            y[u] = load16_nt(Y + r[u] * Lt + c8 * 8);
 #pragma unroll
         for (int u = 0; u < CB; u++)
             add(wj[u], y[u]);
     }
     for (; j0 < K; j0++)
-        add(wt[j0], load16(Y + (int64_t)it[j0] * Lt + c8 * 8));
+        add(wt[j0], load16_nt(Y + (int64_t)it[j0] * Lt + c8 * 8));
     u32x4_t o;
 #pragma unroll
     for (int i = 0; i < 4; i++)

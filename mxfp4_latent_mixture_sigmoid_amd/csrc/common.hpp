@@ -137,9 +137,13 @@ __device__ inline __amdgpu_buffer_rsrc_t row_window(void *base, int rows, int ld
 {
     return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, rows * ld * 2, 0x00020000);
 }
+// Cache-policy argument of a non-temporal (streaming) store: outputs written once and read back only
+// after far more data has passed through the caches.
+constexpr int CPOL_NT = 2;
+template <int CPOL = 0>
 __device__ inline void store16_window(u32x4_t v, __amdgpu_buffer_rsrc_t w, int byte_offset)
 {
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4_t, v), w, byte_offset, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4_t, v), w, byte_offset, 0, CPOL);
 }
 
 } // namespace mxmoe

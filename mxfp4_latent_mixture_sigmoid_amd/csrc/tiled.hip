@@ -697,7 +697,7 @@ __device__ __attribute__((always_inline)) inline void astat_item(const GemmArgs 
             for (int h = 0; h < 2; h++) {
                 const int rr = h * 8 + (lane >> 3);
                 const u32x4_t v = *reinterpret_cast<const u32x4_t *>(stage + rr * AS_STAGE_PITCH + (lane & 7) * 16);
-                store16_window(v, win, ((f * 16 + rr) * d.ld + (lane & 7) * 8) * 2);
+                store16_window<CPOL_NT>(v, win, ((f * 16 + rr) * d.ld + (lane & 7) * 8) * 2);
             }
             __builtin_amdgcn_wave_barrier();
         }

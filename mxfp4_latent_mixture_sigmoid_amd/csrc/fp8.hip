@@ -287,12 +287,13 @@ __device__ __attribute__((always_inline)) inline void astat8_item(const Fp8DownA
 
     const uint8_t *Bg = g.B + (int64_t)group * g.b_stride;
     const int nbmax = g.N / 16 - 1;
+    // cached loads: every tile of an expert reads the expert's whole matrix
     auto load_kb = [&](int j, int kb, u32x4_t *codes, uint32_t *sc) {
 #pragma unroll
         for (int nf = 0; nf < A8_NF; nf++) {
             const int nb = min((j * A8_BN + wv * 64) / 16 + nf, nbmax);
             const uint8_t *p = Bg + ((int64_t)nb * KB + kb) * MX_BLOCK_BYTES;
-            codes[nf] = load16_nt(p + lane * 16);
+            codes[nf] = load16(p + lane * 16);
             sc[nf] = p[MX_CODE_BYTES + lane];
         }
     };

@@ -621,14 +621,16 @@ __device__ __attribute__((always_inline)) inline void astat_item(const GemmArgs 
     const uint8_t *Bg = g.B + (int64_t)group * g.b_stride;
     const int nbmax = g.N / 16 - 1;
     // B is prefetched one 128-input block ahead (the next block of this N block, or the first of the
-    // wave's next N block), so a wave holds two blocks of B at a time.
+    // wave's next N block), so a wave holds two blocks of B at a time. These are cached loads: every
+    // tile of an expert reads the expert's whole matrix, and a popular expert has dozens of tiles
+    // (8192 tokens: 408 -> 391 us against non-temporal loads).
     auto load_kb = [&](int j, int kb, u32x4_t *codes, uint32_t *sc) {
 #pragma unroll
         for (int nf = 0; nf < AS_NF; nf++) {
             const int nb = min((j * AS_BN + wn * TL_WAVE_N) / 16 + nf, nbmax);
             const uint8_t *p = Bg + ((int64_t)nb * KB + kb) * MX_BLOCK_BYTES;
-            codes[nf] = load16_nt(p + lane * 16);
-            sc[nf] = load4_nt(p + MX_CODE_BYTES + 4 * (lane & 15));
+            codes[nf] = load16(p + lane * 16);
+            sc[nf] = *reinterpret_cast<const uint32_t *>(p + MX_CODE_BYTES + 4 * (lane & 15));
         }
     };
     u32x4_t bc[AS_NF];

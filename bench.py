@@ -32,9 +32,18 @@ MX_BYTES_PER_VALUE = 17 / 32    # E2M1 nibble + one E8M0 byte per 32 values
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
+# Headers every kernel source includes: a change there changes the compiled kernel too.
+SHARED_HEADERS = ("common.hpp", "kernels.hpp", "wave.hpp", "partials.hpp")
+
+
 def source_hash(rel: str) -> str:
-    with open(os.path.join(ROOT, rel), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of a kernel source file together with the shared headers beside it."""
+    h = hashlib.sha256()
+    path = os.path.join(ROOT, rel)
+    for p in [path] + [os.path.join(os.path.dirname(path), n) for n in SHARED_HEADERS]:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def algorithmic(shape, n_active: int) -> dict:

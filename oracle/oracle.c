@@ -435,6 +435,100 @@ void or_expert_down_fp8(const uint8_t *hq, const uint8_t *hs, int64_t T, int64_t
     }
 }
 
+/* ------------------------------------------------- MXFP4 first stage (opt-in mode, A4W4) -------
+ * [K31-opt] ("Kimi K3.1 Pro on AMD Instinct GPUs", section "What we optimized", and its appendix of
+ * environment variables) names an A4W4 mode of the grouped MoE: activations in 4-bit MX as well as
+ * the weights. The pages fix neither the activation format's scale rule nor its rounding; reading
+ * A1, the same conversion rule as F1 with the E2M1 element:
+ *  A1  z is quantised per token row in blocks of 32 consecutive values along Lt (the first stage's
+ *      input axis, the same blocks as the gate/up weights' scales) to OCP MX FP4: E2M1 elements
+ *      with one E8M0 block scale 2^X, X = floor(log2(max |z| over the block)) - 2 (2 = exponent of
+ *      E2M1's largest normal, 6 = 1.5 . 2^2), clamped to [-127, 127]; an all-zero block takes
+ *      X = -127. Each element z / 2^X is rounded to nearest even at E2M1's precision (2 significant
+ *      bits, subnormal quantum 1/2) and saturates at +-6; its sign bit is kept (also for zero).
+ *      Codes are packed as the weights are: element 2i in the low nibble of byte i.
+ *  A2  The gate/up product then reads the dequantised values: g = sum_k q_k 2^X_k . Wg[j][k] (and
+ *      u likewise), h = bf16(silu(g) u); everything after h is unchanged.
+ */
+
+/* E2M1 code of |a| (a >= 0, finite) rounded to nearest even, saturating at 6; sign added by caller. */
+static int e2m1_round(double a)
+{
+    if (a == 0.0)
+        return 0;
+    int ex;
+    frexp(a, &ex);                       /* leading bit of a at 2^(ex-1) */
+    int q = ex - 1 - 1;                  /* quantum for 2 significant bits */
+    if (q < -1)
+        q = -1;                          /* subnormal range: quantum 1/2 */
+    double r = ldexp(nearbyint(ldexp(a, -q)), q);
+    if (r > 6.0)
+        r = 6.0;
+    for (int c = 0; c <= 7; c++)         /* codes 0..7 are monotone in magnitude */
+        if (or_e2m1(c) == r)
+            return c;
+    return -1;                           /* unreachable: r is an E2M1 value */
+}
+
+/* O11a. MX FP4 quantisation of z [R, L] bf16 (L a multiple of 32) per A1: codes u8 [R, L/2] (two
+ * per byte, element 2i low) and scale bytes u8 [R, L/32]. */
+void or_fp4_quant(const uint16_t *z, int64_t R, int64_t L, uint8_t *codes, uint8_t *scales)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < R; r++)
+        for (int64_t b = 0; b < L / 32; b++) {
+            const uint16_t *v = z + r * L + b * 32;
+            double amax = 0.0;
+            for (int i = 0; i < 32; i++) {
+                double a = fabs(or_bf16_to_double(v[i]));
+                if (a > amax)
+                    amax = a;
+            }
+            int X = -127;
+            if (amax > 0.0) {
+                int ex;
+                frexp(amax, &ex);        /* floor(log2 amax) = ex - 1 */
+                X = ex - 1 - 2;
+                if (X < -127)
+                    X = -127;
+                if (X > 127)
+                    X = 127;
+            }
+            scales[r * (L / 32) + b] = (uint8_t)(X + 127);
+            for (int i = 0; i < 32; i += 2) {
+                int c0 = e2m1_round(ldexp(fabs(or_bf16_to_double(v[i])), -X)) | ((v[i] & 0x8000) ? 8 : 0);
+                int c1 = e2m1_round(ldexp(fabs(or_bf16_to_double(v[i + 1])), -X)) | ((v[i + 1] & 0x8000) ? 8 : 0);
+                codes[r * (L / 2) + (b * 32 + i) / 2] = (uint8_t)(c0 | (c1 << 4));
+            }
+        }
+}
+
+/* O11b. The A4W4 first stage on given quantised z (A2): for every pair p = t*K + j with
+ * e = ids[p], h_p = bf16(silu(g) u), g = zq_t . Wg_e^T, u = zq_t . Wu_e^T, zq the dequantised
+ * MX FP4 row of token t. zc codes [T, Lt/2], scales [T, Lt/32]; h [T*K, I] by pair id. */
+void or_expert_gateup_a4(const uint8_t *zq, const uint8_t *zs, int64_t T, int64_t Lt, const int32_t *ids, int64_t K,
+                         int64_t I, const uint8_t *gate_codes, const uint8_t *gate_scales, const uint8_t *up_codes,
+                         const uint8_t *up_scales, uint16_t *h_out)
+{
+    const int64_t gcb = I * (Lt / 2), gsb = I * (Lt / 32);
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t p = 0; p < T * K; p++) {
+        const int64_t t = p / K, e = ids[p];
+        double *zt = (double *)malloc((size_t)Lt * sizeof(double));
+        for (int64_t k = 0; k < Lt; k++)
+            zt[k] = mx_elem(zq, zs, Lt, t, k);
+        for (int64_t j = 0; j < I; j++) {
+            double g = 0.0, u = 0.0;
+            for (int64_t k = 0; k < Lt; k++) {
+                g += zt[k] * mx_elem(gate_codes + e * gcb, gate_scales + e * gsb, Lt, j, k);
+                u += zt[k] * mx_elem(up_codes + e * gcb, up_scales + e * gsb, Lt, j, k);
+            }
+            h_out[p * I + j] = or_double_to_bf16(g * sigmoid(g) * u);
+        }
+        free(zt);
+    }
+}
+
 /* O9b. The down half of O9 on given h_s: ys[t] = sum_s h_s[t] . Wd_s^T (FP64, not rounded).
  * hs [T, S*Is] bf16; sd [S,H,Is]; ys [T,H]. */
 void or_shared_down(const uint16_t *hs, int64_t T, int64_t S, int64_t Is, const uint16_t *sd, int64_t H, double *ys)

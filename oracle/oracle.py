@@ -61,6 +61,8 @@ def lib():
             "or_e4m3": (ctypes.c_double, [ctypes.c_int]),
             "or_fp8_quant": (None, [P, I64, I64, P, P]),
             "or_expert_down_fp8": (None, [P, P, I64, I64, I64, I64, P, P, P, P]),
+            "or_fp4_quant": (None, [P, I64, I64, P, P]),
+            "or_expert_gateup_a4": (None, [P, P, I64, I64, P, I64, I64, P, P, P, P, P]),
             "or_num_threads": (ctypes.c_int, []),
             "or_expert_down": (None, [P, I64, I64, I64, I64, P, P, P, P]),
             "or_shared_down": (None, [P, I64, I64, I64, P, I64, P]),
@@ -265,6 +267,31 @@ def expert_down_fp8(hq, hs, ids, down_codes, down_scales) -> np.ndarray:
     return y
 
 
+def fp4_quant(z) -> tuple[np.ndarray, np.ndarray]:
+    """MX FP4 quantisation of BF16 rows [R, L]: (E2M1 codes packed two per byte [R, L/2],
+    E8M0 scale bytes [R, L/32]) -- the A4W4 first stage's activations (oracle.c, O11)."""
+    z = _c(z, np.uint16)
+    R, L = z.shape
+    codes = np.empty((R, L // 2), np.uint8)
+    scales = np.empty((R, L // 32), np.uint8)
+    lib().or_fp4_quant(_p(z), R, L, _p(codes), _p(scales))
+    return codes, scales
+
+
+def expert_gateup_a4(zq, zs, ids, gate_codes, gate_scales, up_codes, up_scales) -> np.ndarray:
+    """h by pair id from MX FP4 z (token order) -- the A4W4 first stage."""
+    zq = _c(zq, np.uint8)
+    zs = _c(zs, np.uint8)
+    ids = _c(ids, np.int32)
+    T, K = ids.shape
+    Lt = zq.shape[1] * 2
+    I = gate_codes.shape[1]
+    arrs = [_c(a, np.uint8) for a in (gate_codes, gate_scales, up_codes, up_scales)]
+    h = np.empty((T * K, I), np.uint16)
+    lib().or_expert_gateup_a4(_p(zq), _p(zs), T, Lt, _p(ids), K, I, *[_p(a) for a in arrs], _p(h))
+    return h
+
+
 def shared_down(hs, sh_down) -> np.ndarray:
     """sum over shared experts of h_s . Wd_s^T (FP64) from given h_s -- the down half of `shared`."""
     hs = _c(hs, np.uint16)
@@ -289,15 +316,16 @@ def combine(y, w) -> np.ndarray:
 # ------------------------------------------------------------------ whole layer
 
 def forward(inp: dict, K: int, logits_in=None, ids_in=None, want_intermediates=True,
-            stage2_fp8: bool = False) -> dict:
+            stage2_fp8: bool = False, stage1_a4: bool = False) -> dict:
     """Whole routed-expert forward on the tokens of ``inp["x"]``.
 
     ``logits_in`` replaces the router product (as the library's logits input does);
     ``ids_in`` forces the expert selection (the floating-point parity protocol uses the
     selection that was already checked bit-exactly, so a near-tie cannot mask a numeric
-    comparison). ``stage2_fp8`` runs the down product on MX FP8 h (oracle.c, O10).
-    Returns logits, ids, w, perm, z, h, hq / hs8 (FP8 codes and scales, or None), y (pair
-    order), zc, hs, ys, out.
+    comparison). ``stage2_fp8`` runs the down product on MX FP8 h (oracle.c, O10);
+    ``stage1_a4`` runs the gate/up product on MX FP4 z (oracle.c, O11).
+    Returns logits, ids, w, perm, z, zq / zs4 (FP4 codes and scales, or None), h, hq / hs8
+    (FP8 codes and scales, or None), y (pair order), zc, hs, ys, out.
     """
     x = inp["x"]
     has_latent = "w_down" in inp
@@ -311,6 +339,12 @@ def forward(inp: dict, K: int, logits_in=None, ids_in=None, want_intermediates=T
     h, y = experts(z, ids, inp["gate_codes"], inp["gate_scales"], inp["up_codes"],
                    inp["up_scales"], inp["down_codes"], inp["down_scales"],
                    want_h=want_intermediates or stage2_fp8)
+    zq = zs4 = None
+    if stage1_a4:    # first stage on MX FP4 z instead of BF16 z
+        zq, zs4 = fp4_quant(z)
+        h = expert_gateup_a4(zq, zs4, ids, inp["gate_codes"], inp["gate_scales"], inp["up_codes"],
+                             inp["up_scales"])
+        y = expert_down(h, ids, inp["down_codes"], inp["down_scales"])
     hq = hs8 = None
     if stage2_fp8:   # second stage on MX FP8 h instead of BF16 h
         hq, hs8 = fp8_quant(h)
@@ -323,5 +357,5 @@ def forward(inp: dict, K: int, logits_in=None, ids_in=None, want_intermediates=T
         out = output(zc, inp["w_up"], ys)
     else:
         out = zc
-    return dict(logits=lg, ids=ids, w=w, perm=perm, z=z, h=h, hq=hq, hs8=hs8, y=y, zc=zc, hs=hs, ys=ys,
-                out=out)
+    return dict(logits=lg, ids=ids, w=w, perm=perm, z=z, zq=zq, zs4=zs4, h=h, hq=hq, hs8=hs8, y=y, zc=zc,
+                hs=hs, ys=ys, out=out)

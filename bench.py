@@ -28,6 +28,7 @@ METRIC = "routed-MoE tokens/s per MI355X; HBM GB/s (decode), MFMA TFLOPS (prefil
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0       # MI355X dense BF16 matrix cores
 FP8_PEAK_TFLOPS = 5000.0        # MI355X dense FP8 matrix cores (the FP8 x FP4 down product's rate)
+FP4_PEAK_TFLOPS = 10100.0       # MI355X dense MXFP4 matrix cores (the A4W4 gate/up product's rate)
 MX_BYTES_PER_VALUE = 17 / 32    # E2M1 nibble + one E8M0 byte per 32 values
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
@@ -106,6 +107,9 @@ def main() -> int:
     ap.add_argument("--stage2", choices=("bf16", "fp8"), default="bf16",
                     help="arithmetic of the experts' down product: BF16 h (the layer as defined), or h "
                          "quantised to MX FP8 on the scaled FP8 x FP4 matrix-core instruction")
+    ap.add_argument("--stage1", choices=("bf16", "mxfp4"), default="bf16",
+                    help="arithmetic of the experts' gate/up product: BF16 z (the layer as defined), or z "
+                         "quantised to MX FP4 on the scaled FP4 x FP4 matrix-core instruction (A4W4)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -140,8 +144,9 @@ def main() -> int:
 
     weights = {k: dev(v) for k, v in inp.items() if k in abi.WEIGHT_FIELDS and v is not None}
     fp8 = args.stage2 == "fp8"
+    a4 = args.stage1 == "mxfp4"
     layer = MoELayer(shape.H, shape.Lt, shape.E, shape.K, shape.I, shape.S, shape.Is, shape.has_latent,
-                     weights, T_max=T, stage2_fp8=fp8)
+                     weights, T_max=T, stage2_fp8=fp8, stage1_a4=a4)
     torch.cuda.synchronize()
     del weights
     x = dev(inp["x"])
@@ -202,15 +207,19 @@ def main() -> int:
     decode = T * shape.K <= 4 * shape.E    # few tokens per expert: weight streaming bound
     gateup_s = kernels_us["gateup"] * 1e-6
     if decode:
-        achieved = alg["gateup_bytes"] / gateup_s / 1e9
+        gb = alg["gateup_bytes"]
+        if a4:   # the gate/up product reads MX FP4 z (17/32 bytes per value) instead of BF16 z
+            gb += T * shape.Lt * (MX_BYTES_PER_VALUE - 2)
+        achieved = gb / gateup_s / 1e9
         roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBPS, unit="GB/s",
                     frac=round(achieved / HBM_PEAK_GBPS, 4))
-    else:
+    else:   # a contraction against the peak of its own operand type
+        peak = FP4_PEAK_TFLOPS if a4 else BF16_PEAK_TFLOPS
         achieved = alg["gateup_flops"] / gateup_s / 1e12
-        roof = dict(bound="mfma", achieved=round(achieved, 2), peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
-                    frac=round(achieved / BF16_PEAK_TFLOPS, 4))
+        roof = dict(bound="mfma", achieved=round(achieved, 2), peak=peak, unit="TFLOP/s",
+                    frac=round(achieved / peak, 4))
     roof["kernel"] = "gateup"
-    roof["traffic"] = read_traffic(shape.name, "gateup")
+    roof["traffic"] = None if a4 else read_traffic(shape.name, "gateup")
     down_roof = None
     if fp8:   # the FP8 x FP4 down product against its own roof
         down_s = kernels_us["down"] * 1e-6
@@ -232,7 +241,7 @@ def main() -> int:
         sub = dict(inp, x=inp["x"][tok])
         print(f"[bench] CPU oracle on {len(tok)} tokens", file=sys.stderr, flush=True)
         c0 = time.perf_counter()
-        O.forward(sub, shape.K, want_intermediates=False, stage2_fp8=fp8)
+        O.forward(sub, shape.K, want_intermediates=False, stage2_fp8=fp8, stage1_a4=a4)
         csec = time.perf_counter() - c0
         cpu = dict(value=round(len(tok) / csec, 3), unit="tokens/s", cores=O.num_threads(), kind="oracle",
                    sample=f"{len(tok)} seeded tokens of {shape.name}, full forward in FP64 ({csec:.1f} s)")
@@ -249,12 +258,12 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16+fp8" if fp8 else "bf16",
+        "dtype": "+".join(["bf16"] + (["mxfp4"] if a4 else []) + (["fp8"] if fp8 else [])),
         "data": "synthetic",
         "config": {"workload": shape.name, "tokens": T, "hidden": shape.H, "latent": shape.Lt,
                    "experts": shape.E, "top_k": shape.K, "inter": shape.I, "shared_experts": shape.S,
                    "shared_inter": shape.Is, "routing": shape.routing, "active_experts": n_active,
-                   "stage2": args.stage2},
+                   "stage1": args.stage1, "stage2": args.stage2},
         "roofline": roof,
         "cpu_baseline": cpu,
         "gpu_ms_per_step": round(gpu_ms / args.steps, 5),

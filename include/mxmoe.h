@@ -65,6 +65,20 @@ typedef enum { MOE_ACT_SILU_GLU = 0 } moe_act;
  *   matrix-core instruction. */
 typedef enum { MOE_STAGE2_BF16 = 0, MOE_STAGE2_FP8 = 1 } moe_stage2;
 
+/* Arithmetic of the routed experts' first stage (the gate|up product with the GLU).
+ * MOE_STAGE1_BF16:  the product reads z in BF16 (the layer as defined above).
+ * MOE_STAGE1_MXFP4: z is first quantised to MX FP4 and the product reads the quantised values, as
+ *   the reference engine's A4W4 mode does (page "Kimi K3.1 Pro on AMD Instinct GPUs", section "What
+ *   we optimized" and its appendix of environment variables). The pages fix neither the scale rule
+ *   nor the rounding; this build takes the OCP MX reading: per token row, blocks of 32 consecutive
+ *   z values along Lt share one E8M0 scale 2^X with X = floor(log2(max |z| in the block)) - 2
+ *   (clamped to [-127, 127]; -127 for an all-zero block), and each element z / 2^X is rounded to
+ *   nearest even to an E2M1 code (2 significant bits, subnormal quantum 1/2) that saturates at +-6
+ *   and keeps the sign of z; codes are packed two per byte, the even element in the low nibble.
+ *   h = bf16(silu(g) * u) from those values; everything after h is unchanged. The packed buffer then
+ *   also holds the gate|up weights in the layout of gfx950's scaled MX matrix-core instruction. */
+typedef enum { MOE_STAGE1_BF16 = 0, MOE_STAGE1_MXFP4 = 1 } moe_stage1;
+
 typedef struct {
     int32_t hidden;          /* H: width of x and out (multiple of 128); unused without latent  */
     int32_t latent;          /* Lt: latent width (multiple of 128)                               */
@@ -76,6 +90,7 @@ typedef struct {
     int32_t has_latent_proj; /* 1: x is the hidden state (down/up projections, shared experts)   */
     int32_t act;             /* moe_act                                                          */
     int32_t stage2;          /* moe_stage2                                                       */
+    int32_t stage1;          /* moe_stage1                                                       */
 } moe_config;
 
 /* Canonical weights (device, caller-owned; only read by moe_create's packing kernels, so they
@@ -121,7 +136,9 @@ moe_status moe_query(const moe_config *cfg, int32_t T_max, size_t *packed_bytes,
  * per-block expert histogram, the expert tile list, z [T,Lt], [zc | h_s] [T, Lt + S Is],
  * h [T K, I] and y [T K, Lt] (expert-sorted rows, BF16), the MX FP8 h of MOE_STAGE2_FP8 (E4M3
  * codes [T K, I], then from byte offset T K I the E8M0 scales [T K, I/32]; empty otherwise),
- * FP32 split-K partials, then the total size. `offsets` is a host array of 10 entries.
+ * the MX FP4 z of MOE_STAGE1_MXFP4 (E2M1 codes [T, Lt/2], then from byte offset T Lt/2 the E8M0
+ * scales [T, Lt/32]; empty otherwise), FP32 split-K partials, then the total size. `offsets` is a
+ * host array of 11 entries.
  * Host-only. */
 moe_status moe_query_workspace_layout(const moe_config *cfg, int32_t T, size_t *offsets);
 
@@ -178,7 +195,8 @@ typedef enum {
     MOE_KERNEL_XSIDE_EPI = 9,/* few-token x-side partial sums, GLU and tile lists   */
     MOE_KERNEL_OUT_EPI = 10, /* few-token output partial sums                       */
     MOE_KERNEL_ROUTER_XSIDE = 11,/* router + x-side product as one (moe_route_forward) */
-    MOE_KERNEL_H_QUANT = 12  /* MX FP8 quantisation of h (MOE_STAGE2_FP8)           */
+    MOE_KERNEL_H_QUANT = 12, /* MX FP8 quantisation of h (MOE_STAGE2_FP8)           */
+    MOE_KERNEL_Z_QUANT = 13  /* MX FP4 quantisation of z (MOE_STAGE1_MXFP4)         */
 } moe_kernel;
 
 /* Profiling hook (benchmarks, tests): after moe_profile_begin, every kernel launch of moe_route

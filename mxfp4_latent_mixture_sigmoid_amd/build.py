@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmxmoe.so")
-SOURCES = ["api.cpp", "pack.hip", "gemm.hip", "skinny.hip", "tiled.hip", "route.hip", "combine.hip", "fp8.hip"]
+SOURCES = ["api.cpp", "pack.hip", "gemm.hip", "skinny.hip", "tiled.hip", "route.hip", "combine.hip", "fp8.hip", "fp4.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",

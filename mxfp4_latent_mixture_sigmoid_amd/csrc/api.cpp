@@ -17,7 +17,7 @@ struct moe_handle {
     int E_pad;           // router rows padded to 16
     int E_rx;            // router rows padded to 64 in the combined router + x-side matrix
     uint8_t *packed;
-    int64_t off_router, off_xside, off_rx, off_outside, off_gateup, off_down, off_down8;
+    int64_t off_router, off_xside, off_rx, off_outside, off_gateup, off_down, off_down8, off_gateup4;
     int64_t gateup_stride, down_stride;   // packed bytes per expert
     // profiling hook state
     bool prof = false;
@@ -57,6 +57,8 @@ bool valid_config(const moe_config *c)
         return false;
     if (c->stage2 != MOE_STAGE2_BF16 && c->stage2 != MOE_STAGE2_FP8)
         return false;
+    if (c->stage1 != MOE_STAGE1_BF16 && c->stage1 != MOE_STAGE1_MXFP4)
+        return false;
     // the FP8 down product keeps a whole 128-row tile of h (inter bytes per row) in LDS
     if (c->stage2 == MOE_STAGE2_FP8 && (c->inter > FP8_DOWN_MAX_K || c->latent % 64))
         return false;
@@ -80,7 +82,7 @@ bool valid_config(const moe_config *c)
 }
 
 struct PackedLayout {
-    int64_t router, xside, rx, outside, gateup, down, down8, total, gateup_stride, down_stride;
+    int64_t router, xside, rx, outside, gateup, down, down8, gateup4, total, gateup_stride, down_stride;
 };
 
 PackedLayout packed_layout(const moe_config *c)
@@ -112,12 +114,16 @@ PackedLayout packed_layout(const moe_config *c)
     L.down8 = off;
     if (c->stage2 == MOE_STAGE2_FP8)
         off = align_up(off + c->n_experts * L.down_stride);
+    // A4W4 first stage: the gate|up weights once more, in the scaled instruction's operand layout
+    L.gateup4 = off;
+    if (c->stage1 == MOE_STAGE1_MXFP4)
+        off = align_up(off + c->n_experts * L.gateup_stride);
     L.total = off;
     return L;
 }
 
 struct WsLayout {
-    int64_t logits, hist, tiles, z, acat, h, y, h8, partials, total;
+    int64_t logits, hist, tiles, z, acat, h, y, h8, z4, partials, total;
     int64_t rpartials;                  // router partials (inside the partials region, before the dense ones)
     int64_t max_tiles;                  // capacity of the expert tile list (shared by both expert products)
 };
@@ -155,6 +161,9 @@ WsLayout ws_layout(const moe_config *c, int64_t T)
     L.h8 = off;   // MX FP8 h: E4M3 codes [T K, I], then E8M0 scales [T K, I / 32]
     if (c->stage2 == MOE_STAGE2_FP8)
         off = align_up(off + T * K * I + T * K * (I / 32));
+    L.z4 = off;   // MX FP4 z: E2M1 codes [T, Lt / 2], then E8M0 scales [T, Lt / 32]
+    if (c->stage1 == MOE_STAGE1_MXFP4)
+        off = align_up(off + T * (Lt / 2) + T * (Lt / 32));
     L.partials = off;
     L.rpartials = off;
     if (T <= SKINNY_MAX_M) {   // split-K partial tiles of the few-token dense products
@@ -258,8 +267,8 @@ moe_status moe_query_workspace_layout(const moe_config *cfg, int32_t T, size_t *
     if (!valid_config(cfg) || T < 0 || !sizes_fit_int32(cfg, T) || !offsets)
         return MOE_ERR_INVALID_ARG;
     const WsLayout W = ws_layout(cfg, T);
-    const int64_t v[10] = {W.logits, W.hist, W.tiles, W.z, W.acat, W.h, W.y, W.h8, W.rpartials, W.total};
-    for (int i = 0; i < 10; i++)
+    const int64_t v[11] = {W.logits, W.hist, W.tiles, W.z, W.acat, W.h, W.y, W.h8, W.z4, W.rpartials, W.total};
+    for (int i = 0; i < 11; i++)
         offsets[i] = (size_t)v[i];
     return MOE_OK;
 }
@@ -305,6 +314,7 @@ moe_status moe_create(const moe_config *cfg, const moe_weights *w, void *packed,
     h->off_gateup = L.gateup;
     h->off_down = L.down;
     h->off_down8 = L.down8;
+    h->off_gateup4 = L.gateup4;
     h->gateup_stride = L.gateup_stride;
     h->down_stride = L.down_stride;
 
@@ -331,6 +341,10 @@ moe_status moe_create(const moe_config *cfg, const moe_weights *w, void *packed,
     if (e == hipSuccess)
         e = launch_pack_down(h->packed + L.down, static_cast<const uint8_t *>(w->down_codes),
                              static_cast<const uint8_t *>(w->down_scales), E, I, Lt, st);
+    if (e == hipSuccess && cfg->stage1 == MOE_STAGE1_MXFP4)
+        e = launch_pack_gateup4(h->packed + L.gateup4, static_cast<const uint8_t *>(w->gate_codes),
+                                static_cast<const uint8_t *>(w->gate_scales), static_cast<const uint8_t *>(w->up_codes),
+                                static_cast<const uint8_t *>(w->up_scales), E, I, Lt, st);
     if (e == hipSuccess && cfg->stage2 == MOE_STAGE2_FP8)
         e = launch_pack_down8(h->packed + L.down8, static_cast<const uint8_t *>(w->down_codes),
                               static_cast<const uint8_t *>(w->down_scales), E, I, Lt, st);
@@ -597,7 +611,13 @@ moe_status experts_impl(moe_handle *h, const void *x, int32_t T, const moe_routi
     uint16_t *Yb = reinterpret_cast<uint16_t *>(ws + W.y);
     int32_t *tl = reinterpret_cast<int32_t *>(ws + W.tiles);
     const bool tiled = tiled_experts(c, T);
-    {   // h = bf16(silu(z Wg_e^T) (z Wu_e^T)) for every pair, rows in expert-sorted order
+    if (c->stage1 == MOE_STAGE1_MXFP4) {   // z -> MX FP4, then h = bf16(silu(g) u) on the scaled instruction
+        const uint16_t *A = lat ? Z : static_cast<const uint16_t *>(x);
+        uint8_t *zq = ws + W.z4, *zs = ws + W.z4 + (int64_t)T * (Lt / 2);
+        MOE_LAUNCH(MOE_KERNEL_Z_QUANT, launch_fp4_quant(A, T, Lt, zq, zs, st));
+        A4GateupArgs g{zq, zs, r->sorted_pairs, K, h->packed + h->off_gateup4, h->gateup_stride, 2 * I, Lt, tl, Hb, I};
+        MOE_LAUNCH(MOE_KERNEL_GATEUP, launch_a4_gateup(g, (int)W.max_tiles, st));
+    } else {   // h = bf16(silu(z Wg_e^T) (z Wu_e^T)) for every pair, rows in expert-sorted order
         GemmArgs g{};
         g.A = lat ? Z : static_cast<const uint16_t *>(x);
         g.lda = Lt;

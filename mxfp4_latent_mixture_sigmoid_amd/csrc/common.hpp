@@ -73,6 +73,13 @@ __device__ inline uint32_t pack_bf16x2(float lo, float hi)
 // float -> BF16 bits, round to nearest even.
 __device__ inline uint32_t f32_to_bf16_bits(float f) { return pack_bf16x2(f, 0.0f) & 0xFFFFu; }
 
+// floor(log2 |v|) of a non-zero BF16 magnitude (bits without the sign).
+__device__ inline int bf16_ilogb(uint32_t mag)
+{
+    const uint32_t eb = mag >> 7, m = mag & 0x7Fu;
+    return eb ? (int)eb - 127 : (31 - __builtin_clz(m)) - 133;
+}
+
 // E8M0 byte -> the float 2^(e-127) used as the conversion scale (255 -> NaN).
 __device__ inline float e8m0_to_f32(uint32_t e)
 {
@@ -125,6 +132,12 @@ __device__ inline uint32_t load4_nt(const void *p)
 {
     return __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(p));
 }
+
+// s_waitcnt immediates: at most n vector-memory operations outstanding (the other counters free),
+// and no LDS (lgkm) operation outstanding (the others free).
+constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | (((n >> 4) & 3) << 14); }
+constexpr int LGKM_ZERO = 15 | (7 << 4) | (0 << 8) | (3 << 14);
+constexpr int vmcnt_lgkm_imm(int n) { return (n & 15) | (7 << 4) | (0 << 8) | (((n >> 4) & 3) << 14); }
 
 // Stores into a window of `rows` rows of `ld` BF16 values that starts at `base`, through a raw
 // buffer resource: a store whose byte offset lies past the window is dropped by the hardware's

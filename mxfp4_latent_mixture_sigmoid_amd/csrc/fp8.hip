@@ -81,13 +81,6 @@ hipError_t launch_pack_down8(uint8_t *dst, const uint8_t *dc, const uint8_t *ds,
 // h / 2^X is rounded to nearest even at E4M3 precision in integer arithmetic, exactly: a BF16
 // value is S 2^E0 with an integer significand S < 256, so the quotient's bits are S's bits.
 
-// floor(log2 |v|) of a non-zero BF16 magnitude (bits without the sign).
-__device__ inline int bf16_ilogb(uint32_t mag)
-{
-    const uint32_t eb = mag >> 7, m = mag & 0x7Fu;
-    return eb ? (int)eb - 127 : (31 - __builtin_clz(m)) - 133;
-}
-
 // E4M3 code of the BF16 value `b` divided by 2^X: round to nearest even, saturate at 448,
 // keep the sign bit.
 __device__ inline uint32_t e4m3_code(uint32_t b, int X)

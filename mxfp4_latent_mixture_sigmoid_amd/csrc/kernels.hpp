@@ -75,6 +75,26 @@ struct Fp8DownArgs {
 hipError_t launch_fp8_quant(const uint16_t *h, int64_t rows, int64_t I, uint8_t *codes, uint8_t *scales,
                             hipStream_t st);
 hipError_t launch_down_fp8(const Fp8DownArgs &g, bool many_rows, int max_tiles, hipStream_t st);
+// A4W4 first stage: z -> MX FP4 (codes [rows, L/2], scales [rows, L/32]) and the grouped gate|up
+// product with the GLU on the scaled FP4 x FP4 instruction (tile list required, N = 2I a multiple
+// of 256, K a multiple of 128). Output h rows in tile-list (expert-sorted) order.
+struct A4GateupArgs {
+    const uint8_t *zq;          // FP4 codes of the token rows [rows, K/2]
+    const uint8_t *zs;          // E8M0 scales [rows, K/32]
+    const int32_t *a_index;     // row r of a tile reads token row a_index[r] / a_div
+    int a_div;
+    const uint8_t *B;           // A4 weight blocks, b_stride bytes per expert
+    int64_t b_stride;
+    int N, K;                   // 2I, Lt
+    const int32_t *tiles;
+    uint16_t *h;                // [P, ldh] BF16
+    int ldh;
+};
+hipError_t launch_fp4_quant(const uint16_t *z, int64_t rows, int64_t L, uint8_t *codes, uint8_t *scales,
+                            hipStream_t st);
+hipError_t launch_a4_gateup(const A4GateupArgs &g, int max_tiles, hipStream_t st);
+hipError_t launch_pack_gateup4(uint8_t *dst, const uint8_t *gc, const uint8_t *gs, const uint8_t *uc,
+                               const uint8_t *us, int64_t E, int64_t I, int64_t Lt, hipStream_t st);
 hipError_t launch_pack_down8(uint8_t *dst, const uint8_t *dc, const uint8_t *ds, int64_t E, int64_t I, int64_t Lt,
                              hipStream_t st);
 

@@ -24,11 +24,6 @@ constexpr int TL_MF = TL_WAVE_M / 16, TL_NF = TL_WAVE_N / 16;   // 8 x 4 fragmen
 constexpr int TL_STAGE_K = 128;                                 // K per LDS stage
 constexpr int TL_SUB = TL_STAGE_K / 32;                         // 32-wide sub-steps per stage
 
-// s_waitcnt immediates: at most n vector-memory operations outstanding (the other counters free),
-// and no LDS (lgkm) operation outstanding (the others free).
-constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | (((n >> 4) & 3) << 14); }
-constexpr int LGKM_ZERO = 15 | (7 << 4) | (0 << 8) | (3 << 14);
-constexpr int vmcnt_lgkm_imm(int n) { return (n & 15) | (7 << 4) | (0 << 8) | (((n >> 4) & 3) << 14); }
 
 constexpr int TL_XCDS = 8;      // workgroups are dealt to the XCDs round-robin by linear id
 constexpr int TL_GROUP_M = 8;   // dense products: M tiles per group, walked M-fastest

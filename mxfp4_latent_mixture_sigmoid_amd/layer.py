@@ -17,9 +17,9 @@ class MoELayer:
 
     def __init__(self, hidden, latent, n_experts, top_k, inter, n_shared, shared_inter,
                  has_latent_proj, weights: dict, T_max: int, device="cuda", stream=None,
-                 stage2_fp8: bool = False):
+                 stage2_fp8: bool = False, stage1_a4: bool = False):
         self.cfg = abi.make_config(hidden, latent, n_experts, top_k, inter, n_shared, shared_inter,
-                                   has_latent_proj, stage2_fp8)
+                                   has_latent_proj, stage2_fp8, stage1_a4)
         self.E, self.K, self.Lt = n_experts, top_k, latent
         self.H = hidden if has_latent_proj else latent
         self.T_max = T_max

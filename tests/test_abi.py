@@ -112,3 +112,25 @@ def test_unknown_second_stage_is_rejected():
     c = _cfg()
     c.stage2 = 2
     assert abi.lib().moe_query(ctypes.byref(c), 64, None, None) == abi.Status.INVALID_ARG
+
+
+def test_mxfp4_first_stage_sizes():
+    """MOE_STAGE1_MXFP4 adds one A4 copy of the gate|up weights and the MX FP4 z (codes + scales)."""
+    T, E, Lt, I = 64, 896, 3584, 384
+    pb0, wb0 = abi.query(_cfg(), T)
+    pb1, wb1 = abi.query(_cfg(stage1_a4=True), T)
+    mx_gateup = (2 * I // 16) * (Lt // 128) * 1088
+    assert pb1 - pb0 == E * mx_gateup
+    lay0, lay1 = abi.workspace_layout(_cfg(), T), abi.workspace_layout(_cfg(stage1_a4=True), T)
+    assert lay0["partials"] == lay0["z4"] == lay0["h8"]      # both quantised regions empty
+    assert lay1["partials"] - lay1["z4"] == -(-(T * Lt // 2 + T * Lt // 32) // 256) * 256
+    assert wb1 - wb0 == lay1["partials"] - lay1["z4"]
+    # both modes together: two regions side by side
+    lay2 = abi.workspace_layout(_cfg(stage1_a4=True, stage2_fp8=True), T)
+    assert lay2["z4"] > lay2["h8"] and lay2["partials"] > lay2["z4"]
+
+
+def test_unknown_first_stage_is_rejected():
+    c = _cfg()
+    c.stage1 = 2
+    assert abi.lib().moe_query(ctypes.byref(c), 64, None, None) == abi.Status.INVALID_ARG

@@ -220,14 +220,14 @@ __device__ __attribute__((always_inline)) inline void a4_tile(const A4GateupArgs
         for (int nf = 0; nf < A4_NF; nf++)
             acc[f][nf] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
+    // the first B before the first A stage, so that the prologue's full wait covers both
+    u32x4_t bcur[A4_NF];
+    uint32_t scur[A4_NF];
+    load_b(0, bcur, scur);
     issue_a(0, 0);
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-
-    u32x4_t bcur[A4_NF];
-    uint32_t scur[A4_NF];
-    load_b(0, bcur, scur);
     const int q = lane >> 4;
     for (int st = 0; st < kblocks; st++) {
         const int cur = st & 1;
@@ -252,10 +252,14 @@ __device__ __attribute__((always_inline)) inline void a4_tile(const A4GateupArgs
         }
         // This wave's part of the next stage's A is in LDS and its reads of this stage's are done,
         // then the waves meet; the next stage's B prefetch (2 A4_NF loads, issued after the A
-        // loads) stays in flight.
+        // loads) stays in flight through the barrier and is waited for after it, so that no load
+        // is outstanding at the loop head (the compiler does not order direct-to-LDS loads with
+        // register loads in its wait counts, and a B load still pending there made it wait for the
+        // next A stage before the multiplies).
         asm volatile("" ::: "memory");
         __builtin_amdgcn_s_waitcnt(vmcnt_lgkm_imm(2 * A4_NF));
         __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
         asm volatile("" ::: "memory");
     }
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // the last (repeated) A stage has landed before exit

@@ -129,18 +129,6 @@ __device__ __attribute__((always_inline)) inline void tiled_tile(const GemmArgs 
         for (int j = 0; j < TL_NF; j++)
             acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    if constexpr (MX) {
-        issue_a(0, 0);
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-        __builtin_amdgcn_s_barrier();
-        asm volatile("" ::: "memory");
-    } else {
-        u32x4_t av[NMF];
-        load_a(0, av);
-        store_a(0, av);
-        __syncthreads();
-    }
-
     const bool wave_active = n0 < g.N;
     // B of this wave, prefetched ahead of use: MXFP4 one stage (128 inputs) ahead, BF16 one 32-wide
     // step ahead (across stage boundaries). Past-the-end prefetches re-read the last valid block.
@@ -166,10 +154,23 @@ __device__ __attribute__((always_inline)) inline void tiled_tile(const GemmArgs 
     // and the last stage re-stages a clamped valid A stage, so no value crosses a branch.
     u32x4_t bcur[TL_NF];
     uint32_t sccur[TL_NF];
-    if constexpr (MX)
+    if constexpr (MX) {
+        // The first stage's B is loaded before the first A stage, so the prologue's full wait
+        // covers it: the compiler does not order direct-to-LDS loads with register loads in its
+        // wait counts, and a B load still pending at the loop head made it wait for the whole
+        // next A stage (vmcnt(0)) before every stage's multiplies.
         load_mx(0, bcur, sccur);
-    else
+        issue_a(0, 0);
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+    } else {
+        u32x4_t av[NMF];
+        load_a(0, av);
+        store_a(0, av);
+        __syncthreads();
         load_b(0, bcur);
+    }
 
     for (int st = 0; st < nstages; st++) {
         const int cur = st & 1;

@@ -101,12 +101,15 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="tp8_decode_t64")
-    ap.add_argument("--cpu-sample", type=int, default=16, help="tokens the CPU oracle evaluates")
+    ap.add_argument("--cpu-sample", type=int, default=256,
+                    help="tokens the CPU oracle evaluates (seeded sample; the whole batch if it is smaller)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES")
     ap.add_argument("--stage2", choices=("bf16", "fp8"), default="bf16",
                     help="arithmetic of the experts' down product: BF16 h (the layer as defined), or h "
                          "quantised to MX FP8 on the scaled FP8 x FP4 matrix-core instruction")
+    ap.add_argument("--flush-steps", type=int, default=20,
+                    help="steps timed one by one after a 1 GiB scratch write each (cache-cold distribution)")
     ap.add_argument("--stage1", choices=("bf16", "mxfp4"), default="bf16",
                     help="arithmetic of the experts' gate/up product: BF16 z (the layer as defined), or z "
                          "quantised to MX FP4 on the scaled FP4 x FP4 matrix-core instruction (A4W4)")
@@ -179,6 +182,35 @@ def main() -> int:
     gpu_ms = ev0.elapsed_time(ev1)
     ms_per_step = wall * 1e3 / args.steps
     print(f"[bench] timed {args.steps} steps: {ms_per_step:.4f} ms/step", file=sys.stderr, flush=True)
+
+    # Per-step distribution: events between back-to-back steps, then steps timed one by one, each
+    # after a 1 GiB scratch write outside the timed region (nothing of the layer left in the caches).
+    def pct(v):
+        v = sorted(v)
+        q = lambda f: v[min(len(v) - 1, int(round(f * (len(v) - 1))))]   # noqa: E731
+        return {"p10": round(q(0.1), 5), "p50": round(q(0.5), 5), "p90": round(q(0.9), 5), "n": len(v)}
+
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    evs[0].record(stream)
+    for i in range(args.steps):
+        step()
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    step_pct = pct([evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)])
+    flushed_pct = None
+    if args.flush_steps > 0:
+        scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        fl = []
+        for i in range(args.flush_steps):
+            scratch.fill_(i & 0xFF)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            step()
+            b.record(stream)
+            torch.cuda.synchronize()
+            fl.append(a.elapsed_time(b))
+        flushed_pct = pct(fl)
+        del scratch
 
     # The same work as two calls (moe_route, then moe_forward) on the one stream, for reference.
     for _ in range(args.warmup):
@@ -267,6 +299,8 @@ def main() -> int:
         "roofline": roof,
         "cpu_baseline": cpu,
         "gpu_ms_per_step": round(gpu_ms / args.steps, 5),
+        "step_ms_percentiles": step_pct,
+        "step_ms_percentiles_cache_flushed": flushed_pct,
         "ms_per_step_route_then_forward": round(ms_separate, 5),
         "step_hbm_gbps": round(alg["step_bytes"] / step_s / 1e9, 1),
         "step_tflops": round(alg["step_flops"] / step_s / 1e12, 2),

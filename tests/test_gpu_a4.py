@@ -12,6 +12,8 @@ expert tiles (few rows per expert) and 128-row tiles with ragged ends, empty exp
 I = 128, 256 and 384, and the layer without latent projections; one shape runs both quantised
 stages together.
 """
+from dataclasses import replace
+
 import numpy as np
 import pytest
 import torch
@@ -77,6 +79,10 @@ def _rest_from_h(shape, inp, run, h, fp8):
 def _check(name, fp8=False):
     shape, inp, layer = _setup(name, fp8)
     G.log(f"[a4 forward] {name}{' + fp8 second stage' if fp8 else ''}")
+    return _check_run(shape, inp, layer, fp8)
+
+
+def _check_run(shape, inp, layer, fp8):
     run = G.GpuRun(layer, shape, inp)
     G.check_routing_exact(run, shape.E, shape.K, run.logits)
     got = run.rows()
@@ -132,6 +138,17 @@ def test_a4_stage_parity(name):
 
 def test_a4_with_fp8_second_stage():
     _check("prefill_small", fp8=True)
+
+
+@pytest.mark.parametrize("name,T", [("mid", 1), ("mid", 2), ("mid", 17), ("prefill_small", 128),
+                                    ("prefill_small", 131), ("prefill_small", 257)])
+def test_quantised_stages_ragged_token_counts(name, T):
+    """Both quantised stages on a prefix of T tokens: 16-row expert tiles (mid) and, around the
+    128-row tile threshold, ragged last tiles of 1-8 fragments (prefill_small)."""
+    shape, inp, layer = _setup(name, fp8=True)
+    sub = dict(inp, x=inp["x"][:T])
+    G.log(f"[a4+fp8 ragged] {name} T={T}")
+    _check_run(replace(shape, T=T), sub, layer, True)
 
 
 @pytest.mark.parametrize("name", ["tiny", "prefill_small"])

@@ -13,6 +13,10 @@ class MoELayer:
     ``weights`` maps the canonical weight names of ``abi.WEIGHT_FIELDS`` to device tensors
     (BF16 bit patterns as int16/bfloat16, MXFP4 codes/scales as uint8); they are only read while
     the packing kernels run and may be dropped after the first synchronisation.
+
+    ``stage2_fp8`` quantises h to MX FP8 for the down product (MOE_STAGE2_FP8); ``stage1_a4``
+    quantises z to MX FP4 for the gate/up product (MOE_STAGE1_MXFP4, A4W4). Both default to the
+    BF16 layer; each adds one packed copy of the weights it changes.
     """
 
     def __init__(self, hidden, latent, n_experts, top_k, inter, n_shared, shared_inter,

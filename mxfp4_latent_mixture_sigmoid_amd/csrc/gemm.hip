@@ -56,7 +56,6 @@ __global__ __launch_bounds__(WAVE *WK) void gemm_kernel(const GemmArgs g)
 
     const u32x4_t zero4 = {0u, 0u, 0u, 0u};
     {
-#pragma unroll 2
         for (int s = s0; s < s1; s++) {
             u32x4_t codes[NT];
             uint32_t sc[NT];

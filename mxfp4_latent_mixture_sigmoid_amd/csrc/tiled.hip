@@ -20,7 +20,7 @@
 namespace mxmoe {
 
 constexpr int TL_WAVE_M = 128, TL_WAVE_N = 64;
-constexpr int TL_MF = TL_WAVE_M / 16, TL_NF = TL_WAVE_N / 16;   // 8 x 4 fragments per wave
+constexpr int TL_NF = TL_WAVE_N / 16;   // 16-column fragments per wave (and TL_WAVE_M / 16 = 8 row fragments)
 constexpr int TL_STAGE_K = 128;                                 // K per LDS stage
 constexpr int TL_SUB = TL_STAGE_K / 32;                         // 32-wide sub-steps per stage
 
@@ -584,7 +584,7 @@ hipError_t launch_ring(const GemmArgs &g, hipStream_t st)
 // waves of 128 x 64 -- the kernel ran at half the rate; eight waves of 128 x 64 spill.)
 // Work is mapped XCD-major: the eight XCDs each take a contiguous run of the (tile, N-run) items
 // counted on the device, so the tiles of one expert share an L2.
-constexpr int AS_WAVES = 8, AS_WN = 4, AS_BM = 128, AS_BN = AS_WN * TL_WAVE_N, AS_MF = 8, AS_NF = 4, AS_XCDS = 8;
+constexpr int AS_WAVES = 8, AS_WN = 4, AS_BN = AS_WN * TL_WAVE_N, AS_MF = 8, AS_NF = 4, AS_XCDS = 8;
 constexpr int AS_STAGE_PITCH = 144;                     // bytes per staged output row (128 + 16 padding)
 constexpr int AS_STAGE_BYTES = 16 * AS_STAGE_PITCH;      // one 16-row fragment of one wave
 

@@ -152,7 +152,7 @@ moe_status moe_create(const moe_config *cfg, const moe_weights *w, void *packed,
                       size_t packed_bytes, void *stream, moe_handle **out);
 
 /* Routing for T tokens (0 <= T; T = 0 enqueues nothing and leaves `r` untouched).
- * x: bf16 [T, Hin]. logit_bias: fp32 [E] added to the router product, or NULL.
+ * x: bf16 [T, Hin], 16-byte aligned. logit_bias: fp32 [E] added to the router product, or NULL.
  * logits_in: fp32 [T, E] final logits to select on instead of computing them (then x and
  * logit_bias must be NULL). logits_out: fp32 [T, E] receives the computed logits, or NULL.
  * Writes every array of `r`. workspace: >= moe_query(cfg, T).workspace_bytes. */
@@ -162,7 +162,8 @@ moe_status moe_route(moe_handle *h, const void *x, int32_t T, const float *logit
 
 /* Forward for the same T tokens, given the routing moe_route produced for them.
  * x: bf16 [T, Hin]; out: bf16 [T, H] (or [T, Lt] without latent projections), must not alias
- * x. workspace: >= moe_query(cfg, T).workspace_bytes (may be the one given to moe_route). */
+ * x; both 16-byte aligned (MOE_ERR_INVALID_ARG otherwise). workspace: 256-byte aligned, >=
+ * moe_query(cfg, T).workspace_bytes (may be the one given to moe_route). */
 moe_status moe_forward(moe_handle *h, const void *x, int32_t T, const moe_routing *r, void *out,
                        void *workspace, size_t workspace_bytes, void *stream);
 

@@ -33,6 +33,11 @@ def test_full_size_parity(name, n_sample):
     inp = make_inputs(shape)
     layer = G.make_layer(shape, inp, T_max=shape.T)
     run = G.GpuRun(layer, shape, inp)
+    again = G.GpuRun(layer, shape, inp)
+    assert torch.equal(again._out.view(torch.int16), run._out.view(torch.int16)), "second run differs"
+    assert np.array_equal(again.ids, run.ids) and np.array_equal(again.inv, run.inv)
+    del again
+    G.log("  a second run: bit-identical")
     G.check_fused_identical(layer, shape, inp, run)
     G.log("  route_forward: bit-identical to route + forward")
     tokens = None if n_sample is None else sample_tokens(shape, n_sample)

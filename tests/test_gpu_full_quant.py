@@ -48,6 +48,9 @@ def test_full_size_quantised_stages(name, n_sample, fp8):
     inp = make_inputs(shape)
     layer = G.make_layer(shape, inp, T_max=T, stage1_a4=True, stage2_fp8=fp8)
     run = G.GpuRun(layer, shape, inp)
+    again = G.GpuRun(layer, shape, inp)
+    assert torch.equal(again._out.view(torch.int16), run._out.view(torch.int16)), "second run differs"
+    del again
     G.check_routing_exact(run, shape.E, K, run.logits)
     tok = np.arange(T) if n_sample is None else sample_tokens(shape, n_sample)
     got = run.rows(tok)

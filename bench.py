@@ -304,6 +304,13 @@ def main() -> int:
         "ms_per_step_route_then_forward": round(ms_separate, 5),
         "step_hbm_gbps": round(alg["step_bytes"] / step_s / 1e9, 1),
         "step_tflops": round(alg["step_flops"] / step_s / 1e12, 2),
+        # the whole step against the roof of its regime (HBM for decode, dense BF16 for prefill)
+        "step_roofline": (dict(bound="hbm", achieved=round(alg["step_bytes"] / step_s / 1e9, 1),
+                               peak=HBM_PEAK_GBPS, unit="GB/s",
+                               frac=round(alg["step_bytes"] / step_s / 1e9 / HBM_PEAK_GBPS, 4)) if decode else
+                          dict(bound="mfma", achieved=round(alg["step_flops"] / step_s / 1e12, 2),
+                               peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
+                               frac=round(alg["step_flops"] / step_s / 1e12 / BF16_PEAK_TFLOPS, 4))),
         "kernels_us": kernels_us,
     }
     if down_roof:

@@ -369,27 +369,36 @@ static hipError_t launch_tiled_t(const GemmArgs &g, int grid_m, hipStream_t st)
     return hipGetLastError();
 }
 
-// ---- Ring product: dense BF16 C = A . B^T for many rows (M, N >= 256) with both operands staged
-// through LDS. The workgroup computes 256 x 256 outputs. K advances in 32-input stages; RG_NBUF
-// stages are resident in LDS, each 32 KiB: 16 operand-order 1 KiB blocks of A (16 rows each) and 16
-// of B (the packed fragment blocks). Both are moved by direct global->LDS loads -- one wave instruction fills one
-// 1 KiB block, no register round trip -- issued RG_NBUF - 1 stages ahead; a wave waits for its own
-// loads of the next stage (vmcnt) and a barrier makes every wave's loads visible. K must be a
-// multiple of 32; N and the output region boundaries must be multiples of 64 columns.
-constexpr int RG_BM = 256, RG_BN = 256, RG_WM = 128;
-constexpr int RG_MF = RG_WM / 16;                          // 8 row fragments per wave
-constexpr int RG_AF = RG_BM / 16, RG_BF = RG_BN / 16;      // 16 + 16 blocks per stage
+// ---- Ring product: dense BF16 C = A . B^T for many rows (M >= 256) with both operands staged
+// through LDS. K advances in 32-input stages; RG_NBUF stages are resident in LDS, each holding the
+// operand-order 1 KiB blocks of A (16 rows each) and of B (the packed fragment blocks). Both are
+// moved by direct global->LDS loads -- one wave instruction fills one 1 KiB block, no register round
+// trip -- issued RG_NBUF - 1 stages ahead; a wave waits for its own loads of the next stage (vmcnt)
+// and a barrier makes every wave's loads visible. K must be a multiple of 32.
+// Two tile shapes, both eight waves at two per SIMD:
+//  * 256 x 256 (2 x 4 waves of 128 x 64): every product; N and the output region boundaries must
+//    be multiples of 64 columns so that a wave's columns lie in one region;
+//  * 256 x 224 (4 x 2 waves of 64 x 112): single-region, non-GLU outputs, chosen when it fills the
+//    last round of workgroups better -- e.g. 8192 x 7168 outputs are 896 tiles of 256 x 256 (3.5
+//    rounds of 256 CUs, the last one half idle) but 1024 tiles of 256 x 224 (four full rounds, each
+//    tile 7/8 of the work).
+constexpr int RG_BM = 256, RG_BN = 256;
 constexpr int RG_NBUF = 4;
+constexpr int RG_WAVES = 8;
 
-
-// Eight waves, 2 x 4, each 128 x 64 outputs (128 accumulators): two waves per SIMD, which cover
-// each other's waits (measured 1.07 PFLOP/s against 0.82 for four waves of 128 x 128 at one wave per
+// NWM x (8 / NWM) waves, each WMF x WNF fragments of 16 x 16 outputs (measured for the square tile:
+// eight waves of 128 x 64 at 1.07 PFLOP/s against 0.82 for four waves of 128 x 128 at one wave per
 // SIMD with the next stage's fragments read during the MFMAs).
-__global__ __launch_bounds__(WAVE * 8) void ring_kernel(const GemmArgs g, int gx, int gy)
+template <int NWM, int WMF, int WNF>
+__global__ __launch_bounds__(WAVE *RG_WAVES) void ring_kernel(const GemmArgs g, int gx, int gy)
 {
-    constexpr int NWN = 4, NW = 2 * NWN, RG_WN = RG_BN / NWN, RG_NF = RG_WN / 16;
-    constexpr int RG_LOADS = (RG_AF + RG_BF) / NW;        // loads per wave per stage
-    __shared__ u32x4_t lds[RG_NBUF][RG_AF + RG_BF][WAVE];
+    constexpr int NW = RG_WAVES, NWN = NW / NWM;
+    constexpr int BM = NWM * WMF * 16, BN = NWN * WNF * 16;
+    constexpr int AF = BM / 16, BF = BN / 16;            // A and B blocks per stage
+    constexpr int LOADS = (AF + BF + NW - 1) / NW;       // loads per wave per stage
+    constexpr int AW = AF / LOADS;                       // the first AW waves load A, the rest B
+    static_assert(AF % LOADS == 0 && BF <= (NW - AW) * LOADS, "stage blocks must split over the waves");
+    __shared__ u32x4_t lds[RG_NBUF][AF + BF][WAVE];
     const int lane = threadIdx.x & (WAVE - 1);
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE);
     const int wm = wv / NWN, wn = wv % NWN;
@@ -398,17 +407,19 @@ __global__ __launch_bounds__(WAVE * 8) void ring_kernel(const GemmArgs g, int gx
         return;
     // The last tile of each axis is shifted back to end at M (N): it overlaps its neighbour and
     // recomputes identical values in the same order, so no load or store leaves the matrices.
-    const int m0 = min(by * RG_BM, g.M - RG_BM), n0 = min(bx * RG_BN, g.N - RG_BN);
+    const int m0 = min(by * BM, g.M - BM), n0 = min(bx * BN, g.N - BN);
     const int nst = g.K / BF16_STEP;
 
-    // This wave's loads: blocks wv*L .. wv*L+L-1 of a stage (the first half of the waves load A, the
-    // rest B). Within a stage they are one base plus a fixed stride: 16 rows of A, or one row-block
-    // stride of B's current 16-step chunk.
-    const bool loads_a = wv < NW / 2;
-    const int li = loads_a ? wv : wv - NW / 2;
+    // This wave's loads: blocks wv*LOADS .. wv*LOADS+LOADS-1 of a stage. Within a stage they are one
+    // base plus a fixed stride: 16 rows of A, or one row-block stride of B's current 16-step chunk.
+    // When the B blocks do not fill the last wave, its spare loads repeat the last block (the same
+    // bytes into the same slot), so that every wave issues the same number of loads.
+    const bool loads_a = wv < AW;
+    const int li = loads_a ? wv : wv - AW;
+    const int bfirst = li * LOADS;                       // first B block of a B wave
     const uint8_t *a_base = reinterpret_cast<const uint8_t *>(
-        g.A + (int64_t)(m0 + li * (RG_LOADS * 16) + (lane & 15)) * g.lda + 8 * (lane >> 4));
-    const int bnb0 = n0 / 16 + li * RG_LOADS;
+        g.A + (int64_t)(m0 + li * (LOADS * 16) + (lane & 15)) * g.lda + 8 * (lane >> 4));
+    const int bnb0 = n0 / 16 + bfirst;
     auto issue = [&](int s) {                // stage min(s, nst - 1) into buffer s % RG_NBUF
         const int ss = min(s, nst - 1), buf = s % RG_NBUF;
         const uint8_t *base;
@@ -422,41 +433,43 @@ __global__ __launch_bounds__(WAVE * 8) void ring_kernel(const GemmArgs g, int gx
             stride = (rest < BF16_CHUNK_STEPS ? rest : BF16_CHUNK_STEPS) * BF16_BLOCK_BYTES;
         }
 #pragma unroll
-        for (int i = 0; i < RG_LOADS; i++)
-            __builtin_amdgcn_global_load_lds(base + i * stride,
-                                             (__attribute__((address_space(3))) void *)&lds[buf][wv * RG_LOADS + i][0],
+        for (int i = 0; i < LOADS; i++) {
+            const int bi = loads_a ? i : min(i, BF - 1 - bfirst);
+            __builtin_amdgcn_global_load_lds(base + bi * stride,
+                                             (__attribute__((address_space(3))) void *)&lds[buf][wv * LOADS + bi][0],
                                              16, 0, 0);
+        }
     };
 
-    f32x4_t acc[RG_MF][RG_NF];
+    f32x4_t acc[WMF][WNF];
 #pragma unroll
-    for (int f = 0; f < RG_MF; f++)
+    for (int f = 0; f < WMF; f++)
 #pragma unroll
-        for (int j = 0; j < RG_NF; j++)
+        for (int j = 0; j < WNF; j++)
             acc[f][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
     auto read_frags = [&](int s, u32x4_t *bf, u32x4_t *af) {
         const int buf = s % RG_NBUF;
 #pragma unroll
-        for (int j = 0; j < RG_NF; j++)
-            bf[j] = lds[buf][RG_AF + wn * RG_NF + j][lane];
+        for (int j = 0; j < WNF; j++)
+            bf[j] = lds[buf][AF + wn * WNF + j][lane];
 #pragma unroll
-        for (int f = 0; f < RG_MF; f++)
-            af[f] = lds[buf][wm * RG_MF + f][lane];
+        for (int f = 0; f < WMF; f++)
+            af[f] = lds[buf][wm * WMF + f][lane];
     };
     // Wait until only the later stages' loads of this wave are outstanding, then a barrier makes every
     // wave's loads of this stage visible (and all waves are past the previous stage).
     auto sync_stages = [&]() {
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm((RG_NBUF - 2) * RG_LOADS));
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm((RG_NBUF - 2) * LOADS));
         asm volatile("" ::: "memory");
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
     };
     auto mma = [&](const u32x4_t *bc, const u32x4_t *ac) {
 #pragma unroll
-        for (int j = 0; j < RG_NF; j++)
+        for (int j = 0; j < WNF; j++)
 #pragma unroll
-            for (int f = 0; f < RG_MF; f++)
+            for (int f = 0; f < WMF; f++)
                 acc[f][j] = mfma16(as_bf16x8(bc[j]), as_bf16x8(ac[f]), acc[f][j]);
     };
 #pragma unroll
@@ -465,28 +478,28 @@ __global__ __launch_bounds__(WAVE * 8) void ring_kernel(const GemmArgs g, int gx
     for (int s = 0; s < nst; s++) {
         sync_stages();                        // stage s landed for every wave; buffer s - 1 free
         issue(s + RG_NBUF - 1);
-        u32x4_t bc[RG_NF], ac[RG_MF];
+        u32x4_t bc[WNF], ac[WMF];
         read_frags(s, bc, ac);
         mma(bc, ac);
     }
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // no load may land in LDS after the workgroup ends
 
     // Epilogue: lane (q, c) of fragment (f, j) holds row 16 f + c and columns 16 j + 4 q .. +3.
-    const int n0w = n0 + wn * RG_WN;
+    const int n0w = n0 + wn * (WNF * 16);
     if (n0w >= g.N)
         return;
     const OutDesc d = out_region(g, n0w);
     const int q = lane >> 4;
-    const int rbase = m0 + wm * RG_WM + (lane & 15);
+    const int rbase = m0 + wm * (WMF * 16) + (lane & 15);
     if (d.kind == OUT_GLU) {
         uint16_t *o = reinterpret_cast<uint16_t *>(d.ptr);
 #pragma unroll
-        for (int p = 0; p < RG_NF / 2; p++) {
+        for (int p = 0; p < WNF / 2; p++) {
             if (n0w + 32 * p + 32 > g.N)
                 break;
             const int oc = (n0w - d.col0) / 2 + p * 16 + 4 * q;
 #pragma unroll
-            for (int f = 0; f < RG_MF; f++) {
+            for (int f = 0; f < WMF; f++) {
                 const int r = rbase + f * 16;
                 float hf[4];
 #pragma unroll
@@ -499,7 +512,7 @@ __global__ __launch_bounds__(WAVE * 8) void ring_kernel(const GemmArgs g, int gx
         return;
     }
 #pragma unroll
-    for (int j = 0; j < RG_NF; j++) {
+    for (int j = 0; j < WNF; j++) {
         const int n = n0w + j * 16 + 4 * q;
         if (n >= d.n_valid)
             continue;
@@ -510,7 +523,7 @@ __global__ __launch_bounds__(WAVE * 8) void ring_kernel(const GemmArgs g, int gx
             for (int i = 0; i < 4; i++)
                 bias[i] = (n + i < d.n_valid) ? d.bias[n + i] : 0.f;
 #pragma unroll
-        for (int f = 0; f < RG_MF; f++) {
+        for (int f = 0; f < WMF; f++) {
             const int r = rbase + f * 16;
             if (d.kind == OUT_F32) {
                 float *dst = reinterpret_cast<float *>(d.ptr) + (int64_t)r * d.ld + (n - d.col0);
@@ -540,6 +553,8 @@ __global__ __launch_bounds__(WAVE * 8) void ring_kernel(const GemmArgs g, int gx
     }
 }
 
+constexpr int RG_NARROW_BN = 224;
+
 bool ring_supported(const GemmArgs &g)
 {
     auto out_ok = [](const OutDesc &d) {
@@ -560,15 +575,40 @@ bool ring_preferred(const GemmArgs &g)
     return ring_supported(g) && (int64_t)((g.M + RG_BM - 1) / RG_BM) * ((g.N + RG_BN - 1) / RG_BN) >= 256;
 }
 
+// The narrow tile serves one output region that is not a GLU; it is taken when whole rounds of
+// workgroups times the tile's work come out below the square tile's (ties keep the square tile).
+static bool ring_narrow(const GemmArgs &g, int cus)
+{
+    const bool one_region = g.split >= g.N && !(g.split2 > 0 && g.split2 < g.N);
+    if (!one_region || g.lo.kind == OUT_GLU || g.N < RG_NARROW_BN || cus < 1)
+        return false;
+    auto cost = [&](int bn) {
+        const int64_t tiles = (int64_t)((g.M + RG_BM - 1) / RG_BM) * ((g.N + bn - 1) / bn);
+        return (tiles + cus - 1) / cus * bn;
+    };
+    return cost(RG_NARROW_BN) < cost(RG_BN);
+}
+
 hipError_t launch_ring(const GemmArgs &g, hipStream_t st)
 {
     if (!ring_supported(g))
         return hipErrorInvalidValue;
-    const int gx = (g.N + RG_BN - 1) / RG_BN, gy = (g.M + RG_BM - 1) / RG_BM;
+    int dev = 0, cus = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess)
+        e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess)
+        return e;
+    const bool narrow = ring_narrow(g, cus);
+    const int bn = narrow ? RG_NARROW_BN : RG_BN;
+    const int gx = (g.N + bn - 1) / bn, gy = (g.M + RG_BM - 1) / RG_BM;
     const int64_t grid = ((int64_t)gx * gy + TL_XCDS - 1) / TL_XCDS * TL_XCDS;
     if (grid > INT32_MAX)
         return hipErrorInvalidValue;
-    hipLaunchKernelGGL(ring_kernel, dim3((unsigned)grid), dim3(WAVE * 8), 0, st, g, gx, gy);
+    if (narrow)
+        hipLaunchKernelGGL((ring_kernel<4, 4, 7>), dim3((unsigned)grid), dim3(WAVE * RG_WAVES), 0, st, g, gx, gy);
+    else
+        hipLaunchKernelGGL((ring_kernel<2, 8, 4>), dim3((unsigned)grid), dim3(WAVE * RG_WAVES), 0, st, g, gx, gy);
     return hipGetLastError();
 }
 

@@ -2,7 +2,11 @@
 (8192 tokens, Zipf-skewed), the full block (16384 tokens, Zipf, 1% exact rank-16/17 ties) and the
 full unsharded experts (4096 tokens, intermediate 3072). Routing is compared bit for bit on every
 token; floating-point tensors on a seeded token sample that the oracle computes one by one. The
-fused route + forward call must reproduce the separate calls bit for bit at every size."""
+fused route + forward call must reproduce the separate calls bit for bit at every size. A ragged
+prefill (8000 tokens) runs the dense products with their last row tile shifted back over its
+neighbour, in the output product's 256 x 224 tiling."""
+from dataclasses import replace
+
 import numpy as np
 import pytest
 import torch
@@ -58,6 +62,25 @@ def test_full_size_parity(name, n_sample):
     active = int(np.sum(run.counts > 0))
     G.log(f"  active experts {active}/{shape.E}, max load {int(run.counts.max())}")
     G.check_forward(shape, inp, run, oracle_logits_in=tied_logits, tokens=tokens)
+    layer.close()
+    del layer, run
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.timeout(400)
+def test_ragged_prefill_shifted_last_row_tile():
+    """8000 tokens at the prefill shape: 32 row tiles of 256 with the last one starting at row 7744,
+    so rows 7744..7935 are computed by two workgroups; the output product still takes 256 x 224 tiles
+    (1024 tiles in four rounds against 896 of 256 x 256). The sample includes rows of the overlap,
+    the last row and rows next to the tile boundaries."""
+    shape = replace(SHAPES["tp8_prefill_t8192"], T=8000, name="tp8_prefill_t8000")
+    G.log(f"[full] {shape.name}: T={shape.T}")
+    inp = make_inputs(shape)
+    layer = G.make_layer(shape, inp, T_max=shape.T)
+    run = G.GpuRun(layer, shape, inp)
+    G.check_fused_identical(layer, shape, inp, run)
+    tokens = np.union1d(sample_tokens(shape, 24), [0, 255, 256, 7679, 7680, 7743, 7744, 7800, 7935, 7936, 7999])
+    G.check_forward(shape, inp, run, tokens=tokens)
     layer.close()
     del layer, run
     torch.cuda.empty_cache()

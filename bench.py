@@ -304,6 +304,9 @@ def main() -> int:
         "ms_per_step_route_then_forward": round(ms_separate, 5),
         "step_hbm_gbps": round(alg["step_bytes"] / step_s / 1e9, 1),
         "step_tflops": round(alg["step_flops"] / step_s / 1e12, 2),
+        # the whole step against both roofs (the full unsharded experts sit at the ridge between them)
+        "step_fracs": {"hbm": round(alg["step_bytes"] / step_s / 1e9 / HBM_PEAK_GBPS, 4),
+                       "mfma": round(alg["step_flops"] / step_s / 1e12 / BF16_PEAK_TFLOPS, 4)},
         # the whole step against the roof of its regime (HBM for decode, dense BF16 for prefill)
         "step_roofline": (dict(bound="hbm", achieved=round(alg["step_bytes"] / step_s / 1e9, 1),
                                peak=HBM_PEAK_GBPS, unit="GB/s",

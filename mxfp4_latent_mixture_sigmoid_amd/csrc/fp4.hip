@@ -177,14 +177,15 @@ __device__ __attribute__((always_inline)) inline void a4_tile(const A4GateupArgs
 
     // A blocks of a stage: for every 16-row fragment one block of codes and one of scale dwords.
     // Wave wv loads fragments f = wv + 4u (u < CU) of both; with fewer than four fragments the
-    // spare waves load fragment wv % NMF once more (the same bytes into the same LDS slots), so
-    // every wave issues the same number of loads on every path and the waits stay exact.
+    // spare waves load fragment wv % NMF once more, and past the last fragment (NMF = 5, 6) a load
+    // repeats the last one (the same bytes into the same LDS slots), so every wave issues the same
+    // number of loads on every path and the waits stay exact.
     constexpr int CU = (NMF + A4_WAVES - 1) / A4_WAVES;
     const uint8_t *csrc[CU], *ssrc[CU];
     int fslot[CU];
 #pragma unroll
     for (int u = 0; u < CU; u++) {
-        const int f = NMF >= A4_WAVES ? wv + A4_WAVES * u : wv % NMF;
+        const int f = NMF >= A4_WAVES ? min(wv + A4_WAVES * u, NMF - 1) : wv % NMF;
         const int r = min(m0 + f * 16 + (lane & 15), m1 - 1);   // clamped valid row, never stored
         const int64_t row = g.a_index ? (int64_t)(g.a_index[r] / g.a_div) : (int64_t)r;
         csrc[u] = g.zq + row * (g.K / 2) + 16 * (lane >> 4);
@@ -301,10 +302,16 @@ void a4_gateup_kernel(const A4GateupArgs g, int gx)
     const int nmf = __builtin_amdgcn_readfirstlane((t.z - t.y + 15) / 16);
     if (nmf <= 1)
         a4_tile<1>(g, bx, t.x, t.y, t.z, lds);
-    else if (nmf <= 2)
+    else if (nmf == 2)
         a4_tile<2>(g, bx, t.x, t.y, t.z, lds);
-    else if (nmf <= 4)
+    else if (nmf == 3)
+        a4_tile<3>(g, bx, t.x, t.y, t.z, lds);
+    else if (nmf == 4)
         a4_tile<4>(g, bx, t.x, t.y, t.z, lds);
+    else if (nmf == 5)
+        a4_tile<5>(g, bx, t.x, t.y, t.z, lds);
+    else if (nmf == 6)
+        a4_tile<6>(g, bx, t.x, t.y, t.z, lds);
     else
         a4_tile<8>(g, bx, t.x, t.y, t.z, lds);
 }

@@ -64,7 +64,7 @@ template <bool MX, int NMF>
 __device__ __attribute__((always_inline)) inline void tiled_tile(const GemmArgs &g, int bx, int group, int m0, int m1,
                                                                  u32x4_t (*lds)[TL_SLOTS])
 {
-    static_assert(NMF == 2 || NMF == 4 || NMF == 8, "row fragments per tile");
+    static_assert(NMF >= 2 && NMF <= 8 && NMF != 7, "row fragments per tile");
     const int lane = threadIdx.x & (WAVE - 1);
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE);   // wave-uniform
     const int n0 = bx * TL_BN + wv * TL_WAVE_N;                  // this wave's first column
@@ -73,13 +73,14 @@ __device__ __attribute__((always_inline)) inline void tiled_tile(const GemmArgs 
 
     // ---- A staging. A stage holds TL_SUB x NMF 1 KiB blocks (sub-step s, fragment f at block
     // s * TL_MFW + f, lane slot l = row f*16 + l%16, inputs s*32 + 8(l/16)). Thread t fills lane slot
-    // t % 64 of blocks b = wv + 4u (u < NMF), b -> (s, f) = (b / NMF, b % NMF): its fragment rows
-    // are f = wv % NMF + 4 (u % FR), FR = NMF / 4 (at least 1) distinct rows.
-    constexpr int FR = NMF >= 8 ? NMF / 4 : 1;
+    // t % 64 of blocks b = wv + 4u (u < NMF), b -> (s, f) = (b / NMF, b % NMF): its fragment row
+    // f = (wv + 4u) % NMF repeats with period FR = NMF / gcd(NMF, 4) in u (NMF = 2..6, 8: 1, 3, 1,
+    // 5, 3, 2 distinct rows), so row pointer u % FR serves load u.
+    constexpr int FR = NMF / (NMF % 4 == 0 ? 4 : NMF % 2 == 0 ? 2 : 1);
     const uint16_t *arow[FR];
 #pragma unroll
     for (int i = 0; i < FR; i++) {
-        const int f = wv % NMF + 4 * i;
+        const int f = (wv + 4 * i) % NMF;
         const int r = min(m0 + f * 16 + (lane & 15), m1 - 1);   // clamped valid row
         const int64_t row = g.a_index ? (int64_t)(g.a_index[r] / g.a_div) : (int64_t)r;
         arow[i] = g.A + row * g.lda + 8 * (lane >> 4);
@@ -352,8 +353,14 @@ __global__ __launch_bounds__(WAVE * 4) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int nmf = __builtin_amdgcn_readfirstlane((m1 - m0 + 15) / 16);
     if (nmf <= 2)
         tiled_tile<MX, 2>(g, bx, group, m0, m1, lds);
-    else if (nmf <= 4)
+    else if (nmf == 3)
+        tiled_tile<MX, 3>(g, bx, group, m0, m1, lds);
+    else if (nmf == 4)
         tiled_tile<MX, 4>(g, bx, group, m0, m1, lds);
+    else if (nmf == 5)
+        tiled_tile<MX, 5>(g, bx, group, m0, m1, lds);
+    else if (nmf == 6)
+        tiled_tile<MX, 6>(g, bx, group, m0, m1, lds);
     else
         tiled_tile<MX, 8>(g, bx, group, m0, m1, lds);
 }

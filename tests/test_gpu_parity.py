@@ -108,6 +108,16 @@ def test_ragged_token_counts(T):
     G.check_forward(replace(shape, T=T), sub, run)
 
 
+@pytest.mark.parametrize("T", [128, 131, 257])
+def test_tiled_expert_paths_ragged(T):
+    """Prefixes of prefill_small on the tiled expert path: partial tiles of every fragment count
+    (the 3-, 4-, 5- and 6-fragment code paths among them), every token compared."""
+    shape, inp, layer = _setup("prefill_small")
+    sub = dict(inp, x=inp["x"][:T])
+    run = G.GpuRun(layer, shape, sub)
+    G.check_forward(replace(shape, T=T), sub, run)
+
+
 @pytest.mark.parametrize("name", list(SMALL_SHAPES))
 def test_route_forward_bit_identical(name):
     shape, inp, layer = _setup(name)

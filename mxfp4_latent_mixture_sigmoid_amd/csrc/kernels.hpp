@@ -49,7 +49,8 @@ enum GemmShape {
 // Dense (g.tiles null: rows 0..M-1) or grouped (tile list, at most `max_tiles` entries).
 constexpr int TILED_BM = 128;
 hipError_t launch_tiled(const GemmArgs &g, bool mx, int max_tiles, hipStream_t st);
-// Dense BF16 product for many rows with both operands staged through LDS (256 x 256 per workgroup).
+// Dense BF16 product for many rows with both operands staged through LDS (256 x 256 or 256 x 224 per
+// workgroup, the narrower tile where it fills the last round of workgroups better).
 bool ring_supported(const GemmArgs &g);
 bool ring_preferred(const GemmArgs &g);   // supported and at least 256 tiles
 hipError_t launch_ring(const GemmArgs &g, hipStream_t st);

@@ -11,6 +11,7 @@
 
 using namespace mxmoe;
 
+
 struct moe_handle {
     moe_config cfg;
     int Hin;             // width of x and of the router's input
@@ -185,6 +186,21 @@ WsLayout ws_layout(const moe_config *c, int64_t T)
     return L;
 }
 
+// Workspace that serves every T <= T_max. Each region grows with T except the few-token
+// split-K partials (present only for T <= SKINNY_MAX_M, at a fixed 64-row size) and the tile
+// list (16-row tiles below the tiled-expert threshold, 128-row tiles from there on), so the
+// maximum over T <= T_max is reached at T_max, at min(T_max, SKINNY_MAX_M) or just below the
+// threshold.
+int64_t ws_bytes_upto(const moe_config *c, int64_t T_max)
+{
+    int64_t best = ws_layout(c, T_max).total;
+    best = std::max(best, ws_layout(c, std::min<int64_t>(T_max, SKINNY_MAX_M)).total);
+    const int64_t thr = ((int64_t)TILED_MIN_ROWS * c->n_experts + c->top_k - 1) / c->top_k;   // first tiled T
+    if (thr - 1 >= 0)
+        best = std::max(best, ws_layout(c, std::min(T_max, thr - 1)).total);
+    return best;
+}
+
 // Largest element index any kernel forms from a 32-bit product must stay below 2^31.
 bool sizes_fit_int32(const moe_config *c, int64_t T)
 {
@@ -192,9 +208,47 @@ bool sizes_fit_int32(const moe_config *c, int64_t T)
     return P < INT_MAX && T * c->n_experts < INT_MAX;
 }
 
+// Every grid that a call for T tokens launches fits the launch limits (grid.x < 2^31, grid.y <
+// 2^16), so that a call that passes argument validation never fails part-way through its
+// launches. Mirrors the grid computations of the launchers (rounded up generously).
+bool launch_shapes_ok(const moe_config *c, int64_t T)
+{
+    if (T <= 0)
+        return true;
+    const int64_t E = c->n_experts, K = c->top_k, Lt = c->latent, I = c->inter, P = T * K;
+    const int64_t Hin = c->has_latent_proj ? c->hidden : c->latent;
+    const int64_t S = c->has_latent_proj ? c->n_shared : 0, Is = S ? c->shared_inter : 0;
+    const int64_t X_MAX = INT32_MAX, Y_MAX = 65535;
+    auto cdiv = [](int64_t a, int64_t b) { return (a + b - 1) / b; };
+    // dense products (router, x-side, router + x-side, output): the widest output has N columns
+    const int64_t N = std::max({(E + 63) / 64 * 64 + Lt + 2 * S * Is, Hin, E + 15});
+    if (cdiv(T, TILED_BM) * cdiv(N, 224) + 8 > X_MAX)
+        return false;
+    // grouping and top-K: one workgroup per 32 tokens / 4 tokens
+    if (cdiv(T, 4) > X_MAX)
+        return false;
+    // expert products over the tile list
+    const int64_t tiles = max_tiles(T, K, E, expert_bm(c, T));
+    if (!tiled_experts(c, T)) {
+        if (tiles > Y_MAX)   // grid.y of the streaming expert kernels
+            return false;
+    } else {
+        const int64_t widest = std::max(cdiv(2 * I, 256), cdiv(Lt, 256));
+        if (tiles * widest + 8 > X_MAX)
+            return false;
+    }
+    // quantisers (one thread per eight values), combine (one workgroup per token and 512 columns)
+    if (cdiv(P * I / 8, 256) > X_MAX || cdiv(T * Lt / 8, 256) > X_MAX || T * cdiv(Lt, 512) > X_MAX)
+        return false;
+    return true;
+}
+
+bool call_fits(const moe_config *c, int64_t T) { return sizes_fit_int32(c, T) && launch_shapes_ok(c, T); }
+
 bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 
 moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
 
 void prof_mark(moe_handle *h, int kid, hipStream_t st, bool start)
 {
@@ -253,18 +307,18 @@ const char *moe_strerror(moe_status s)
 
 moe_status moe_query(const moe_config *cfg, int32_t T_max, size_t *packed_bytes, size_t *workspace_bytes)
 {
-    if (!valid_config(cfg) || T_max < 0 || !sizes_fit_int32(cfg, T_max))
+    if (!valid_config(cfg) || T_max < 0 || !call_fits(cfg, T_max))
         return MOE_ERR_INVALID_ARG;
     if (packed_bytes)
         *packed_bytes = (size_t)packed_layout(cfg).total;
     if (workspace_bytes)
-        *workspace_bytes = (size_t)ws_layout(cfg, T_max).total;
+        *workspace_bytes = (size_t)ws_bytes_upto(cfg, T_max);
     return MOE_OK;
 }
 
 moe_status moe_query_workspace_layout(const moe_config *cfg, int32_t T, size_t *offsets)
 {
-    if (!valid_config(cfg) || T < 0 || !sizes_fit_int32(cfg, T) || !offsets)
+    if (!valid_config(cfg) || T < 0 || !call_fits(cfg, T) || !offsets)
         return MOE_ERR_INVALID_ARG;
     const WsLayout W = ws_layout(cfg, T);
     const int64_t v[11] = {W.logits, W.hist, W.tiles, W.z, W.acat, W.h, W.y, W.h8, W.z4, W.rpartials, W.total};
@@ -683,7 +737,7 @@ moe_status experts_impl(moe_handle *h, const void *x, int32_t T, const moe_routi
 moe_status check_route_args(moe_handle *h, const void *x, int32_t T, const float *logit_bias, const float *logits_in,
                             const float *logits_out, const moe_routing *r)
 {
-    if (!h || T < 0 || !r || !sizes_fit_int32(&h->cfg, T))
+    if (!h || T < 0 || !r || !call_fits(&h->cfg, T))
         return MOE_ERR_INVALID_ARG;
     if (T == 0)
         return MOE_OK;
@@ -698,7 +752,7 @@ moe_status check_route_args(moe_handle *h, const void *x, int32_t T, const float
 
 moe_status check_forward_args(moe_handle *h, const void *x, int32_t T, const moe_routing *r, const void *out)
 {
-    if (!h || T < 0 || !r || !sizes_fit_int32(&h->cfg, T))
+    if (!h || T < 0 || !r || !call_fits(&h->cfg, T))
         return MOE_ERR_INVALID_ARG;
     if (T == 0)
         return MOE_OK;
@@ -755,21 +809,28 @@ moe_status moe_forward(moe_handle *h, const void *x, int32_t T, const moe_routin
     return experts_impl(h, x, T, r, out, W, ws, st);
 }
 
-moe_status moe_route_forward(moe_handle *h, const void *x, int32_t T, const float *logit_bias, float *logits_out,
-                             const moe_routing *r, void *out, void *workspace, size_t workspace_bytes, void *stream)
+} // extern "C"
+
+namespace {
+
+moe_status check_route_forward_args(moe_handle *h, const void *x, int32_t T, const float *logit_bias,
+                                    const float *logits_out, const moe_routing *r, const void *out)
 {
     moe_status e = check_route_args(h, x, T, logit_bias, nullptr, logits_out, r);
     if (e == MOE_OK)
         e = check_forward_args(h, x, T, r, out);
     if (e != MOE_OK || T == 0)
         return e;
-    if (logits_out == out || (const void *)logits_out == x)
+    if ((const void *)logits_out == out || (const void *)logits_out == x)
         return MOE_ERR_INVALID_ARG;
-    const WsLayout W = ws_layout(&h->cfg, T);
-    if ((e = check_workspace(W, workspace, workspace_bytes)) != MOE_OK)
-        return e;
-    uint8_t *ws = static_cast<uint8_t *>(workspace);
-    hipStream_t st = static_cast<hipStream_t>(stream);
+    return MOE_OK;
+}
+
+// The launch sequence of moe_route_forward on workspace `ws` (layout W); arguments checked.
+moe_status route_forward_impl(moe_handle *h, const void *x, int32_t T, const float *logit_bias, float *logits_out,
+                              const moe_routing *r, void *out, const WsLayout &W, uint8_t *ws, hipStream_t st)
+{
+    moe_status e;
     if (h->cfg.has_latent_proj)
         e = front_impl(h, x, T, logit_bias, logits_out, r, W, ws, st);
     else {   // no x-side products: router, then the grouping builds the tile lists
@@ -781,6 +842,23 @@ moe_status moe_route_forward(moe_handle *h, const void *x, int32_t T, const floa
     if (e != MOE_OK)
         return e;
     return experts_impl(h, x, T, r, out, W, ws, st);
+}
+
+} // namespace
+
+extern "C" {
+
+moe_status moe_route_forward(moe_handle *h, const void *x, int32_t T, const float *logit_bias, float *logits_out,
+                             const moe_routing *r, void *out, void *workspace, size_t workspace_bytes, void *stream)
+{
+    moe_status e = check_route_forward_args(h, x, T, logit_bias, logits_out, r, out);
+    if (e != MOE_OK || T == 0)
+        return e;
+    const WsLayout W = ws_layout(&h->cfg, T);
+    if ((e = check_workspace(W, workspace, workspace_bytes)) != MOE_OK)
+        return e;
+    return route_forward_impl(h, x, T, logit_bias, logits_out, r, out, W, static_cast<uint8_t *>(workspace),
+                              static_cast<hipStream_t>(stream));
 }
 
 moe_status moe_unpack_expert(moe_handle *h, int32_t e, int32_t which, void *out, void *stream)

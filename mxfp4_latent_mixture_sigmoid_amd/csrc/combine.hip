@@ -25,10 +25,10 @@ hipError_t launch_tilemap(const int32_t *offsets, int E, int bm, int32_t *tiles,
 constexpr int CB = 8;
 __global__ __launch_bounds__(64) void combine_kernel(const uint16_t *__restrict__ Y, int Lt,
                                                      const int32_t *__restrict__ inv, const float *__restrict__ w,
-                                                     int K, uint16_t *__restrict__ out, int64_t ldo)
+                                                     int K, uint16_t *__restrict__ out, int64_t ldo, int chunks)
 {
-    const int t = blockIdx.y;
-    const int c8 = blockIdx.x * 64 + threadIdx.x;
+    const int t = (int)(blockIdx.x / chunks);
+    const int c8 = (int)(blockIdx.x % chunks) * 64 + threadIdx.x;
     if (c8 * 8 >= Lt)
         return;
     const int32_t *it = inv + (int64_t)t * K;
@@ -71,10 +71,13 @@ hipError_t launch_combine(const uint16_t *Y, int Lt, const int32_t *inv, const f
                           uint16_t *out, int64_t ldo, hipStream_t st)
 {
     // column chunks fastest: the chunks of one token (its K rows of y read whole) run back to back
-    if (T > 65535)
+    const int64_t chunks = (Lt / 8 + 63) / 64;
+    if (T <= 0)
+        return hipSuccess;
+    if (chunks * T > INT32_MAX)
         return hipErrorInvalidValue;
-    const dim3 grid((Lt / 8 + 63) / 64, T);
-    hipLaunchKernelGGL(combine_kernel, grid, dim3(64), 0, st, Y, Lt, inv, w, K, out, ldo);
+    hipLaunchKernelGGL(combine_kernel, dim3((unsigned)(chunks * T)), dim3(64), 0, st, Y, Lt, inv, w, K, out, ldo,
+                       (int)chunks);
     return hipGetLastError();
 }
 

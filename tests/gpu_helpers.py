@@ -200,9 +200,11 @@ def assert_close_e2e(name: str, got, ref) -> dict:
     err = np.abs(got - ref)
     rms = float(np.sqrt(np.mean(ref * ref)))
     over = err > MAX_REL_RMS * rms
-    near = over & (err <= E2E_ULPS * bf16_ulp(ref))
+    ulps = err / bf16_ulp(ref)
+    near = over & (ulps <= E2E_ULPS)
+    worst = float(ulps[over].max()) if np.any(over) else 0.0
     log(f"  {name}: max|err|={err.max():.3e} mean|err|={err.mean():.3e} rms(ref)={rms:.3e} "
-        f"beyond-bar(<= {E2E_ULPS} ulp)={int(near.sum())}/{err.size}")
+        f"beyond-bar(<= {E2E_ULPS} ulp)={int(near.sum())}/{err.size} worst-beyond-bar-ulps={worst:g}")
     assert np.all(np.isfinite(got)), f"{name}: non-finite values"
     assert not np.any(over & ~near), f"{name}: {int(np.sum(over & ~near))} elements beyond the bar by > {E2E_ULPS} ulp"
     assert near.sum() <= MAX_FLIP_FRAC * err.size, f"{name}: {int(near.sum())} elements beyond the bar"

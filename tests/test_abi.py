@@ -134,3 +134,47 @@ def test_unknown_first_stage_is_rejected():
     c = _cfg()
     c.stage1 = 2
     assert abi.lib().moe_query(ctypes.byref(c), 64, None, None) == abi.Status.INVALID_ARG
+
+
+def _shape_cfg(shape, **kw):
+    return abi.make_config(shape.H, shape.Lt, shape.E, shape.K, shape.I, shape.S, shape.Is, shape.has_latent, **kw)
+
+
+@pytest.mark.parametrize("name", ["tiny", "tp8_decode_t64", "tp8_prefill_t8192", "full_experts_t4096"])
+@pytest.mark.parametrize("quant", [{}, dict(stage2_fp8=True, stage1_a4=True)])
+def test_query_workspace_serves_every_smaller_batch(name, quant):
+    """moe_query(T_max) must cover every call with T <= T_max: the few-token split-K partials exist
+    only up to 64 tokens and the tile list shrinks once experts average 32 rows, so the workspace
+    of T_max alone can be smaller than that of a smaller T."""
+    from workload import SHAPES
+    s = SHAPES[name]
+    if quant and s.I > 512:
+        return   # the FP8 second stage keeps an I-wide h tile in LDS (I <= 512)
+    c = _shape_cfg(s, **quant)
+    thr = -(-32 * s.E // s.K)                 # first token count on the many-rows expert path
+    for T_max in sorted({1, 63, 64, 65, 128, 200, thr - 1, thr, thr + 7, 2 * thr, s.T}):
+        _, wb = abi.query(c, T_max)
+        for T in sorted({0, 1, 16, 63, 64, 65, T_max // 2, thr - 1, thr, T_max}):
+            if 0 <= T <= T_max:
+                need = abi.workspace_layout(c, T)["total"]
+                assert need <= wb, (name, T_max, T, need, wb)
+
+
+def test_query_accepts_large_batches_and_rejects_unlaunchable_ones():
+    """Token counts past the 65,535 grid.y limit are served (the combine takes a 1-D grid); counts
+    whose index products or grids cannot be formed are rejected before anything is enqueued."""
+    c = _cfg()
+    pb, wb = abi.query(c, 70000)
+    assert pb > 0 and wb > 0
+    assert abi.lib().moe_query(ctypes.byref(c), 70000, None, None) == abi.Status.OK
+    # T x E >= 2^31
+    assert abi.lib().moe_query(ctypes.byref(c), 2_400_000, None, None) == abi.Status.INVALID_ARG
+    # index products fit, but the combine's grid (T x 7 workgroups) would not
+    big = abi.make_config(3584, 3584, 1, 1, 3072, 0, 0, False)
+    assert abi.lib().moe_query(ctypes.byref(big), 2_000_000_000, None, None) == abi.Status.INVALID_ARG
+    lay = (ctypes.c_size_t * 11)()
+    assert abi.lib().moe_query_workspace_layout(ctypes.byref(big), 2_000_000_000, lay) == abi.Status.INVALID_ARG
+    r = abi.MoeRouting()
+    # route / forward reject such T before touching the handle's GPU state (null handle here)
+    assert abi.lib().moe_route(None, None, 2_000_000_000, None, None, None, ctypes.byref(r), None, 0, None) == \
+        abi.Status.INVALID_ARG

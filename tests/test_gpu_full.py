@@ -18,7 +18,7 @@ from workload import SHAPES, make_inputs, sample_tokens, tie_tokens
 pytestmark = pytest.mark.gpu
 
 FULL = [("tp8_decode_t64", None), ("tp8_prefill_t8192", 48), ("tp8_block_t16384", 40),
-        ("full_experts_t4096", 10)]
+        ("full_experts_t4096", 64)]
 
 
 @pytest.fixture(scope="module", autouse=True)

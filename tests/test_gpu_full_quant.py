@@ -24,7 +24,7 @@ pytestmark = pytest.mark.gpu
 # (workload, sampled tokens or all, FP8 second stage too). The FP8 stage keeps a 128-row tile of h in
 # LDS and so needs I <= 512: the full unsharded experts (I = 3072) run the A4W4 stage alone.
 CASES = [("tp8_decode_t64", None, True), ("tp8_prefill_t8192", 32, True), ("tp8_prefill_t8192", 32, False),
-         ("tp8_block_t16384", 24, True), ("full_experts_t4096", 8, False)]
+         ("tp8_block_t16384", 24, True), ("full_experts_t4096", 64, False)]
 
 
 @pytest.fixture(scope="module", autouse=True)

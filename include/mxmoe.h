@@ -177,6 +177,25 @@ moe_status moe_route_forward(moe_handle *h, const void *x, int32_t T, const floa
                              float *logits_out, const moe_routing *r, void *out, void *workspace,
                              size_t workspace_bytes, void *stream);
 
+/* Size of the device scratch array that moe_route_forward_static works in: 40 MiB, enough for the
+ * workspace of up to ~280 tokens at one GPU's TP8 share of the Kimi K3 layer (64 decode tokens
+ * need 29.5 MiB) and of every call whose moe_query workspace_bytes is at most this size. */
+#define MOE_STATIC_SCRATCH_BYTES ((size_t)40 << 20)
+
+/* moe_route_forward without a workspace argument, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that forbid allocation.
+ * The workspace is a file-scope device array of MOE_STATIC_SCRATCH_BYTES inside the library, one
+ * per GPU, allocated when the library's code is loaded on that GPU and held until the process
+ * ends; the call itself allocates nothing (no hipMalloc / hipFree). Results are identical bit for
+ * bit to moe_route_forward's with a caller workspace. Arguments and errors as for
+ * moe_route_forward, plus MOE_ERR_BUFFER_TOO_SMALL when this call's workspace (moe_query with
+ * T_max = T) exceeds MOE_STATIC_SCRATCH_BYTES, returned before anything is enqueued.
+ * Every call on one GPU uses that GPU's single array, which keeps the previous call's contents:
+ * calls that overlap on one GPU (concurrent streams, or several handles) race on it and must be
+ * serialised by the caller (e.g. one stream per GPU). */
+moe_status moe_route_forward_static(moe_handle *h, const void *x, int32_t T, const float *logit_bias,
+                                    float *logits_out, const moe_routing *r, void *out, void *stream);
+
 /* Test hook: dequantise expert e's packed matrix `which` (0 gate [I, Lt], 1 up [I, Lt],
  * 2 down [Lt, I]) back to canonical row-major BF16 in `out` through the same in-register
  * E2M1/E8M0 conversion the expert GEMMs use. */

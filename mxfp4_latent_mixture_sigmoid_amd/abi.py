@@ -65,6 +65,7 @@ SIGNATURES = {
     "moe_forward": (c_i32, [c_vp, c_vp, c_i32, ctypes.POINTER(MoeRouting), c_vp, c_vp, c_size, c_vp]),
     "moe_route_forward": (c_i32, [c_vp, c_vp, c_i32, c_vp, c_vp, ctypes.POINTER(MoeRouting), c_vp, c_vp, c_size,
                                   c_vp]),
+    "moe_route_forward_static": (c_i32, [c_vp, c_vp, c_i32, c_vp, c_vp, ctypes.POINTER(MoeRouting), c_vp, c_vp]),
     "moe_unpack_expert": (c_i32, [c_vp, c_i32, c_i32, c_vp, c_vp]),
     "moe_profile_begin": (c_i32, [c_vp, c_i32]),
     "moe_profile_end": (c_i32, [c_vp, ctypes.POINTER(c_i32), ctypes.POINTER(ctypes.c_float), ctypes.POINTER(c_i32)]),
@@ -165,6 +166,16 @@ def route_forward(h, x, T, routing: dict, out, workspace, logit_bias=None, logit
     rs = routing_struct(routing)
     check(lib().moe_route_forward(h, ptr(x), T, ptr(logit_bias), ptr(logits_out), ctypes.byref(rs), ptr(out),
                                   ptr(workspace), workspace.numel(), stream_handle(stream)), "moe_route_forward")
+
+
+STATIC_SCRATCH_BYTES = 40 << 20   # MOE_STATIC_SCRATCH_BYTES
+
+
+def route_forward_static(h, x, T, routing: dict, out, logit_bias=None, logits_out=None, stream=None) -> None:
+    """moe_route_forward_static: no workspace argument (the library's per-GPU scratch array)."""
+    rs = routing_struct(routing)
+    check(lib().moe_route_forward_static(h, ptr(x), T, ptr(logit_bias), ptr(logits_out), ctypes.byref(rs), ptr(out),
+                                         stream_handle(stream)), "moe_route_forward_static")
 
 
 def unpack_expert(h, e: int, which: int, out, stream=None) -> None:

@@ -7,10 +7,15 @@
 #include <cstdlib>
 #include <new>
 #include <algorithm>
+#include <mutex>
 #include <vector>
 
 using namespace mxmoe;
 
+// Workspace of moe_route_forward_static: a file-scope device array, one copy per GPU that the
+// library's code object is loaded on, held until the process ends. Host code never passes the
+// array's name to a kernel: it uses the device address looked up per device (scratch_address).
+static __device__ __align__(256) uint8_t scratch[MOE_STATIC_SCRATCH_BYTES];
 
 struct moe_handle {
     moe_config cfg;
@@ -249,6 +254,27 @@ bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 
 moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
+// Device address of `scratch` on each device, looked up once per device with that device current
+// (moe_create's, or the first static call's), then reused.
+constexpr int SCRATCH_MAX_DEVICES = 64;
+std::mutex scratch_mu;
+void *scratch_dev_ptr[SCRATCH_MAX_DEVICES];
+
+moe_status scratch_address(void **out)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= SCRATCH_MAX_DEVICES)
+        return MOE_ERR_HIP;
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (!scratch_dev_ptr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p)
+            return MOE_ERR_HIP;
+        scratch_dev_ptr[dev] = p;
+    }
+    *out = scratch_dev_ptr[dev];
+    return MOE_OK;
+}
 
 void prof_mark(moe_handle *h, int kid, hipStream_t st, bool start)
 {
@@ -406,6 +432,10 @@ moe_status moe_create(const moe_config *cfg, const moe_weights *w, void *packed,
         moe_destroy(h);
         return MOE_ERR_HIP;
     }
+    // set-up of moe_route_forward_static's scratch on this device (a failure here is reported by
+    // that entry point's first call, which looks the address up again)
+    void *scratch_ptr = nullptr;
+    (void)scratch_address(&scratch_ptr);
     *out = h;
     return MOE_OK;
 }
@@ -858,6 +888,24 @@ moe_status moe_route_forward(moe_handle *h, const void *x, int32_t T, const floa
     if ((e = check_workspace(W, workspace, workspace_bytes)) != MOE_OK)
         return e;
     return route_forward_impl(h, x, T, logit_bias, logits_out, r, out, W, static_cast<uint8_t *>(workspace),
+                              static_cast<hipStream_t>(stream));
+}
+
+moe_status moe_route_forward_static(moe_handle *h, const void *x, int32_t T, const float *logit_bias,
+                                    float *logits_out, const moe_routing *r, void *out, void *stream)
+{
+    moe_status e = check_route_forward_args(h, x, T, logit_bias, logits_out, r, out);
+    if (e != MOE_OK || T == 0)
+        return e;
+    const WsLayout W = ws_layout(&h->cfg, T);
+    if ((uint64_t)W.total > (uint64_t)MOE_STATIC_SCRATCH_BYTES)
+        return MOE_ERR_BUFFER_TOO_SMALL;
+    void *ws = nullptr;
+    if ((e = scratch_address(&ws)) != MOE_OK)
+        return e;
+    // nothing in the workspace has to start at zero: every region a launch reads is written
+    // earlier in the same call
+    return route_forward_impl(h, x, T, logit_bias, logits_out, r, out, W, static_cast<uint8_t *>(ws),
                               static_cast<hipStream_t>(stream));
 }
 

@@ -64,6 +64,14 @@ class MoELayer:
         abi.route_forward(self.handle, x, T, routing, out, self.workspace, logit_bias, logits_out, stream)
         return out
 
+    def route_forward_static(self, x, T, routing, out=None, logit_bias=None, logits_out=None, stream=None):
+        """route + forward in the library's per-GPU scratch array instead of this layer's workspace
+        (the call allocates nothing; bitwise identical to route_forward)."""
+        if out is None:
+            out = torch.empty(max(T, 1), self.H, dtype=torch.bfloat16, device=self.device)
+        abi.route_forward_static(self.handle, x, T, routing, out, logit_bias, logits_out, stream)
+        return out
+
     def unpack_expert(self, e: int, which: int, stream=None):
         rows, cols = (self.cfg.inter, self.Lt) if which < 2 else (self.Lt, self.cfg.inter)
         out = torch.empty(rows, cols, dtype=torch.bfloat16, device=self.device)

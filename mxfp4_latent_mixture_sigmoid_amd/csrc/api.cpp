@@ -2,11 +2,14 @@
 // layouts, and the launch sequence of moe_route / moe_forward on the caller's stream.
 #include "kernels.hpp"
 #include "mxmoe.h"
+#include "sync.hpp"
 
 #include <climits>
 #include <cstdlib>
 #include <new>
 #include <algorithm>
+#include <atomic>
+#include <chrono>
 #include <mutex>
 #include <vector>
 
@@ -49,6 +52,17 @@ constexpr int SKINNY_XSTEPS = 16;  // ... and of the few-token x-side and output
 constexpr int XSIDE_GROUPS = 18, OUT_GROUPS = 28;
 // ... and of the combined router + x-side product (6016 columns at the full size)
 constexpr int RX_GROUPS = 18;
+
+// Sequence number of a call: the epoch of the in-kernel counters it uses (sync.hpp). Unique within
+// the process, and started from the clock so that a counter left in reused memory by an earlier
+// process is unlikely to carry a current epoch.
+uint64_t initial_seq()
+{
+    const uint64_t t = (uint64_t)std::chrono::steady_clock::now().time_since_epoch().count();
+    return (t >> 8) & ((1ull << 40) - 1);
+}
+std::atomic<uint64_t> call_seq{initial_seq()};
+uint64_t next_seq() { return call_seq.fetch_add(1) & ((1ull << (64 - EPOCH_SHIFT)) - 1); }
 // Router rows in the combined router + x-side matrix: a multiple of the 64-column wave width, so
 // that no wave of the many-token product straddles the logits and the z columns.
 int64_t router_rows_rx(const moe_config *c) { return ((int64_t)c->n_experts + 63) / 64 * 64; }
@@ -130,6 +144,7 @@ PackedLayout packed_layout(const moe_config *c)
 
 struct WsLayout {
     int64_t logits, hist, tiles, z, acat, h, y, h8, z4, partials, total;
+    int64_t sync;                       // epoch counter of the top-K launch's grouping (T <= SKINNY_MAX_M)
     int64_t rpartials;                  // router partials (inside the partials region, before the dense ones)
     int64_t max_tiles;                  // capacity of the expert tile list (shared by both expert products)
 };
@@ -187,6 +202,9 @@ WsLayout ws_layout(const moe_config *c, int64_t T)
             off = align_up(off + p * 4);
         }
     }
+    L.sync = off;
+    if (T <= SKINNY_MAX_M)
+        off += ALIGN;
     L.total = off;
     return L;
 }
@@ -501,10 +519,26 @@ void moe_destroy(moe_handle *h)
 
 namespace {
 
+// The grouping by expert runs inside the top-K launch (few tokens, logits from split-K partials):
+// the last top-K workgroup writes the routing arrays, and the tile list when `tiles` is set.
+void set_grouping(TopkArgs &ta, const moe_routing *r, const WsLayout &W, uint8_t *ws, int32_t *tiles, int bm,
+                  uint64_t seq)
+{
+    ta.group = 1;
+    ta.counts = r->counts;
+    ta.offsets = r->offsets;
+    ta.sorted_pairs = r->sorted_pairs;
+    ta.inv = r->inv;
+    ta.tiles = tiles;
+    ta.bm = bm;
+    ta.sync = reinterpret_cast<uint64_t *>(ws + W.sync);
+    ta.seq = seq;
+}
+
 // Router product (logits, or split-K partials for few tokens); fills the top-K arguments.
 moe_status router_impl(moe_handle *h, const void *x, int32_t T, const float *logit_bias, const float *logits_in,
                        float *logits_out, const moe_routing *r, const WsLayout &W, uint8_t *ws, hipStream_t st,
-                       TopkArgs &ta)
+                       uint64_t seq, TopkArgs &ta)
 {
     const moe_config *c = &h->cfg;
     const int E = c->n_experts, K = c->top_k;
@@ -530,6 +564,7 @@ moe_status router_impl(moe_handle *h, const void *x, int32_t T, const float *log
         ta.splits = skinny_splits(h->Hin, SKINNY_STEPS);
         ta.bias = logit_bias;
         ta.logits_out = logits_out;
+        set_grouping(ta, r, W, ws, nullptr, 0, seq);
     } else {
         float *lg = logits_out ? logits_out : reinterpret_cast<float *>(ws + W.logits);
         GemmArgs g{};
@@ -554,9 +589,16 @@ moe_status select_impl(moe_handle *h, int32_t T, const TopkArgs &ta, const moe_r
 {
     const moe_config *c = &h->cfg;
     const int E = c->n_experts, K = c->top_k;
-    MOE_LAUNCH(MOE_KERNEL_TOPK, launch_topk(ta, st));
     int32_t *tl = reinterpret_cast<int32_t *>(ws + W.tiles);
     const int bm = expert_bm(c, T);
+    if (ta.group) {   // grouping (and tile list) inside the top-K launch
+        TopkArgs tg = ta;
+        tg.tiles = tiles ? tl : nullptr;
+        tg.bm = bm;
+        MOE_LAUNCH(MOE_KERNEL_TOPK, launch_topk(tg, st));
+        return MOE_OK;
+    }
+    MOE_LAUNCH(MOE_KERNEL_TOPK, launch_topk(ta, st));
     if (T <= PERM_SMALL_MAX_T) {
         MOE_LAUNCH(MOE_KERNEL_PERMUTE, launch_permute_small(r->topk_ids, T, K, E, r->counts, r->offsets,
                                                             r->sorted_pairs, r->inv, st, bm, tiles ? tl : nullptr));
@@ -621,7 +663,7 @@ moe_status xside_impl(moe_handle *h, const void *x, int32_t T, const moe_routing
 // tile lists.
 // Every output element is computed in the same order as by the separate products.
 moe_status front_impl(moe_handle *h, const void *x, int32_t T, const float *logit_bias, float *logits_out,
-                      const moe_routing *r, const WsLayout &W, uint8_t *ws, hipStream_t st)
+                      const moe_routing *r, const WsLayout &W, uint8_t *ws, hipStream_t st, uint64_t seq)
 {
     const moe_config *c = &h->cfg;
     const int E = c->n_experts, K = c->top_k, Lt = c->latent, H = c->hidden;
@@ -651,13 +693,11 @@ moe_status front_impl(moe_handle *h, const void *x, int32_t T, const float *logi
         ta.splits = splits;
         ta.bias = logit_bias;
         ta.logits_out = logits_out;
-        // top-K and the x-side epilogue in one launch, then the grouping with the tile lists
+        // top-K (with the grouping and the tile lists) and the x-side epilogue in one launch
+        set_grouping(ta, r, W, ws, reinterpret_cast<int32_t *>(ws + W.tiles), bm, seq);
         XsideEpiArgs ea{P + (int64_t)(Erx / 16) * SKINNY_TILE_FLOATS, pstride, splits, T, Nx, Lt, 2 * S * Is, Z,
                         Acat, ldcat, nullptr, E, bm, nullptr};
         MOE_LAUNCH(MOE_KERNEL_TOPK, launch_topk_xside(ta, ea, st));
-        MOE_LAUNCH(MOE_KERNEL_PERMUTE,
-                   launch_permute_small(r->topk_ids, T, K, E, r->counts, r->offsets, r->sorted_pairs, r->inv, st, bm,
-                                        reinterpret_cast<int32_t *>(ws + W.tiles)));
         return MOE_OK;
     }
     float *lg = logits_out ? logits_out : reinterpret_cast<float *>(ws + W.logits);
@@ -818,7 +858,7 @@ moe_status moe_route(moe_handle *h, const void *x, int32_t T, const float *logit
     uint8_t *ws = static_cast<uint8_t *>(workspace);
     hipStream_t st = static_cast<hipStream_t>(stream);
     TopkArgs ta;
-    if ((e = router_impl(h, x, T, logit_bias, logits_in, logits_out, r, W, ws, st, ta)) != MOE_OK)
+    if ((e = router_impl(h, x, T, logit_bias, logits_in, logits_out, r, W, ws, st, next_seq(), ta)) != MOE_OK)
         return e;
     return select_impl(h, T, ta, r, W, ws, st, false);
 }
@@ -861,11 +901,12 @@ moe_status route_forward_impl(moe_handle *h, const void *x, int32_t T, const flo
                               const moe_routing *r, void *out, const WsLayout &W, uint8_t *ws, hipStream_t st)
 {
     moe_status e;
+    const uint64_t seq = next_seq();
     if (h->cfg.has_latent_proj)
-        e = front_impl(h, x, T, logit_bias, logits_out, r, W, ws, st);
+        e = front_impl(h, x, T, logit_bias, logits_out, r, W, ws, st, seq);
     else {   // no x-side products: router, then the grouping builds the tile lists
         TopkArgs ta;
-        e = router_impl(h, x, T, logit_bias, nullptr, logits_out, r, W, ws, st, ta);
+        e = router_impl(h, x, T, logit_bias, nullptr, logits_out, r, W, ws, st, seq, ta);
         if (e == MOE_OK)
             e = select_impl(h, T, ta, r, W, ws, st, true);
     }

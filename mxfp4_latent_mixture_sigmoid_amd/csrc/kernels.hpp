@@ -170,6 +170,14 @@ struct TopkArgs {
     int T, E, K;
     int32_t *ids;
     float *w;
+    // Grouping inside the top-K launch (partials path, T <= PERM_SMALL_MAX_T): the last top-K
+    // workgroup to finish writes counts / offsets / sorted_pairs / inv (and the tile list of bm rows
+    // when `tiles` is set) from the ids, handed over as agent-coherent stores and an epoch counter.
+    int group;
+    int32_t *counts, *offsets, *sorted_pairs, *inv, *tiles;
+    int bm;
+    uint64_t *sync;   // one epoch counter
+    uint64_t seq;     // the call's sequence number
 };
 constexpr int PERM_TOKENS_PER_BLOCK = 32;
 constexpr int PERM_SMALL_MAX_T = 256;

@@ -8,8 +8,8 @@
 namespace mxmoe {
 
 // Partial sums load SUM_BATCH splits at a time (addresses clamped, so every load is valid) before
-// any of them is used.
-constexpr int SUM_BATCH = 8;
+// any of them is used: one round of loads for up to 16 splits (K up to 8192 in 512-wide splits).
+constexpr int SUM_BATCH = 16;
 // Sum over the splits of one lane's 16-byte partial slot (four rows of one column), split order.
 __device__ inline f32x4_t sum_slot(const float *slot, int64_t split_stride, int splits)
 {

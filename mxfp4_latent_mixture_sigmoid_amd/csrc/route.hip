@@ -2,6 +2,7 @@
 // token/expert pairs by expert (histogram, per-expert scan, stable scatter).
 #include "kernels.hpp"
 #include "partials.hpp"
+#include "sync.hpp"
 
 
 namespace mxmoe {
@@ -115,9 +116,81 @@ __device__ inline void select_keys(const TopkArgs &a, int t, const uint32_t *key
     const float s = lane < K ? 1.0f / (1.0f + expf(-key_value(my_key))) : 0.0f;
     const float sum = wave_sum_f32(s);
     if (lane < K) {
-        a.ids[(int64_t)t * K + lane] = my_id;
+        if (a.group)   // read back by the grouping workgroup of the same launch
+            store4_sc1(flat_rsrc(a.ids, (int64_t)a.T * K * 4), (int)(((int64_t)t * K + lane) * 4), (uint32_t)my_id);
+        else
+            a.ids[(int64_t)t * K + lane] = my_id;
         a.w[(int64_t)t * K + lane] = s / sum;
     }
+}
+
+// Grouping of the T x K pairs by expert by one workgroup (any size that is a multiple of 64), from
+// ids written earlier in the same launch (agent-coherent loads). As in the one-workgroup grouping
+// kernel below: a bit mask per expert marks its tokens, counts are popcounts, offsets their
+// exclusive scan, and pair (t, j) goes to offsets[e] + the number of e's tokens before t.
+// `lds` holds at least E * ceil(T / 32) + E + 1 words; `sh` 16 ints.
+__device__ inline void group_pairs(const TopkArgs &a, uint32_t *lds, int *sh)
+{
+    const int T = a.T, K = a.K, E = a.E, P = T * K;
+    const int W = (T + 31) / 32;
+    const int nthr = (int)blockDim.x, tid = (int)threadIdx.x;
+    uint32_t *masks = lds;
+    int *off = reinterpret_cast<int *>(lds + E * W);
+    const auto ir = flat_rsrc(a.ids, (int64_t)P * 4);
+    for (int i = tid; i < E * W; i += nthr)
+        masks[i] = 0u;
+    __syncthreads();
+    constexpr int PPT = 4;   // pairs per thread held in registers (P <= PPT * blockDim, host check)
+    int ev[PPT];
+#pragma unroll
+    for (int u = 0; u < PPT; u++) {
+        const int p = tid + u * nthr;
+        ev[u] = p < P ? (int)load4_sc1(ir, p * 4) : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < PPT; u++) {
+        const int p = tid + u * nthr;
+        if (p < P)
+            atomicOr(&masks[ev[u] * W + (p / K) / 32], 1u << ((p / K) & 31));
+    }
+    __syncthreads();
+    const int per = (E + nthr - 1) / nthr, e0 = tid * per, e1 = min(E, e0 + per);
+    int c = 0;
+    for (int e = e0; e < e1; e++)
+        for (int w = 0; w < W; w++)
+            c += __popc(masks[e * W + w]);
+    int total;
+    int run = block_excl_scan(c, sh, &total);
+    for (int e = e0; e < e1; e++) {
+        int n = 0;
+        for (int w = 0; w < W; w++)
+            n += __popc(masks[e * W + w]);
+        a.counts[e] = n;
+        a.offsets[e] = run;
+        off[e] = run;
+        run += n;
+    }
+    if (tid == 0) {
+        a.offsets[E] = total;
+        off[E] = total;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < PPT; u++) {
+        const int p = tid + u * nthr;
+        if (p >= P)
+            continue;
+        const int e = ev[u], t = p / K;
+        const uint32_t *m = masks + e * W;
+        int rank = __popc(m[t / 32] & ((1u << (t & 31)) - 1u));
+        for (int w = 0; w < t / 32; w++)
+            rank += __popc(m[w]);
+        const int pos = off[e] + rank;
+        a.sorted_pairs[pos] = p;
+        a.inv[p] = pos;
+    }
+    if (a.tiles)
+        write_tiles(off, E, a.bm, a.tiles, sh);
 }
 
 // Logits given row by row (src[t * ld + e]): one wave per token.
@@ -138,74 +211,77 @@ __global__ __launch_bounds__(256) void topk_kernel(const TopkArgs a)
     select_keys<SLOTS>(a, t, key, scratch[wv]);
 }
 
+__device__ inline int gridDim_topk(const TopkArgs &a) { return (a.T + 3) / 4; }   // top-K workgroups
+
 // Logits as split-K partial tiles (accumulator order): eight waves per workgroup, which takes tokens
-// 4 b .. 4 b + 3 (one 16-byte partial slot of an expert holds four consecutive tokens). Wave w adds
-// splits w, w + 8, ... of every expert (lane l, slot j: expert l + 64 j), then the eight wave sums
-// are added pairwise through LDS in a fixed tree (w += w + 4, w += w + 2, w += w + 1); waves 0..3
-// then select tokens 4 b .. 4 b + 3 from the totals.
+// 4 b .. 4 b + 3 (one 16-byte partial slot of an expert holds four consecutive tokens). Wave w owns
+// slots j = w, w + 8 (lane l, slot j: expert l + 64 j) and adds them over all splits in split order,
+// with every split's loads in flight at once; the totals go through LDS to waves 0..3, which then
+// select tokens 4 b .. 4 b + 3.
 template <int SLOTS>
 __device__ inline void topk_wide_block(const TopkArgs &a, int blk)
 {
-    constexpr int WAVES = 8;
-    __shared__ f32x4_t red[WAVES / 2 * SLOTS * WAVE];     // tree level buffer, then the totals
+    constexpr int WAVES = 8, SPW = (SLOTS + WAVES - 1) / WAVES;   // slots per wave
+    constexpr int MAX_SPLITS = 16;
+    __shared__ f32x4_t red[SLOTS * WAVE];                  // the totals; then the grouping's masks
     __shared__ uint64_t scratch[4][WAVE];
+    __shared__ int last[1];
+    __shared__ int sh[16];
     const int lane = threadIdx.x & (WAVE - 1);
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE);
     const int t0 = blk * 4;
     const int mf = t0 / 16, quad = (t0 % 16) / 4;
+    if (a.group && threadIdx.x == 0)   // the grouping's counter carries this call's epoch (early: off the critical path)
+        epoch_ensure(a.sync, a.seq);
 
     // expert e = lane + 64 j sits in partial tile e / 16 = lane / 16 + 4 j at column e % 16 = lane % 16
     const float *base = a.src + (int64_t)(lane / 16) * SKINNY_TILE_FLOATS + (mf * WAVE + quad * 16 + lane % 16) * 4;
-    auto slot = [&](int s, int j) {
-        f32x4_t v = {0.f, 0.f, 0.f, 0.f};
-        if (lane + WAVE * j < a.E)
-            v = *reinterpret_cast<const f32x4_t *>(base + s * a.split_stride + (int64_t)j * 4 * SKINNY_TILE_FLOATS);
-        return v;
-    };
-    f32x4_t acc[SLOTS];
 #pragma unroll
-    for (int j = 0; j < SLOTS; j++)
-        acc[j] = wv < a.splits ? slot(wv, j) : f32x4_t{0.f, 0.f, 0.f, 0.f};
-    for (int s = wv + WAVES; s < a.splits; s += WAVES)
+    for (int u = 0; u < SPW; u++) {
+        const int j = wv + WAVES * u;
+        if (j < SLOTS) {
+            const bool valid = lane + WAVE * j < a.E;
+            f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+            for (int s0 = 0; s0 < a.splits; s0 += MAX_SPLITS) {   // one round for up to 16 splits
+                f32x4_t ld[MAX_SPLITS];
 #pragma unroll
-        for (int h = 0; h < 2; h++) {          // half the slots at a time (register budget)
-            f32x4_t ld[SLOTS / 2];
+                for (int s = 0; s < MAX_SPLITS; s++)
+                    ld[s] = valid && s0 + s < a.splits
+                                ? *reinterpret_cast<const f32x4_t *>(base + (s0 + s) * a.split_stride +
+                                                                     (int64_t)j * 4 * SKINNY_TILE_FLOATS)
+                                : f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int j = 0; j < SLOTS / 2; j++)
-                ld[j] = slot(s, h * (SLOTS / 2) + j);
-#pragma unroll
-            for (int j = 0; j < SLOTS / 2; j++)
-                acc[h * (SLOTS / 2) + j] += ld[j];
+                for (int s = 0; s < MAX_SPLITS; s++)
+                    if (s0 + s < a.splits)
+                        acc += ld[s];
+            }
+            red[j * WAVE + lane] = acc;
         }
-#pragma unroll
-    for (int half = WAVES / 2; half >= 1; half /= 2) {
-        if (wv >= half && wv < 2 * half)
-#pragma unroll
-            for (int j = 0; j < SLOTS; j++)
-                red[((wv - half) * SLOTS + j) * WAVE + lane] = acc[j];
-        __syncthreads();
-        if (wv < half)
-#pragma unroll
-            for (int j = 0; j < SLOTS; j++)
-                acc[j] += red[(wv * SLOTS + j) * WAVE + lane];
-        __syncthreads();
     }
-    if (wv == 0)
-#pragma unroll
-        for (int j = 0; j < SLOTS; j++)
-            red[j * WAVE + lane] = acc[j];
     __syncthreads();
 
     const int t = t0 + wv;
-    if (wv >= 4 || t >= a.T)
-        return;
-    float v[SLOTS];
+    if (wv < 4 && t < a.T) {
+        float v[SLOTS];
 #pragma unroll
-    for (int j = 0; j < SLOTS; j++)
-        v[j] = red[j * WAVE + lane][wv];
-    uint32_t key[SLOTS];
-    token_keys<SLOTS>(a, t, v, key);
-    select_keys<SLOTS>(a, t, key, scratch[wv]);
+        for (int j = 0; j < SLOTS; j++)
+            v[j] = red[j * WAVE + lane][wv];
+        uint32_t key[SLOTS];
+        token_keys<SLOTS>(a, t, v, key);
+        select_keys<SLOTS>(a, t, key, scratch[wv]);
+    }
+    if (!a.group)
+        return;
+    // The workgroup's ids stores have completed (each wave waits for its own) before one thread
+    // signals; the workgroup that signals last groups every pair, reusing the totals buffer.
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    asm volatile("" ::: "memory");
+    __syncthreads();
+    if (threadIdx.x == 0)
+        last[0] = epoch_arrive(a.sync) == gridDim_topk(a) - 1;
+    __syncthreads();
+    if (last[0])
+        group_pairs(a, reinterpret_cast<uint32_t *>(red), sh);
 }
 
 template <int SLOTS>
@@ -226,9 +302,19 @@ __global__ __launch_bounds__(512) void topk_xside_kernel(const TopkArgs a, const
         xside_epi_item(e, (int64_t)(blockIdx.x - ntopk) * blockDim.x + threadIdx.x);
 }
 
+static bool group_args_ok(const TopkArgs &a)
+{
+    if (!a.group)
+        return true;
+    // the masks (E x ceil(T / 32) words) and offsets (E + 1) reuse the top-K reduction buffer of at
+    // least 64 E bytes, which holds them for T <= SKINNY_MAX_M
+    return a.sync && a.counts && a.offsets && a.sorted_pairs && a.inv && a.T <= SKINNY_MAX_M &&
+           (int64_t)a.T * a.K <= 4 * 512 && (!a.tiles || a.bm >= 1);
+}
+
 hipError_t launch_topk_xside(const TopkArgs &a, const XsideEpiArgs &e, hipStream_t st)
 {
-    if (!a.partials || a.T > SKINNY_MAX_M || a.K > WAVE || a.E > 16 * WAVE || e.tiles)
+    if (!a.partials || a.T > SKINNY_MAX_M || a.K > WAVE || a.E > 16 * WAVE || e.tiles || !group_args_ok(a))
         return hipErrorInvalidValue;
     const int ntopk = (a.T + 3) / 4;
     const int64_t items = (int64_t)(e.Lt / 16 + e.shared_cols / 32) * 4 * WAVE;
@@ -246,7 +332,8 @@ hipError_t launch_topk_xside(const TopkArgs &a, const XsideEpiArgs &e, hipStream
 hipError_t launch_topk(const TopkArgs &a, hipStream_t st)
 {
     const dim3 grid((a.T + 3) / 4);
-    if (a.K > WAVE || a.E > 16 * WAVE || (a.partials && a.T > SKINNY_MAX_M))
+    if (a.K > WAVE || a.E > 16 * WAVE || (a.partials && a.T > SKINNY_MAX_M) || (a.group && !a.partials) ||
+        !group_args_ok(a))
         return hipErrorInvalidValue;
     const int slots = (a.E + WAVE - 1) / WAVE;
     if (a.partials) {

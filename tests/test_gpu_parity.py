@@ -23,10 +23,14 @@ NOLAT = LayerShape("nolat", 77, 512, 512, 32, 4, 256, 0, 0, False, "uniform", 0.
 # the dense and the grouped products, with ragged row tiles and empty experts.
 PREFILL_SMALL = LayerShape("prefill_small", 300, 1024, 512, 16, 4, 256, 1, 128, True, "zipf", 0.0, 12)
 NOLAT_TILED = LayerShape("nolat_tiled", 260, 384, 384, 8, 3, 384, 0, 0, False, "uniform", 0.0, 13)
+# Many rows per expert at 2I = 768 (three 256-column tiles per row tile on the tiled kernel),
+# Zipf-skewed, with ragged prefixes.
+PREFILL_GLU = LayerShape("prefill_glu", 300, 1024, 512, 16, 4, 384, 1, 128, True, "zipf", 0.0, 15)
 # One or two rows per expert (24 * 4 / 128 < 1): the decode expert kernels with 4-row tiles and the
 # activations staged in LDS.
 SPARSE = LayerShape("sparse", 24, 1024, 512, 128, 4, 256, 1, 128, True, "uniform", 0.0, 14)
-SMALL_SHAPES = {s.name: s for s in (SHAPES["tiny"], MID, MID_ZIPF, NOLAT, PREFILL_SMALL, NOLAT_TILED, SPARSE)}
+SMALL_SHAPES = {s.name: s for s in (SHAPES["tiny"], MID, MID_ZIPF, NOLAT, PREFILL_SMALL, NOLAT_TILED, SPARSE,
+                                     PREFILL_GLU)}
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -103,6 +107,15 @@ def test_deterministic_and_token_permutation_invariant(name):
 @pytest.mark.parametrize("T", [1, 2, 15, 17, 33])
 def test_ragged_token_counts(T):
     shape, inp, layer = _setup("mid")
+    sub = dict(inp, x=inp["x"][:T])
+    run = G.GpuRun(layer, shape, sub)
+    G.check_forward(replace(shape, T=T), sub, run)
+
+
+@pytest.mark.parametrize("T", [257, 283])
+def test_tiled_expert_paths_768_ragged(T):
+    """Prefixes of prefill_glu (2I = 768) on the tiled expert path, every token compared."""
+    shape, inp, layer = _setup("prefill_glu")
     sub = dict(inp, x=inp["x"][:T])
     run = G.GpuRun(layer, shape, sub)
     G.check_forward(replace(shape, T=T), sub, run)

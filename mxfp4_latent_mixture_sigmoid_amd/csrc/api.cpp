@@ -53,16 +53,6 @@ constexpr int XSIDE_GROUPS = 18, OUT_GROUPS = 28;
 // ... and of the combined router + x-side product (6016 columns at the full size)
 constexpr int RX_GROUPS = 18;
 
-// Sequence number of a call: the epoch of the in-kernel counters it uses (sync.hpp). Unique within
-// the process, and started from the clock so that a counter left in reused memory by an earlier
-// process is unlikely to carry a current epoch.
-uint64_t initial_seq()
-{
-    const uint64_t t = (uint64_t)std::chrono::steady_clock::now().time_since_epoch().count();
-    return (t >> 8) & ((1ull << 40) - 1);
-}
-std::atomic<uint64_t> call_seq{initial_seq()};
-uint64_t next_seq() { return call_seq.fetch_add(1) & ((1ull << (64 - EPOCH_SHIFT)) - 1); }
 // Router rows in the combined router + x-side matrix: a multiple of the 64-column wave width, so
 // that no wave of the many-token product straddles the logits and the z columns.
 int64_t router_rows_rx(const moe_config *c) { return ((int64_t)c->n_experts + 63) / 64 * 64; }
@@ -144,7 +134,7 @@ PackedLayout packed_layout(const moe_config *c)
 
 struct WsLayout {
     int64_t logits, hist, tiles, z, acat, h, y, h8, z4, partials, total;
-    int64_t sync;                       // epoch counter of the top-K launch's grouping (T <= SKINNY_MAX_M)
+    int64_t sync;                       // arrival counter of the few-token top-K launch (T <= SKINNY_MAX_M)
     int64_t rpartials;                  // router partials (inside the partials region, before the dense ones)
     int64_t max_tiles;                  // capacity of the expert tile list (shared by both expert products)
 };
@@ -521,8 +511,7 @@ namespace {
 
 // The grouping by expert runs inside the top-K launch (few tokens, logits from split-K partials):
 // the last top-K workgroup writes the routing arrays, and the tile list when `tiles` is set.
-void set_grouping(TopkArgs &ta, const moe_routing *r, const WsLayout &W, uint8_t *ws, int32_t *tiles, int bm,
-                  uint64_t seq)
+void set_grouping(TopkArgs &ta, const moe_routing *r, const WsLayout &W, uint8_t *ws, int32_t *tiles, int bm)
 {
     ta.group = 1;
     ta.counts = r->counts;
@@ -531,14 +520,13 @@ void set_grouping(TopkArgs &ta, const moe_routing *r, const WsLayout &W, uint8_t
     ta.inv = r->inv;
     ta.tiles = tiles;
     ta.bm = bm;
-    ta.sync = reinterpret_cast<uint64_t *>(ws + W.sync);
-    ta.seq = seq;
+    ta.arrivals = reinterpret_cast<uint32_t *>(ws + W.sync);
 }
 
 // Router product (logits, or split-K partials for few tokens); fills the top-K arguments.
 moe_status router_impl(moe_handle *h, const void *x, int32_t T, const float *logit_bias, const float *logits_in,
                        float *logits_out, const moe_routing *r, const WsLayout &W, uint8_t *ws, hipStream_t st,
-                       uint64_t seq, TopkArgs &ta)
+                       TopkArgs &ta)
 {
     const moe_config *c = &h->cfg;
     const int E = c->n_experts, K = c->top_k;
@@ -555,8 +543,9 @@ moe_status router_impl(moe_handle *h, const void *x, int32_t T, const float *log
     } else if (T <= SKINNY_MAX_M) {   // few tokens: split-K partials, summed (+bias) by the top-K kernel
         float *partials = reinterpret_cast<float *>(ws + W.rpartials);
         const int64_t pstride = (int64_t)(h->E_pad / 16) * SKINNY_TILE_FLOATS;
+        // the product also clears the arrival counter of the top-K launch after it
         SkinnyArgs g{static_cast<const uint16_t *>(x), h->Hin, T, h->packed + h->off_router, h->E_pad, h->Hin,
-                     partials, pstride};
+                     partials, pstride, reinterpret_cast<uint32_t *>(ws + W.sync)};
         MOE_LAUNCH(MOE_KERNEL_ROUTER, launch_skinny(g, 4, SKINNY_STEPS, st));
         ta.src = partials;
         ta.partials = 1;
@@ -564,7 +553,7 @@ moe_status router_impl(moe_handle *h, const void *x, int32_t T, const float *log
         ta.splits = skinny_splits(h->Hin, SKINNY_STEPS);
         ta.bias = logit_bias;
         ta.logits_out = logits_out;
-        set_grouping(ta, r, W, ws, nullptr, 0, seq);
+        set_grouping(ta, r, W, ws, nullptr, 0);
     } else {
         float *lg = logits_out ? logits_out : reinterpret_cast<float *>(ws + W.logits);
         GemmArgs g{};
@@ -663,7 +652,7 @@ moe_status xside_impl(moe_handle *h, const void *x, int32_t T, const moe_routing
 // tile lists.
 // Every output element is computed in the same order as by the separate products.
 moe_status front_impl(moe_handle *h, const void *x, int32_t T, const float *logit_bias, float *logits_out,
-                      const moe_routing *r, const WsLayout &W, uint8_t *ws, hipStream_t st, uint64_t seq)
+                      const moe_routing *r, const WsLayout &W, uint8_t *ws, hipStream_t st)
 {
     const moe_config *c = &h->cfg;
     const int E = c->n_experts, K = c->top_k, Lt = c->latent, H = c->hidden;
@@ -685,7 +674,9 @@ moe_status front_impl(moe_handle *h, const void *x, int32_t T, const float *logi
         float *P = reinterpret_cast<float *>(ws + W.rpartials);
         const int64_t pstride = (int64_t)(Nrx / 16) * SKINNY_TILE_FLOATS;
         const int splits = skinny_splits(H, SKINNY_XSTEPS);
-        SkinnyArgs g{static_cast<const uint16_t *>(x), H, T, h->packed + h->off_rx, Nrx, H, P, pstride};
+        // the product also clears the arrival counter of the top-K launch after it
+        SkinnyArgs g{static_cast<const uint16_t *>(x), H, T, h->packed + h->off_rx, Nrx, H, P, pstride,
+                     reinterpret_cast<uint32_t *>(ws + W.sync)};
         MOE_LAUNCH(MOE_KERNEL_ROUTER_XSIDE, launch_skinny_persist(g, 8, RX_GROUPS, SKINNY_XSTEPS, st));
         ta.src = P;
         ta.partials = 1;
@@ -694,7 +685,7 @@ moe_status front_impl(moe_handle *h, const void *x, int32_t T, const float *logi
         ta.bias = logit_bias;
         ta.logits_out = logits_out;
         // top-K (with the grouping and the tile lists) and the x-side epilogue in one launch
-        set_grouping(ta, r, W, ws, reinterpret_cast<int32_t *>(ws + W.tiles), bm, seq);
+        set_grouping(ta, r, W, ws, reinterpret_cast<int32_t *>(ws + W.tiles), bm);
         XsideEpiArgs ea{P + (int64_t)(Erx / 16) * SKINNY_TILE_FLOATS, pstride, splits, T, Nx, Lt, 2 * S * Is, Z,
                         Acat, ldcat, nullptr, E, bm, nullptr};
         MOE_LAUNCH(MOE_KERNEL_TOPK, launch_topk_xside(ta, ea, st));
@@ -858,7 +849,7 @@ moe_status moe_route(moe_handle *h, const void *x, int32_t T, const float *logit
     uint8_t *ws = static_cast<uint8_t *>(workspace);
     hipStream_t st = static_cast<hipStream_t>(stream);
     TopkArgs ta;
-    if ((e = router_impl(h, x, T, logit_bias, logits_in, logits_out, r, W, ws, st, next_seq(), ta)) != MOE_OK)
+    if ((e = router_impl(h, x, T, logit_bias, logits_in, logits_out, r, W, ws, st, ta)) != MOE_OK)
         return e;
     return select_impl(h, T, ta, r, W, ws, st, false);
 }
@@ -901,12 +892,11 @@ moe_status route_forward_impl(moe_handle *h, const void *x, int32_t T, const flo
                               const moe_routing *r, void *out, const WsLayout &W, uint8_t *ws, hipStream_t st)
 {
     moe_status e;
-    const uint64_t seq = next_seq();
     if (h->cfg.has_latent_proj)
-        e = front_impl(h, x, T, logit_bias, logits_out, r, W, ws, st, seq);
+        e = front_impl(h, x, T, logit_bias, logits_out, r, W, ws, st);
     else {   // no x-side products: router, then the grouping builds the tile lists
         TopkArgs ta;
-        e = router_impl(h, x, T, logit_bias, nullptr, logits_out, r, W, ws, st, seq, ta);
+        e = router_impl(h, x, T, logit_bias, nullptr, logits_out, r, W, ws, st, ta);
         if (e == MOE_OK)
             e = select_impl(h, T, ta, r, W, ws, st, true);
     }

@@ -137,6 +137,7 @@ struct SkinnyArgs {
     int N, K;
     float *P;            // partials, split s at P + s * p_split_stride (>= N / 16 * SKINNY_TILE_FLOATS)
     int64_t p_split_stride;
+    uint32_t *zero_word; // nullable: set to 0 by the launch (the arrival counter of the launch after it)
 };
 int skinny_splits(int K, int chunk_steps);
 hipError_t launch_skinny(const SkinnyArgs &g, int waves, int chunk_steps, hipStream_t st);
@@ -172,12 +173,11 @@ struct TopkArgs {
     float *w;
     // Grouping inside the top-K launch (partials path, T <= PERM_SMALL_MAX_T): the last top-K
     // workgroup to finish writes counts / offsets / sorted_pairs / inv (and the tile list of bm rows
-    // when `tiles` is set) from the ids, handed over as agent-coherent stores and an epoch counter.
+    // when `tiles` is set) from the ids, handed over as agent-coherent stores and an arrival counter.
     int group;
     int32_t *counts, *offsets, *sorted_pairs, *inv, *tiles;
     int bm;
-    uint64_t *sync;   // one epoch counter
-    uint64_t seq;     // the call's sequence number
+    uint32_t *arrivals;   // zero when the launch starts (cleared by the product launch before it)
 };
 constexpr int PERM_TOKENS_PER_BLOCK = 32;
 constexpr int PERM_SMALL_MAX_T = 256;

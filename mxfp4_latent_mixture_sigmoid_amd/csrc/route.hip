@@ -46,7 +46,7 @@ __device__ inline void token_keys(const TopkArgs &a, int t, float *v, uint32_t *
 //  1. bound: the K-th largest of the 64 lane maxima (keys only), built bit by bit from the top with
 //     one ballot per bit. At least K lanes hold a key >= bound, so every selected key is >= bound.
 //  2. The candidates (keys >= bound; K or a few more in practice) are gathered into `scratch` (64
-//     entries of this wave); each ranks itself against all of them by broadcast reads, and the K
+//     entries of this wave); each ranks itself against all of them by lane broadcasts, and the K
 //     best are placed at their ranks, so lane k then holds the rank-k expert.
 //  3. With more than 64 candidates (heavy ties), K rounds of wave-wide maxima select directly.
 template <int SLOTS>
@@ -82,9 +82,12 @@ __device__ inline void select_keys(const TopkArgs &a, int t, const uint32_t *key
             if (key[j] != 0u && key[j] >= bound)
                 scratch[pos++] = c[j];
         const uint64_t mine = lane < total ? scratch[lane] : 0;
+        const uint32_t mh = (uint32_t)(mine >> 32), ml = (uint32_t)mine;
         int rank = 0;
-        for (int m = 0; m < total; m++)
-            rank += scratch[m] > mine ? 1 : 0;
+        for (int m = 0; m < total; m++) {   // candidate m broadcast from its lane
+            const uint32_t oh = __builtin_amdgcn_readlane(mh, m), ol = __builtin_amdgcn_readlane(ml, m);
+            rank += (oh > mh || (oh == mh && ol > ml)) ? 1 : 0;
+        }
         if (lane < total && rank < K)
             scratch[rank] = mine;
         const uint64_t r = lane < K ? scratch[lane] : 0;
@@ -223,7 +226,7 @@ __device__ inline void topk_wide_block(const TopkArgs &a, int blk)
 {
     constexpr int WAVES = 8, SPW = (SLOTS + WAVES - 1) / WAVES;   // slots per wave
     constexpr int MAX_SPLITS = 16;
-    __shared__ f32x4_t red[SLOTS * WAVE];                  // the totals; then the grouping's masks
+    __shared__ float red[4 * SLOTS * WAVE];                // the totals [token][slot][lane]; then the grouping's masks
     __shared__ uint64_t scratch[4][WAVE];
     __shared__ int last[1];
     __shared__ int sh[16];
@@ -231,31 +234,48 @@ __device__ inline void topk_wide_block(const TopkArgs &a, int blk)
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE);
     const int t0 = blk * 4;
     const int mf = t0 / 16, quad = (t0 % 16) / 4;
-    if (a.group && threadIdx.x == 0)   // the grouping's counter carries this call's epoch (early: off the critical path)
-        epoch_ensure(a.sync, a.seq);
 
     // expert e = lane + 64 j sits in partial tile e / 16 = lane / 16 + 4 j at column e % 16 = lane % 16
     const float *base = a.src + (int64_t)(lane / 16) * SKINNY_TILE_FLOATS + (mf * WAVE + quad * 16 + lane % 16) * 4;
+    // The loads of both slots over (up to 16) splits, and the slots' bias, are all issued before any
+    // is used: one memory round trip. Sums run in split order; the bias is added to the total.
+    f32x4_t acc[SPW];
+    float bias[SPW];
+#pragma unroll
+    for (int u = 0; u < SPW; u++) {
+        const int j = wv + WAVES * u, e = lane + WAVE * j;
+        acc[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        bias[u] = a.bias && j < SLOTS && e < a.E ? a.bias[e] : 0.f;
+    }
+    for (int s0 = 0; s0 < a.splits; s0 += MAX_SPLITS) {   // one round for up to 16 splits
+        f32x4_t ld[SPW][MAX_SPLITS];
+#pragma unroll
+        for (int u = 0; u < SPW; u++) {
+            const int j = wv + WAVES * u;
+            const bool valid = j < SLOTS && lane + WAVE * j < a.E;
+#pragma unroll
+            for (int s = 0; s < MAX_SPLITS; s++)
+                ld[u][s] = valid && s0 + s < a.splits
+                               ? *reinterpret_cast<const f32x4_t *>(base + (s0 + s) * a.split_stride +
+                                                                    (int64_t)j * 4 * SKINNY_TILE_FLOATS)
+                               : f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int u = 0; u < SPW; u++)
+#pragma unroll
+            for (int s = 0; s < MAX_SPLITS; s++)
+                if (s0 + s < a.splits)
+                    acc[u] += ld[u][s];
+    }
 #pragma unroll
     for (int u = 0; u < SPW; u++) {
         const int j = wv + WAVES * u;
         if (j < SLOTS) {
-            const bool valid = lane + WAVE * j < a.E;
-            f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-            for (int s0 = 0; s0 < a.splits; s0 += MAX_SPLITS) {   // one round for up to 16 splits
-                f32x4_t ld[MAX_SPLITS];
+            if (a.bias)
+                acc[u] += f32x4_t{bias[u], bias[u], bias[u], bias[u]};
 #pragma unroll
-                for (int s = 0; s < MAX_SPLITS; s++)
-                    ld[s] = valid && s0 + s < a.splits
-                                ? *reinterpret_cast<const f32x4_t *>(base + (s0 + s) * a.split_stride +
-                                                                     (int64_t)j * 4 * SKINNY_TILE_FLOATS)
-                                : f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int s = 0; s < MAX_SPLITS; s++)
-                    if (s0 + s < a.splits)
-                        acc += ld[s];
-            }
-            red[j * WAVE + lane] = acc;
+            for (int i = 0; i < 4; i++)
+                red[(i * SLOTS + j) * WAVE + lane] = acc[u][i];
         }
     }
     __syncthreads();
@@ -265,9 +285,11 @@ __device__ inline void topk_wide_block(const TopkArgs &a, int blk)
         float v[SLOTS];
 #pragma unroll
         for (int j = 0; j < SLOTS; j++)
-            v[j] = red[j * WAVE + lane][wv];
+            v[j] = red[(wv * SLOTS + j) * WAVE + lane];
         uint32_t key[SLOTS];
-        token_keys<SLOTS>(a, t, v, key);
+        TopkArgs nb = a;   // the totals already hold the bias
+        nb.bias = nullptr;
+        token_keys<SLOTS>(nb, t, v, key);
         select_keys<SLOTS>(a, t, key, scratch[wv]);
     }
     if (!a.group)
@@ -278,7 +300,8 @@ __device__ inline void topk_wide_block(const TopkArgs &a, int blk)
     asm volatile("" ::: "memory");
     __syncthreads();
     if (threadIdx.x == 0)
-        last[0] = epoch_arrive(a.sync) == gridDim_topk(a) - 1;
+        last[0] = (int)__hip_atomic_fetch_add(a.arrivals, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                  gridDim_topk(a) - 1;
     __syncthreads();
     if (last[0])
         group_pairs(a, reinterpret_cast<uint32_t *>(red), sh);
@@ -308,7 +331,7 @@ static bool group_args_ok(const TopkArgs &a)
         return true;
     // the masks (E x ceil(T / 32) words) and offsets (E + 1) reuse the top-K reduction buffer of at
     // least 64 E bytes, which holds them for T <= SKINNY_MAX_M
-    return a.sync && a.counts && a.offsets && a.sorted_pairs && a.inv && a.T <= SKINNY_MAX_M &&
+    return a.arrivals && a.counts && a.offsets && a.sorted_pairs && a.inv && a.T <= SKINNY_MAX_M &&
            (int64_t)a.T * a.K <= 4 * 512 && (!a.tiles || a.bm >= 1);
 }
 

@@ -26,6 +26,8 @@ __global__ __launch_bounds__(WAVE *WAVES) void skinny_kernel(const SkinnyArgs g)
 {
     extern __shared__ u32x4_t lds_a[];   // [nsteps][4 fragments][64 lanes]
     const int lane = threadIdx.x & (WAVE - 1), wv = threadIdx.x / WAVE;
+    if (g.zero_word && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0)
+        *g.zero_word = 0u;
     const int split = blockIdx.y;
     const int kc0 = split * SK_MAX_STEPS * BF16_STEP;
     const int nsteps = min(SK_MAX_STEPS * BF16_STEP, g.K - kc0) / BF16_STEP;
@@ -108,6 +110,8 @@ __global__ __launch_bounds__(WAVE *WAVES) void skinny_persist_kernel(const Skinn
     constexpr int STEPS = 16, CSTEPS = STEPS * UNITS;
     __shared__ u32x4_t lds_a[CSTEPS * 4 * WAVE];   // [steps][4 fragments][64 lanes]
     const int lane = threadIdx.x & (WAVE - 1);
+    if (g.zero_word && blockIdx.x == 0 && threadIdx.x == 0)
+        *g.zero_word = 0u;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE);
     const int split = blockIdx.x % splits, grp = blockIdx.x / splits;
     const int groups = gridDim.x / splits;

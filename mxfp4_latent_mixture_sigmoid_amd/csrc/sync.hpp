@@ -7,39 +7,16 @@
 // agent-coherent accesses instead -- stores and loads with the sc1 cache policy, the same
 // instructions the compiler emits for agent-scope relaxed atomic stores and loads -- and the
 // writer waits for its stores to complete (s_waitcnt) before it signals on a counter; the reader
-// issues its loads only after its counter access has returned.
-//
-// Counters are 64-bit epoch counters, (sequence number << EPOCH_SHIFT) | count. The host passes a
-// sequence number unique to the call; a counter left by an earlier call (or never initialised)
-// carries another epoch and is moved to (seq, 0) by the first wave that sees it, so the workspace
-// needs no clearing between calls and no launch is spent on it.
+// issues its loads only after its counter access has returned. A counter is a plain 32-bit word
+// that the launch before the one using it sets to zero, so a kernel boundary orders the clearing
+// before every arrival and no workspace clearing launch is needed.
 #pragma once
 
 #include "common.hpp"
 
 namespace mxmoe {
 
-constexpr int EPOCH_SHIFT = 20;                       // count: low 20 bits
-constexpr uint64_t EPOCH_COUNT_MASK = (1ull << EPOCH_SHIFT) - 1;
-constexpr int CPOL_SC1 = 16;                          // agent-coherent access (sc1)
-
-// Make counter c carry epoch seq (count 0) unless it already does. Every wave calls this for each
-// counter before its first arrival there; a compare-and-swap from a stale value can only succeed
-// before any arrival of this epoch, so no arrival is lost.
-__device__ inline void epoch_ensure(uint64_t *c, uint64_t seq)
-{
-    uint64_t v = __hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if ((v >> EPOCH_SHIFT) != seq)
-        (void)__hip_atomic_compare_exchange_strong(c, &v, seq << EPOCH_SHIFT, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                                   __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// One arrival at counter c (already in the call's epoch); returns the number of earlier arrivals.
-__device__ inline int epoch_arrive(uint64_t *c)
-{
-    const uint64_t old = __hip_atomic_fetch_add(c, (uint64_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    return (int)(old & EPOCH_COUNT_MASK);
-}
+constexpr int CPOL_SC1 = 16;   // agent-coherent access (sc1)
 
 // Raw buffer resource over [base, base + bytes) (bytes < 2^31).
 __device__ inline __amdgpu_buffer_rsrc_t flat_rsrc(const void *base, int64_t bytes)

@@ -151,6 +151,10 @@ class Leg:
     def step(self):
         self.layer.route_forward(self.x, self.shape.T, self.routing, out=self.out, logit_bias=self.bias)
 
+    def make_graph(self):
+        """The step captured as one HIP graph on this leg's buffers (moe_graph_create)."""
+        return self.layer.graph(self.x, self.shape.T, self.routing, self.out, logit_bias=self.bias)
+
     def step_separate(self):
         self.layer.route(self.x, self.shape.T, self.routing, logit_bias=self.bias)
         self.layer.forward(self.x, self.shape.T, self.routing, out=self.out)
@@ -367,6 +371,14 @@ def main() -> int:
         main_leg.step_separate()
     ms_separate, _ = main_leg.timed(args.steps, main_leg.step_separate)
 
+    # The same step replayed from one captured HIP graph (moe_graph_create / moe_graph_launch).
+    graph = main_leg.make_graph()
+    for _ in range(min(args.warmup, 5)):
+        graph.launch()
+    ms_graph, gpu_ms_graph = main_leg.timed(args.steps, graph.launch)
+    graph.close()
+    log(f"graph replay: {ms_graph:.4f} ms/step")
+
     kernels_us = main_leg.kernels_us(args.steps)
     n_active = main_leg.n_active()
     roof = main_leg.roofline(kernels_us, n_active)
@@ -415,6 +427,8 @@ def main() -> int:
         "step_ms_percentiles": step_pct,
         "step_ms_percentiles_cache_flushed": flushed_pct,
         "ms_per_step_route_then_forward": round(ms_separate, 5),
+        "ms_per_step_graph": round(ms_graph, 5),
+        "gpu_ms_per_step_graph": round(gpu_ms_graph, 5),
         "step_hbm_gbps": round(alg["step_bytes"] / step_s / 1e9, 1),
         "step_tflops": round(alg["step_flops"] / step_s / 1e12, 2),
         # the whole step against both roofs (the full unsharded experts sit at the ridge between them)

@@ -196,6 +196,27 @@ moe_status moe_route_forward(moe_handle *h, const void *x, int32_t T, const floa
 moe_status moe_route_forward_static(moe_handle *h, const void *x, int32_t T, const float *logit_bias,
                                     float *logits_out, const moe_routing *r, void *out, void *stream);
 
+/* The whole few-token step as one HIP graph (the fused decode step: route, grouping, expert
+ * products, combine and shared experts replayed as a unit; page "Kimi K3.1 Pro on AMD Instinct
+ * GPUs", sections "Serving with ATOM / What we optimized", paragraph "Mono decode", and "Serving
+ * with vLLM / What we optimized", paragraph on fused low-latency decode).
+ * moe_graph_create captures moe_route_forward's launches for these exact arguments into an
+ * executable graph: the graph keeps the pointers (x, logit_bias, logits_out, every array of r,
+ * out, workspace), so the caller writes each step's tokens into the same x buffer and keeps every
+ * buffer alive and unmoved until moe_graph_destroy. Capture runs on a stream of the library's own
+ * and enqueues no work; it returns MOE_ERR_INVALID_ARG for T = 0, for arguments moe_route_forward
+ * would reject, and while the profiling hook is active on h. The graph holds no memset node.
+ * moe_graph_launch enqueues one replay on `stream` (allocating nothing): results are identical
+ * bit for bit to moe_route_forward on the buffers' contents at that point of the stream. Replays
+ * that overlap (several streams) race on the workspace like overlapping calls. */
+typedef struct moe_graph moe_graph;
+moe_status moe_graph_create(moe_handle *h, const void *x, int32_t T, const float *logit_bias,
+                            float *logits_out, const moe_routing *r, void *out, void *workspace,
+                            size_t workspace_bytes, moe_graph **g);
+moe_status moe_graph_launch(moe_graph *g, void *stream);
+/* Free the graph (its host and driver objects; no buffer it refers to). NULL is a no-op. */
+void moe_graph_destroy(moe_graph *g);
+
 /* Test hook: dequantise expert e's packed matrix `which` (0 gate [I, Lt], 1 up [I, Lt],
  * 2 down [Lt, I]) back to canonical row-major BF16 in `out` through the same in-register
  * E2M1/E8M0 conversion the expert GEMMs use. */

@@ -66,6 +66,10 @@ SIGNATURES = {
     "moe_route_forward": (c_i32, [c_vp, c_vp, c_i32, c_vp, c_vp, ctypes.POINTER(MoeRouting), c_vp, c_vp, c_size,
                                   c_vp]),
     "moe_route_forward_static": (c_i32, [c_vp, c_vp, c_i32, c_vp, c_vp, ctypes.POINTER(MoeRouting), c_vp, c_vp]),
+    "moe_graph_create": (c_i32, [c_vp, c_vp, c_i32, c_vp, c_vp, ctypes.POINTER(MoeRouting), c_vp, c_vp, c_size,
+                                 ctypes.POINTER(c_vp)]),
+    "moe_graph_launch": (c_i32, [c_vp, c_vp]),
+    "moe_graph_destroy": (None, [c_vp]),
     "moe_unpack_expert": (c_i32, [c_vp, c_i32, c_i32, c_vp, c_vp]),
     "moe_profile_begin": (c_i32, [c_vp, c_i32]),
     "moe_profile_end": (c_i32, [c_vp, ctypes.POINTER(c_i32), ctypes.POINTER(ctypes.c_float), ctypes.POINTER(c_i32)]),
@@ -176,6 +180,23 @@ def route_forward_static(h, x, T, routing: dict, out, logit_bias=None, logits_ou
     rs = routing_struct(routing)
     check(lib().moe_route_forward_static(h, ptr(x), T, ptr(logit_bias), ptr(logits_out), ctypes.byref(rs), ptr(out),
                                          stream_handle(stream)), "moe_route_forward_static")
+
+
+def graph_create(h, x, T, routing: dict, out, workspace, logit_bias=None, logits_out=None):
+    """moe_graph_create: moe_route_forward captured for these buffers; returns the graph handle."""
+    rs = routing_struct(routing)
+    g = c_vp()
+    check(lib().moe_graph_create(h, ptr(x), T, ptr(logit_bias), ptr(logits_out), ctypes.byref(rs), ptr(out),
+                                 ptr(workspace), workspace.numel(), ctypes.byref(g)), "moe_graph_create")
+    return g
+
+
+def graph_launch(g, stream=None) -> None:
+    check(lib().moe_graph_launch(g, stream_handle(stream)), "moe_graph_launch")
+
+
+def graph_destroy(g) -> None:
+    lib().moe_graph_destroy(g)
 
 
 def unpack_expert(h, e: int, which: int, out, stream=None) -> None:

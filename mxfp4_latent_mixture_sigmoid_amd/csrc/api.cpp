@@ -2,14 +2,11 @@
 // layouts, and the launch sequence of moe_route / moe_forward on the caller's stream.
 #include "kernels.hpp"
 #include "mxmoe.h"
-#include "sync.hpp"
 
 #include <climits>
 #include <cstdlib>
 #include <new>
 #include <algorithm>
-#include <atomic>
-#include <chrono>
 #include <mutex>
 #include <vector>
 
@@ -938,6 +935,68 @@ moe_status moe_route_forward_static(moe_handle *h, const void *x, int32_t T, con
     // earlier in the same call
     return route_forward_impl(h, x, T, logit_bias, logits_out, r, out, W, static_cast<uint8_t *>(ws),
                               static_cast<hipStream_t>(stream));
+}
+
+struct moe_graph {
+    hipGraphExec_t exec;
+};
+
+moe_status moe_graph_create(moe_handle *h, const void *x, int32_t T, const float *logit_bias, float *logits_out,
+                            const moe_routing *r, void *out, void *workspace, size_t workspace_bytes, moe_graph **g)
+{
+    if (!g)
+        return MOE_ERR_INVALID_ARG;
+    *g = nullptr;
+    moe_status e = check_route_forward_args(h, x, T, logit_bias, logits_out, r, out);
+    if (e != MOE_OK)
+        return e;
+    if (T == 0 || h->prof)
+        return MOE_ERR_INVALID_ARG;
+    const WsLayout W = ws_layout(&h->cfg, T);
+    if ((e = check_workspace(W, workspace, workspace_bytes)) != MOE_OK)
+        return e;
+    hipStream_t cs = nullptr;
+    if (hipStreamCreateWithFlags(&cs, hipStreamNonBlocking) != hipSuccess)
+        return MOE_ERR_HIP;
+    hipGraph_t graph = nullptr;
+    hipGraphExec_t exec = nullptr;
+    if (hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal) != hipSuccess) {
+        (void)hipStreamDestroy(cs);
+        return MOE_ERR_HIP;
+    }
+    e = route_forward_impl(h, x, T, logit_bias, logits_out, r, out, W, static_cast<uint8_t *>(workspace), cs);
+    const hipError_t ce = hipStreamEndCapture(cs, &graph);   // ends the capture whatever happened
+    if (e == MOE_OK && (ce != hipSuccess || !graph))
+        e = MOE_ERR_HIP;
+    if (e == MOE_OK && hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0) != hipSuccess)
+        e = MOE_ERR_HIP;
+    if (graph)
+        (void)hipGraphDestroy(graph);
+    (void)hipStreamDestroy(cs);
+    if (e != MOE_OK)
+        return e;
+    moe_graph *gr = new (std::nothrow) moe_graph{exec};
+    if (!gr) {
+        (void)hipGraphExecDestroy(exec);
+        return MOE_ERR_HIP;
+    }
+    *g = gr;
+    return MOE_OK;
+}
+
+moe_status moe_graph_launch(moe_graph *g, void *stream)
+{
+    if (!g)
+        return MOE_ERR_INVALID_ARG;
+    return hip_status(hipGraphLaunch(g->exec, static_cast<hipStream_t>(stream)));
+}
+
+void moe_graph_destroy(moe_graph *g)
+{
+    if (!g)
+        return;
+    (void)hipGraphExecDestroy(g->exec);
+    delete g;
 }
 
 moe_status moe_unpack_expert(moe_handle *h, int32_t e, int32_t which, void *out, void *stream)

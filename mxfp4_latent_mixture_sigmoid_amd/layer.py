@@ -72,6 +72,12 @@ class MoELayer:
         abi.route_forward_static(self.handle, x, T, routing, out, logit_bias, logits_out, stream)
         return out
 
+    def graph(self, x, T, routing, out, logit_bias=None, logits_out=None):
+        """route_forward captured as one HIP graph on these buffers (see StepGraph)."""
+        self._check_T(T)
+        return StepGraph(self, abi.graph_create(self.handle, x, T, routing, out, self.workspace, logit_bias,
+                                                logits_out), (x, routing, out, logit_bias, logits_out))
+
     def unpack_expert(self, e: int, which: int, stream=None):
         rows, cols = (self.cfg.inter, self.Lt) if which < 2 else (self.Lt, self.cfg.inter)
         out = torch.empty(rows, cols, dtype=torch.bfloat16, device=self.device)
@@ -91,6 +97,30 @@ class MoELayer:
         if self.handle:
             abi.destroy(self.handle)
             self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class StepGraph:
+    """One captured route_forward: launch() replays it on the buffers it was captured with (write
+    each step's tokens into the same x tensor). Holds references to those buffers and the layer."""
+
+    def __init__(self, layer, g, buffers):
+        self.layer, self.g, self.buffers = layer, g, buffers
+
+    def launch(self, stream=None):
+        if not self.g:
+            raise RuntimeError("graph destroyed")
+        abi.graph_launch(self.g, stream)
+
+    def close(self):
+        if self.g:
+            abi.graph_destroy(self.g)
+            self.g = None
 
     def __del__(self):
         try:

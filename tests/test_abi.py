@@ -89,6 +89,19 @@ def test_create_route_forward_reject_null_arguments_without_gpu_work():
     L.moe_destroy(None)
 
 
+def test_graph_entry_points_reject_bad_arguments_without_gpu_work():
+    L = abi.lib()
+    r = abi.MoeRouting()
+    g = ctypes.c_void_p(123)
+    assert L.moe_graph_create(None, None, 4, None, None, ctypes.byref(r), None, None, 0, ctypes.byref(g)) == \
+        abi.Status.INVALID_ARG
+    assert g.value is None                      # cleared before any check that fails
+    assert L.moe_graph_create(None, None, 4, None, None, ctypes.byref(r), None, None, 0, None) == \
+        abi.Status.INVALID_ARG
+    assert L.moe_graph_launch(None, None) == abi.Status.INVALID_ARG
+    L.moe_graph_destroy(None)
+
+
 def test_fp8_second_stage_sizes():
     """MOE_STAGE2_FP8 adds one MX8 copy of the down weights and the FP8 h (codes + scales)."""
     T, E, Lt, I, K = 64, 896, 3584, 384, 16

@@ -58,14 +58,23 @@ def source_hash(rel: str) -> str:
 
 
 def cpu_model() -> str:
+    """The host CPU as /proc/cpuinfo names it, with its family / model / stepping numbers (some hosts
+    report only a generic model name)."""
+    info = {}
     try:
         with open("/proc/cpuinfo") as f:
             for line in f:
-                if line.startswith("model name"):
-                    return line.split(":", 1)[1].strip()
+                if ":" in line:
+                    k, v = (x.strip() for x in line.split(":", 1))
+                    if k in ("model name", "cpu family", "model", "stepping") and k not in info:
+                        info[k] = v
+                if not line.strip() and info:
+                    break
     except OSError:
         pass
-    return "unknown"
+    name = info.get("model name", "unknown")
+    ids = ", ".join(f"{k} {info[k]}" for k in ("cpu family", "model", "stepping") if k in info)
+    return f"{name} ({ids})" if ids else name
 
 
 def algorithmic(shape, n_active: int) -> dict:

@@ -188,7 +188,11 @@ def check_routing_exact(run: GpuRun, E: int, K: int, logits_for_select: np.ndarr
     return ids_ref
 
 
-E2E_ULPS = 4            # end-to-end: elements past the max bound must be within this many ulps
+# End-to-end: an element past the max bound must be within this many BF16 ulps of the FP64 pipeline.
+# The HIP path rounds z, h, y, zc (and h_s) to BF16 where the oracle does too, but an FP32 sum that
+# lands next to a rounding boundary can round the other way and the flip propagates to the output;
+# over the whole GPU suite (every shape, both quantised stages) the worst such element is 2 ulps.
+E2E_ULPS = 2
 
 
 def assert_close_e2e(name: str, got, ref) -> dict:

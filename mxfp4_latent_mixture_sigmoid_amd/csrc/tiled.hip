@@ -101,20 +101,30 @@ __device__ __attribute__((always_inline)) inline void tiled_tile(const GemmArgs 
             lds[buf][((b / NMF) * TL_MFW + b % NMF) * WAVE + lane] = v[u];
         }
     };
-    // MXFP4 products stage A by direct global->LDS loads instead: one wave instruction fills one
-    // 1 KiB block (its LDS base is wave-uniform, lane l lands at slot l), with no register round
-    // trip. The compiler does not track these loads into LDS, so the stage loop waits for them
-    // itself (vmcnt) before the barrier that publishes the stage.
-    auto issue_a = [&](int stage, int buf) {
+    // MXFP4 products stage A by direct global->LDS loads instead, with no register round trip, and
+    // as whole 128-byte lines: a stage is 16 rows x 256 bytes per fragment (4 KiB, row r at
+    // 256 r), one wave instruction fills 4 rows of it (1 KiB: lane l takes row 4 q + l / 16 of
+    // the fragment, where q is the wave, and position l % 16 of that row). Position p of row r holds
+    // 16-byte chunk p ^ r, so that the operand reads -- rows 0..15 of one chunk -- fall in distinct
+    // banks. (The operand-order alternative, 16 rows x 64 bytes per instruction, fetches half lines:
+    // ~9 against ~25 TB/s from L2 in a streaming probe, and the line's other half is fetched again
+    // by the next sub-step's instruction.) The compiler does not track these loads into LDS, so the
+    // stage loop waits for them itself (vmcnt) before the barrier that publishes the stage.
+    const uint16_t *aline[NMF];
 #pragma unroll
-        for (int u = 0; u < NMF; u++) {
-            const int b = wv + 4 * u;
-            const int k = min(stage * TL_STAGE_K + (b / NMF) * 32, g.K - 32);
-            __builtin_amdgcn_global_load_lds(arow[u % FR] + k,
-                                             (__attribute__((address_space(3))) void *)&lds[buf][((b / NMF) * TL_MFW +
-                                                                                                 b % NMF) * WAVE],
+    for (int u = 0; u < NMF; u++) {
+        const int rf = wv * 4 + (lane >> 4);                        // row of fragment u
+        const int r = min(m0 + u * 16 + rf, m1 - 1);                // clamped valid row
+        const int64_t row = g.a_index ? (int64_t)(g.a_index[r] / g.a_div) : (int64_t)r;
+        aline[u] = g.A + row * g.lda + 8 * ((lane & 15) ^ rf);
+    }
+    auto issue_a = [&](int stage, int buf) {
+        const int k = min(stage, nstages - 1) * TL_STAGE_K;
+#pragma unroll
+        for (int u = 0; u < NMF; u++)
+            __builtin_amdgcn_global_load_lds(aline[u] + k,
+                                             (__attribute__((address_space(3))) void *)&lds[buf][(u * 4 + wv) * WAVE],
                                              16, 0, 0);
-        }
     };
 
     // ---- B fragments of this wave
@@ -189,9 +199,10 @@ __device__ __attribute__((always_inline)) inline void tiled_tile(const GemmArgs 
 #pragma unroll
                 for (int s = 0; s < TL_SUB; s++) {
                     u32x4_t a[NMF];
+                    const int ar = lane & 15, ac = ((s * 4 + (lane >> 4)) ^ ar);   // row, position of its chunk
 #pragma unroll
                     for (int f = 0; f < NMF; f++)
-                        a[f] = lds[cur][(s * TL_MFW + f) * WAVE + lane];
+                        a[f] = lds[cur][f * 256 + ar * 16 + ac];
 #pragma unroll
                     for (int nf = 0; nf < TL_NF; nf++) {
                         const bf16x8_t b = mx_dequant8(bcur[nf][s], e8m0_to_f32((sccur[nf] >> (8 * s)) & 0xFFu));

@@ -661,15 +661,18 @@ __device__ __attribute__((always_inline)) inline void astat_item(const GemmArgs 
     const int jb = NMF > 4 ? j0 : j0 + mh;                       // this wave's first N block
     uint8_t *stage = stage_all + wv * AS_STAGE_BYTES;
 
-    // A tile -> LDS: block (s, f) at s * AS_MF + f holds lane l's operand (row f*16 + l%16,
-    // k = 32 s + 8 (l/16)); only the NMF fragments that hold valid rows are loaded.
+    // A tile -> LDS as whole 128-byte lines: row-half h of fragment f, line L (inputs 64 L .. 64 L +
+    // 63) is one 1 KiB block at (f * KS / 2 + L) * 2 + h, 8 rows x 128 bytes, row r8's 16-byte chunk
+    // c at position c ^ r8 (the operand reads, rows 0..7 of one chunk at a time, then fall in
+    // distinct banks). Only the NMF fragments that hold valid rows are loaded.
     for (int b = wv; b < KS * NMF; b += AS_WAVES) {
-        const int s = b / NMF, f = b % NMF;
-        const int r = min(m0 + f * 16 + (lane & 15), m1 - 1);   // clamped valid row, never stored
+        const int f = b % NMF, L = (b / NMF) / 2, h = (b / NMF) % 2;
+        const int r8 = lane >> 3;
+        const int r = min(m0 + f * 16 + h * 8 + r8, m1 - 1);      // clamped valid row, never stored
         const int64_t row = g.a_index ? (int64_t)(g.a_index[r] / g.a_div) : (int64_t)r;
-        __builtin_amdgcn_global_load_lds(g.A + row * g.lda + s * 32 + 8 * (lane >> 4),
-                                         (__attribute__((address_space(3))) void *)&lds[(s * AS_MF + f) * WAVE], 16,
-                                         0, 0);
+        __builtin_amdgcn_global_load_lds(g.A + row * g.lda + L * 64 + 8 * ((lane & 7) ^ r8),
+                                         (__attribute__((address_space(3))) void *)&lds[((f * (KS / 2) + L) * 2 + h) * WAVE],
+                                         16, 0, 0);
     }
 
     const uint8_t *Bg = g.B + (int64_t)group * g.b_stride;
@@ -714,9 +717,11 @@ __device__ __attribute__((always_inline)) inline void astat_item(const GemmArgs 
 #pragma unroll
             for (int s = 0; s < TL_SUB; s++) {
                 u32x4_t a[WF];
+                const int ss = kb * TL_SUB + s, ar = lane & 15;                 // sub-step, operand row
+                const int ac = ((ss % 2) * 4 + (lane >> 4)) ^ (ar & 7);         // position of its chunk
 #pragma unroll
                 for (int f = 0; f < WF; f++)
-                    a[f] = lds[((kb * TL_SUB + s) * AS_MF + fb + f) * WAVE + lane];
+                    a[f] = lds[(((fb + f) * (KS / 2) + ss / 2) * 2 + (ar >> 3)) * WAVE + (ar & 7) * 8 + ac];
 #pragma unroll
                 for (int nf = 0; nf < AS_NF; nf++) {
                     const bf16x8_t b = mx_dequant8(bc[nf][s], e8m0_to_f32((bs[nf] >> (8 * s)) & 0xFFu));

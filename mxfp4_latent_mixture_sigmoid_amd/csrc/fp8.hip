@@ -235,9 +235,8 @@ __global__ __launch_bounds__(WAVE) void down8_stream_kernel(const Fp8DownArgs g)
 
 // ---------------------------------------------------------------------------------------------
 // A-stationary down product for many rows per expert. The workgroup stages its 128-row FP8 tile
-// of h (128 x K bytes, at most 64 KiB) into LDS once with direct global->LDS loads, in operand
-// order: for 128-input block kb, half s (inputs 64 s ..) and 16-row fragment f, one 1 KiB block
-// holds lane l's 16 bytes (row f*16 + l%16, inputs kb*128 + 64 s + 16 (l/16)). It then walks its
+// of h (128 x K bytes, at most 64 KiB) into LDS once with direct global->LDS loads, as whole
+// 128-byte lines (see astat8_item). It then walks its
 // run of 256-column N blocks; each of the four waves owns 128 x 64 outputs per N block. The
 // weights are operand A of the scaled instruction (FP4, rows = output columns) and h operand B
 // (FP8, columns = rows of h), so lane (q, c) of a fragment holds four consecutive output columns
@@ -258,11 +257,15 @@ __device__ __attribute__((always_inline)) inline void astat8_item(const Fp8DownA
     const int q = lane >> 4;
     uint8_t *stage = stage_all + wv * A8_STAGE_BYTES;
 
+    // As whole 128-byte lines: row-half h of fragment f, block kb is one 1 KiB block at
+    // (f * KB + kb) * 2 + h, 8 rows x 128 bytes, row r8's 16-byte chunk c at position c ^ r8 (the
+    // operand reads, rows 0..7 of one chunk at a time, fall in distinct banks). Operand-order blocks
+    // of 16 rows x 64 bytes, half a line each, stream from L2 at about a third of the rate.
     for (int b = wv; b < KB * 2 * NMF; b += A8_WAVES) {
-        const int kb = b / (2 * NMF), s = (b / NMF) % 2, f = b % NMF;
-        const int r = min(m0 + f * 16 + (lane & 15), m1 - 1);   // clamped valid row, never stored
-        __builtin_amdgcn_global_load_lds(g.codes + (int64_t)r * g.K + kb * MX_STEP + 64 * s + 16 * q,
-                                         (__attribute__((address_space(3))) void *)&lds[((kb * 2 + s) * A8_MF + f) * WAVE],
+        const int f = b % NMF, kb = (b / NMF) / 2, h = (b / NMF) % 2, r8 = lane >> 3;
+        const int r = min(m0 + f * 16 + h * 8 + r8, m1 - 1);   // clamped valid row, never stored
+        __builtin_amdgcn_global_load_lds(g.codes + (int64_t)r * g.K + kb * MX_STEP + 16 * ((lane & 7) ^ r8),
+                                         (__attribute__((address_space(3))) void *)&lds[((f * KB + kb) * 2 + h) * WAVE],
                                          16, 0, 0);
     }
     // h scales: lane l needs row f*16 + l%16, block kb*4 + l/16, one byte per kb
@@ -312,14 +315,18 @@ __device__ __attribute__((always_inline)) inline void astat8_item(const Fp8DownA
                 load_kb(j, kb + 1, bn, bsn);
             else
                 load_kb(min(j + 1, j1 - 1), 0, bn, bsn);
-            // h operands one fragment ahead of their use, so that only two are live at a time
-            u32x4_t alo = lds[((kb * 2 + 0) * A8_MF) * WAVE + lane], ahi = lds[((kb * 2 + 1) * A8_MF) * WAVE + lane];
+            // h operands one fragment ahead of their use, so that only two are live at a time: lane
+            // (q, c) takes chunks q and 4 + q (inputs 16 q .., 64 + 16 q ..) of row c of the fragment
+            const int ar = lane & 15;
+            const int alo_at = (ar >> 3) * WAVE + (ar & 7) * 8 + (q ^ (ar & 7));
+            const int ahi_at = (ar >> 3) * WAVE + (ar & 7) * 8 + ((4 + q) ^ (ar & 7));
+            u32x4_t alo = lds[(kb * 2) * WAVE + alo_at], ahi = lds[(kb * 2) * WAVE + ahi_at];
 #pragma unroll
             for (int f = 0; f < NMF; f++) {
                 const v8i32_t a = fp8_operand(alo, ahi);
                 if (f + 1 < NMF) {
-                    alo = lds[((kb * 2 + 0) * A8_MF + f + 1) * WAVE + lane];
-                    ahi = lds[((kb * 2 + 1) * A8_MF + f + 1) * WAVE + lane];
+                    alo = lds[((f + 1) * KB + kb) * 2 * WAVE + alo_at];
+                    ahi = lds[((f + 1) * KB + kb) * 2 * WAVE + ahi_at];
                 }
                 const uint32_t sa = (hsc[f] >> (8 * kb)) & 0xFFu;
 #pragma unroll

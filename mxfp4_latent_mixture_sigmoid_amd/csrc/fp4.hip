@@ -147,20 +147,23 @@ hipError_t launch_fp4_quant(const uint16_t *z, int64_t rows, int64_t L, uint8_t 
 // Grouped gate|up product with the GLU on MX FP4 z. Each workgroup computes one expert tile (up to
 // 128 rows, gathered through the expert-sorted pair order) times 256 of the 2I interleaved gate /
 // up columns; each of its four waves owns 64 columns (four 16-row weight blocks: gate, up, gate,
-// up) for every row fragment of the tile. K advances in 128-input stages:
+// up) for every row fragment of the tile. K advances in 256-input stages (two MX blocks):
 //  * A (the tile's FP4 rows and their scale dwords) is moved into LDS by direct global->LDS loads,
-//    one stage ahead, into two alternating buffers: per 16-row fragment one 1 KiB block of codes
-//    (lane l: row l % 16, inputs 32 (l / 16) ..) and one 256-byte block of scale dwords (lane l:
-//    the four scale bytes of its row for this stage; byte l / 16 is its operand's);
-//  * B (the weights' A4 blocks) is loaded into registers one stage ahead.
+//    one stage ahead, into two alternating buffers. A stage of one row is one whole 128-byte line
+//    of codes; a load instruction moves eight such lines (lane l: row l / 8, 16-byte chunk
+//    (l % 8) ^ (row % 8), so that the reads below are conflict-free), which keeps every request a
+//    whole line (half lines are served at a third of the rate from L2). Scales: per 16-row
+//    fragment one load of the two scale dwords of every row (lane l: row l % 16, dword (l / 16) % 2);
+//  * B (the weights' A4 blocks, two per stage) is loaded into registers one stage ahead.
 // The weights are operand A of the scaled instruction (rows = output columns) and z operand B, so
 // lane (q, c) of a fragment holds token row c and the four columns 4q .. 4q + 3: the GLU pairs a
 // gate fragment with the up fragment beside it. Work is mapped XCD-major (the column blocks of a
-// tile, then the next tile of the same expert, on one XCD).
+// tile, then the next tile of the same expert, on one XCD). A K that is an odd number of MX blocks
+// ends with a half stage: its second half re-reads valid bytes and its products are skipped.
 constexpr int A4_WAVES = 4, A4_BN = A4_WAVES * 64, A4_MF = 8, A4_NF = 4, A4_XCDS = 8;
 
 struct A4Lds {
-    u32x4_t codes[2][A4_MF][WAVE];
+    u32x4_t codes[2][A4_MF][2][WAVE];   // [buffer][fragment][row half: 8 lines of 8 chunks]
     uint32_t scales[2][A4_MF][WAVE];
 };
 
@@ -173,44 +176,62 @@ __device__ __attribute__((always_inline)) inline void a4_tile(const A4GateupArgs
     const int n0 = bx * A4_BN + wv * 64;                          // this wave's first column
     const int nblocks = g.N / 16;
     const int kblocks = g.K / MX_STEP;
+    const int nst = (kblocks + 1) / 2;
+    const int row_bytes = g.K / 2;
     const uint8_t *Bg = g.B + (int64_t)group * g.b_stride;
 
-    // A blocks of a stage: for every 16-row fragment one block of codes and one of scale dwords.
-    // Wave wv loads fragments f = wv + 4u (u < CU) of both; with fewer than four fragments the
-    // spare waves load fragment wv % NMF once more, and past the last fragment (NMF = 5, 6) a load
-    // repeats the last one (the same bytes into the same LDS slots), so every wave issues the same
-    // number of loads on every path and the waits stay exact.
-    constexpr int CU = (NMF + A4_WAVES - 1) / A4_WAVES;
-    const uint8_t *csrc[CU], *ssrc[CU];
-    int fslot[CU];
+    // Loads of a stage: 2 NMF half fragments of codes (eight lines each) and NMF scale blocks.
+    // Wave wv takes items wv + 4u; with fewer items than waves the spare waves repeat one, and past
+    // the last item a load repeats the last one (the same bytes into the same LDS slots), so every
+    // wave issues the same number of loads on every path and the waits stay exact.
+    constexpr int CC = (2 * NMF + A4_WAVES - 1) / A4_WAVES, CS = (NMF + A4_WAVES - 1) / A4_WAVES;
+    const uint8_t *csrc[CC], *ssrc[CS];
+    int cslot[CC], sslot[CS];
+    bool chi[CC];
+    const int r8 = lane >> 3, cpos = (lane & 7) ^ r8;            // logical chunk this lane moves
 #pragma unroll
-    for (int u = 0; u < CU; u++) {
-        const int f = NMF >= A4_WAVES ? min(wv + A4_WAVES * u, NMF - 1) : wv % NMF;
-        const int r = min(m0 + f * 16 + (lane & 15), m1 - 1);   // clamped valid row, never stored
+    for (int u = 0; u < CC; u++) {
+        const int b = 2 * NMF >= A4_WAVES ? min(wv + A4_WAVES * u, 2 * NMF - 1) : wv % (2 * NMF);
+        const int r = min(m0 + (b >> 1) * 16 + (b & 1) * 8 + r8, m1 - 1);   // clamped valid row, never stored
         const int64_t row = g.a_index ? (int64_t)(g.a_index[r] / g.a_div) : (int64_t)r;
-        csrc[u] = g.zq + row * (g.K / 2) + 16 * (lane >> 4);
-        ssrc[u] = g.zs + row * (g.K / 32);
-        fslot[u] = f;
+        csrc[u] = g.zq + row * row_bytes + 16 * cpos;
+        cslot[u] = b;
+        chi[u] = cpos >= 4;
+    }
+#pragma unroll
+    for (int u = 0; u < CS; u++) {
+        const int f = NMF >= A4_WAVES ? min(wv + A4_WAVES * u, NMF - 1) : wv % NMF;
+        const int r = min(m0 + f * 16 + (lane & 15), m1 - 1);
+        const int64_t row = g.a_index ? (int64_t)(g.a_index[r] / g.a_div) : (int64_t)r;
+        ssrc[u] = g.zs + row * (g.K / 32) + 4 * ((lane >> 4) & 1);
+        sslot[u] = f;
     }
     auto issue_a = [&](int stage, int buf) {
+        // the second half of a final half stage re-reads the first half (in bounds, never used)
+        const bool half = 2 * stage + 1 >= kblocks;
 #pragma unroll
-        for (int u = 0; u < CU; u++) {
-            __builtin_amdgcn_global_load_lds(csrc[u] + stage * (MX_STEP / 2),
-                                             (__attribute__((address_space(3))) void *)&lds.codes[buf][fslot[u]][0], 16, 0,
-                                             0);
-            __builtin_amdgcn_global_load_lds(ssrc[u] + stage * 4,
-                                             (__attribute__((address_space(3))) void *)&lds.scales[buf][fslot[u]][0], 4, 0,
-                                             0);
-        }
+        for (int u = 0; u < CC; u++)
+            __builtin_amdgcn_global_load_lds(csrc[u] + stage * 128 - (half && chi[u] ? 64 : 0),
+                                             (__attribute__((address_space(3))) void *)&lds.codes[buf][cslot[u] >> 1]
+                                                                                                   [cslot[u] & 1][0],
+                                             16, 0, 0);
+#pragma unroll
+        for (int u = 0; u < CS; u++)
+            __builtin_amdgcn_global_load_lds(ssrc[u] + stage * 8 - (half && (lane & 16) ? 4 : 0),
+                                             (__attribute__((address_space(3))) void *)&lds.scales[buf][sslot[u]][0], 4,
+                                             0, 0);
     };
-    auto load_b = [&](int stage, u32x4_t *codes, uint32_t *sc) {
-        stage = min(stage, kblocks - 1);
+    auto load_b = [&](int stage, u32x4_t (*codes)[A4_NF], uint32_t (*sc)[A4_NF]) {
 #pragma unroll
-        for (int nf = 0; nf < A4_NF; nf++) {
-            const int nb = min(n0 / 16 + nf, nblocks - 1);
-            const uint8_t *p = Bg + ((int64_t)nb * kblocks + stage) * MX_BLOCK_BYTES;
-            codes[nf] = load16(p + lane * 16);
-            sc[nf] = p[MX_CODE_BYTES + lane];
+        for (int s = 0; s < 2; s++) {
+            const int kb = min(2 * stage + s, kblocks - 1);
+#pragma unroll
+            for (int nf = 0; nf < A4_NF; nf++) {
+                const int nb = min(n0 / 16 + nf, nblocks - 1);
+                const uint8_t *p = Bg + ((int64_t)nb * kblocks + kb) * MX_BLOCK_BYTES;
+                codes[s][nf] = load16(p + lane * 16);
+                sc[s][nf] = p[MX_CODE_BYTES + lane];
+            }
         }
     };
 
@@ -222,43 +243,51 @@ __device__ __attribute__((always_inline)) inline void a4_tile(const A4GateupArgs
             acc[f][nf] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
     // the first B before the first A stage, so that the prologue's full wait covers both
-    u32x4_t bcur[A4_NF];
-    uint32_t scur[A4_NF];
+    u32x4_t bcur[2][A4_NF];
+    uint32_t scur[2][A4_NF];
     load_b(0, bcur, scur);
     issue_a(0, 0);
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    const int q = lane >> 4;
-    for (int st = 0; st < kblocks; st++) {
+    const int q = lane >> 4, ar = lane & 15, rh = ar >> 3, rl = ar & 7;
+    for (int st = 0; st < nst; st++) {
         const int cur = st & 1;
-        issue_a(min(st + 1, kblocks - 1), cur ^ 1);   // before this stage's B prefetch (vmcnt order)
+        issue_a(min(st + 1, nst - 1), cur ^ 1);   // before this stage's B prefetch (vmcnt order)
         asm volatile("" ::: "memory");
-        u32x4_t bnx[A4_NF];
-        uint32_t snx[A4_NF];
-        load_b(st + 1, bnx, snx);
+        u32x4_t bnx[2][A4_NF];
+        uint32_t snx[2][A4_NF];
+        load_b(min(st + 1, nst - 1), bnx, snx);
+        const int subs = 2 * st + 1 < kblocks ? 2 : 1;
 #pragma unroll
-        for (int f = 0; f < NMF; f++) {
-            const u32x4_t a = lds.codes[cur][f][lane];
-            const uint32_t sa = (lds.scales[cur][f][lane] >> (8 * q)) & 0xFFu;
+        for (int s = 0; s < 2; s++) {
+            if (s >= subs)
+                break;
 #pragma unroll
-            for (int nf = 0; nf < A4_NF; nf++)
-                acc[f][nf] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                    fp4_operand8(bcur[nf]), fp4_operand8(a), acc[f][nf], 4, 4, 0, (int)scur[nf], 0, (int)sa);
+            for (int f = 0; f < NMF; f++) {
+                const u32x4_t a = lds.codes[cur][f][rh][rl * 8 + ((4 * s + q) ^ rl)];
+                const uint32_t sa = (lds.scales[cur][f][16 * s + ar] >> (8 * q)) & 0xFFu;
+#pragma unroll
+                for (int nf = 0; nf < A4_NF; nf++)
+                    acc[f][nf] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                        fp4_operand8(bcur[s][nf]), fp4_operand8(a), acc[f][nf], 4, 4, 0, (int)scur[s][nf], 0, (int)sa);
+            }
         }
 #pragma unroll
-        for (int nf = 0; nf < A4_NF; nf++) {
-            bcur[nf] = bnx[nf];
-            scur[nf] = snx[nf];
-        }
+        for (int s = 0; s < 2; s++)
+#pragma unroll
+            for (int nf = 0; nf < A4_NF; nf++) {
+                bcur[s][nf] = bnx[s][nf];
+                scur[s][nf] = snx[s][nf];
+            }
         // This wave's part of the next stage's A is in LDS and its reads of this stage's are done,
-        // then the waves meet; the next stage's B prefetch (2 A4_NF loads, issued after the A
+        // then the waves meet; the next stage's B prefetch (4 A4_NF loads, issued after the A
         // loads) stays in flight through the barrier and is waited for after it, so that no load
         // is outstanding at the loop head (the compiler does not order direct-to-LDS loads with
         // register loads in its wait counts, and a B load still pending there made it wait for the
         // next A stage before the multiplies).
         asm volatile("" ::: "memory");
-        __builtin_amdgcn_s_waitcnt(vmcnt_lgkm_imm(2 * A4_NF));
+        __builtin_amdgcn_s_waitcnt(vmcnt_lgkm_imm(4 * A4_NF));
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
         asm volatile("" ::: "memory");

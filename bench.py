@@ -99,6 +99,26 @@ def algorithmic(shape, n_active: int) -> dict:
     )
 
 
+def kernel_roof(nbytes: float, flops: float, mma_peak_tflops: float, seconds: float) -> dict:
+    """A kernel against the higher of its two roofs: `nbytes` at the HBM peak, or `flops` at the
+    given matrix-core peak. The bound is the roof with the longer lower-bound time; `achieved` and
+    `frac` are in that roof's unit, and both lower bounds are reported (`roof_us`)."""
+    t_hbm = nbytes / (HBM_PEAK_GBPS * 1e9)
+    t_mma = flops / (mma_peak_tflops * 1e12)
+    if t_hbm >= t_mma:
+        achieved = nbytes / seconds / 1e9
+        roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBPS, unit="GB/s",
+                    frac=round(achieved / HBM_PEAK_GBPS, 4))
+    else:
+        achieved = flops / seconds / 1e12
+        roof = dict(bound="mfma", achieved=round(achieved, 2), peak=mma_peak_tflops, unit="TFLOP/s",
+                    frac=round(achieved / mma_peak_tflops, 4))
+    roof["bytes_per_launch"] = round(nbytes)
+    roof["flops_per_launch"] = round(flops)
+    roof["roof_us"] = {"hbm": round(t_hbm * 1e6, 2), "mfma": round(t_mma * 1e6, 2)}
+    return roof
+
+
 def read_traffic(workload: str, kernel: str):
     """Beyond-L2 bytes per launch from committed PMC counters (FETCH_SIZE + WRITE_SIZE, each scaled
     by the counter's reading for a copy of known size), or None once that kernel's source has
@@ -211,22 +231,18 @@ class Leg:
         return self.shape.T * self.shape.K <= 4 * self.shape.E   # few tokens per expert: weight-stream bound
 
     def roofline(self, kernels_us: dict, n_active: int) -> dict:
-        """The dominant kernel (the routed gate|up product) against its own roof."""
+        """The dominant kernel (the routed gate|up product) against the higher of its two roofs: its
+        algorithmic bytes at the HBM peak, or its flops at the matrix-core peak of its operand type
+        (BF16, or MXFP4 with the A4W4 first stage). Both lower bounds are reported."""
         s = self.shape
         alg = algorithmic(s, n_active)
         gateup_s = kernels_us["gateup"] * 1e-6
-        if self.is_decode():
-            gb = alg["gateup_bytes"]
-            if self.a4:   # the gate/up product reads MX FP4 z (17/32 bytes per value) instead of BF16 z
-                gb += s.T * s.Lt * (MX_BYTES_PER_VALUE - 2)
-            achieved = gb / gateup_s / 1e9
-            roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBPS, unit="GB/s",
-                        frac=round(achieved / HBM_PEAK_GBPS, 4), bytes_per_launch=round(gb))
-        else:   # a contraction against the peak of its own operand type
-            peak = FP4_PEAK_TFLOPS if self.a4 else BF16_PEAK_TFLOPS
-            achieved = alg["gateup_flops"] / gateup_s / 1e12
-            roof = dict(bound="mfma", achieved=round(achieved, 2), peak=peak, unit="TFLOP/s",
-                        frac=round(achieved / peak, 4), flops_per_launch=round(alg["gateup_flops"]))
+        gb = alg["gateup_bytes"]
+        if self.a4:   # the gate/up product reads MX FP4 z (17/32 bytes per value) instead of BF16 z
+            gb += s.T * s.Lt * (MX_BYTES_PER_VALUE - 2)
+        flops = alg["gateup_flops"]
+        peak = FP4_PEAK_TFLOPS if self.a4 else BF16_PEAK_TFLOPS
+        roof = kernel_roof(gb, flops, peak, gateup_s)
         roof["kernel"] = "gateup"
         roof["kernel_us"] = kernels_us["gateup"]
         roof["traffic"] = None if self.a4 else read_traffic(s.name, "gateup")

@@ -728,7 +728,8 @@ moe_status experts_impl(moe_handle *h, const void *x, int32_t T, const moe_routi
         uint8_t *zq = ws + W.z4, *zs = ws + W.z4 + (int64_t)T * (Lt / 2);
         MOE_LAUNCH(MOE_KERNEL_Z_QUANT, launch_fp4_quant(A, T, Lt, zq, zs, st));
         A4GateupArgs g{zq, zs, r->sorted_pairs, K, h->packed + h->off_gateup4, h->gateup_stride, 2 * I, Lt, tl, Hb, I};
-        MOE_LAUNCH(MOE_KERNEL_GATEUP, launch_a4_gateup(g, (int)W.max_tiles, st));
+        MOE_LAUNCH(MOE_KERNEL_GATEUP, tiled ? launch_a4_gateup(g, (int)W.max_tiles, st)
+                                            : launch_a4_gateup_small(g, (int)W.max_tiles, st));
     } else {   // h = bf16(silu(z Wg_e^T) (z Wu_e^T)) for every pair, rows in expert-sorted order
         GemmArgs g{};
         g.A = lat ? Z : static_cast<const uint16_t *>(x);

@@ -361,4 +361,102 @@ hipError_t launch_a4_gateup(const A4GateupArgs &g, int max_tiles, hipStream_t st
     return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------------------------
+// Grouped A4W4 gate|up product with the GLU for expert tiles of at most 16 rows (few tokens per
+// expert), where the time is the HBM stream of the weights: the structure of the BF16 few-row
+// kernel on the scaled FP4 x FP4 instruction. Workgroup (x, y) computes tile y of the list for the
+// 64 columns 64 x .. 64 x + 63 (four 16-row weight blocks: gate, up, gate, up). Its WK waves split
+// the K axis in whole MX blocks; a wave loads SB blocks' weights (codes and scales) and z (codes and
+// the scale byte of its slice) before it multiplies them. The partial tiles are summed in LDS in
+// wave order, then the GLU is written. Lane (q, c) of a fragment holds token row c (clamped to a
+// valid row, never stored past the tile) and columns 4 q .. 4 q + 3.
+template <int WK, int SB>
+__global__ __launch_bounds__(WAVE *WK) void a4_small_kernel(const A4GateupArgs g)
+{
+    constexpr int BN = 64;
+    __shared__ float red[WK * 16 * BN];
+    const int lane = threadIdx.x & (WAVE - 1);
+    const int wv = threadIdx.x / WAVE;
+    if ((int)blockIdx.y >= g.tiles[0])
+        return;
+    const int4 t = reinterpret_cast<const int4 *>(g.tiles + TILE_HEADER_INTS)[blockIdx.y];
+    const int m0 = t.y, m1 = t.z;
+    const int n0 = blockIdx.x * BN;
+    const int kblocks = g.K / MX_STEP;
+    const int s0 = (wv * kblocks) / WK, s1 = ((wv + 1) * kblocks) / WK;
+    const int c = lane & 15, q = lane >> 4;
+    const int r = min(m0 + c, m1 - 1);
+    const int64_t row = g.a_index ? (int64_t)(g.a_index[r] / g.a_div) : (int64_t)r;
+    const uint8_t *zrow = g.zq + row * (g.K / 2) + 16 * q;
+    const uint8_t *srow = g.zs + row * (g.K / 32) + q;
+    const uint8_t *Bg = g.B + (int64_t)t.x * g.b_stride;
+
+    f32x4_t acc[4];
+#pragma unroll
+    for (int nf = 0; nf < 4; nf++)
+        acc[nf] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int s = s0; s < s1; s += SB) {
+        u32x4_t bc[SB][4], a[SB];
+        uint32_t bs[SB][4], as[SB];
+#pragma unroll
+        for (int u = 0; u < SB; u++) {
+            const int kb = min(s + u, s1 - 1);   // past the wave's range: re-read (not multiplied)
+#pragma unroll
+            for (int nf = 0; nf < 4; nf++) {
+                const uint8_t *p = Bg + ((int64_t)(n0 / 16 + nf) * kblocks + kb) * MX_BLOCK_BYTES;
+                bc[u][nf] = load16_nt(p + lane * 16);
+                bs[u][nf] = p[MX_CODE_BYTES + lane];
+            }
+            a[u] = load16(zrow + kb * (MX_STEP / 2));
+            as[u] = srow[kb * 4];
+        }
+#pragma unroll
+        for (int u = 0; u < SB; u++)
+            if (s + u < s1)
+#pragma unroll
+                for (int nf = 0; nf < 4; nf++)
+                    acc[nf] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                        fp4_operand8(bc[u][nf]), fp4_operand8(a[u]), acc[nf], 4, 4, 0, (int)bs[u][nf], 0, (int)as[u]);
+    }
+#pragma unroll
+    for (int nf = 0; nf < 4; nf++)
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+            red[(wv * 16 + c) * BN + nf * 16 + 4 * q + i] = acc[nf][i];
+    __syncthreads();
+    // GLU: output column oc of this block pairs gate column 32 (oc / 16) + oc % 16 with the up
+    // column 16 after it
+    constexpr int BO = BN / 2;
+    for (int idx = threadIdx.x; idx < 16 * BO; idx += WAVE * WK) {
+        const int rr = idx / BO, oc = idx % BO;
+        const int orow = m0 + rr;
+        if (orow >= m1)
+            continue;
+        const int gc = (oc / 16) * 32 + (oc % 16), uc = gc + 16;
+        float gs = 0.f, us = 0.f;
+#pragma unroll
+        for (int w = 0; w < WK; w++) {
+            gs += red[(w * 16 + rr) * BN + gc];
+            us += red[(w * 16 + rr) * BN + uc];
+        }
+        g.h[(int64_t)orow * g.ldh + n0 / 2 + oc] = (uint16_t)f32_to_bf16_bits(silu_f32(gs) * us);
+    }
+}
+
+#ifndef A4_SMALL_SB
+#define A4_SMALL_SB 1
+#endif
+hipError_t launch_a4_gateup_small(const A4GateupArgs &g, int max_tiles, hipStream_t st)
+{
+    if (!g.tiles || !g.zq || !g.zs || !g.B || !g.h || g.N <= 0 || g.N % 64 || g.K < MX_STEP || g.K % MX_STEP ||
+        g.ldh < g.N / 2 || reinterpret_cast<uintptr_t>(g.zq) % 16)
+        return hipErrorInvalidValue;
+    if (max_tiles <= 0)
+        return hipSuccess;
+    if (max_tiles > 65535)
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL((a4_small_kernel<4, A4_SMALL_SB>), dim3(g.N / 64, max_tiles), dim3(WAVE * 4), 0, st, g);
+    return hipGetLastError();
+}
+
 } // namespace mxmoe

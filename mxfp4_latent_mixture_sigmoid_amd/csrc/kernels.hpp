@@ -94,6 +94,8 @@ struct A4GateupArgs {
 hipError_t launch_fp4_quant(const uint16_t *z, int64_t rows, int64_t L, uint8_t *codes, uint8_t *scales,
                             hipStream_t st);
 hipError_t launch_a4_gateup(const A4GateupArgs &g, int max_tiles, hipStream_t st);
+// Few rows per expert (tiles of at most 16 rows): the weight-streaming form.
+hipError_t launch_a4_gateup_small(const A4GateupArgs &g, int max_tiles, hipStream_t st);
 hipError_t launch_pack_gateup4(uint8_t *dst, const uint8_t *gc, const uint8_t *gs, const uint8_t *uc,
                                const uint8_t *us, int64_t E, int64_t I, int64_t Lt, hipStream_t st);
 hipError_t launch_pack_down8(uint8_t *dst, const uint8_t *dc, const uint8_t *ds, int64_t E, int64_t I, int64_t Lt,

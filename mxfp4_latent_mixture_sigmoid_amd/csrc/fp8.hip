@@ -417,7 +417,19 @@ hipError_t launch_down_fp8(const Fp8DownArgs &g, bool many_rows, int max_tiles, 
     if (!many_rows) {
         if (max_tiles > 65535)
             return hipErrorInvalidValue;
-        hipLaunchKernelGGL((down8_stream_kernel<4, 4>), dim3(g.N / 64, max_tiles), dim3(WAVE), 0, st, g);
+        // blocks per batch: all of them up to four, else 4 or 3 when that divides the count, so that
+        // no batch re-reads a clamped block (a repeated fourth block at K = 384 cost 12%)
+        const int nblk = g.K / MX_STEP;
+        const int batch = nblk <= 4 ? nblk : nblk % 3 == 0 && nblk % 4 != 0 ? 3 : 4;
+        const dim3 grid(g.N / 64, max_tiles);
+        if (batch == 4)
+            hipLaunchKernelGGL((down8_stream_kernel<4, 4>), grid, dim3(WAVE), 0, st, g);
+        else if (batch == 3)
+            hipLaunchKernelGGL((down8_stream_kernel<4, 3>), grid, dim3(WAVE), 0, st, g);
+        else if (batch == 2)
+            hipLaunchKernelGGL((down8_stream_kernel<4, 2>), grid, dim3(WAVE), 0, st, g);
+        else
+            hipLaunchKernelGGL((down8_stream_kernel<4, 1>), grid, dim3(WAVE), 0, st, g);
         return hipGetLastError();
     }
     switch (g.K / MX_STEP) {

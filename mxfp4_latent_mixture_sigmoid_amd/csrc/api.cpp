@@ -590,9 +590,8 @@ moe_status select_impl(moe_handle *h, int32_t T, const TopkArgs &ta, const moe_r
                                                             r->sorted_pairs, r->inv, st, bm, tiles ? tl : nullptr));
     } else {
         MOE_LAUNCH(MOE_KERNEL_PERMUTE, launch_permute(r->topk_ids, T, K, E, reinterpret_cast<int32_t *>(ws + W.hist),
-                                                      r->counts, r->offsets, r->sorted_pairs, r->inv, st));
-        if (tiles)
-            MOE_LAUNCH(MOE_KERNEL_TILEMAP, launch_tilemap(r->offsets, E, bm, tl, st));
+                                                      r->counts, r->offsets, r->sorted_pairs, r->inv, st, bm,
+                                                      tiles ? tl : nullptr));
     }
     return MOE_OK;
 }

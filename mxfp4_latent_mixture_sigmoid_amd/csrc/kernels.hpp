@@ -191,8 +191,10 @@ hipError_t launch_topk_xside(const TopkArgs &a, const XsideEpiArgs &e, hipStream
 hipError_t launch_permute_small(const int32_t *ids, int T, int K, int E, int32_t *counts, int32_t *offsets,
                                 int32_t *sorted_pairs, int32_t *inv, hipStream_t st, int bm = 0,
                                 int32_t *tiles = nullptr);
+// tiles (nullable): the expert tile list of bm rows, written by the scatter's first workgroup.
 hipError_t launch_permute(const int32_t *ids, int T, int K, int E, int32_t *hist, int32_t *counts,
-                          int32_t *offsets, int32_t *sorted_pairs, int32_t *inv, hipStream_t st);
+                          int32_t *offsets, int32_t *sorted_pairs, int32_t *inv, hipStream_t st, int bm,
+                          int32_t *tiles);
 
 // Forward helpers.
 hipError_t launch_tilemap(const int32_t *offsets, int E, int bm, int32_t *tiles, hipStream_t st);

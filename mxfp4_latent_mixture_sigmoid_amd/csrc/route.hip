@@ -481,17 +481,21 @@ __global__ __launch_bounds__(256) void perm_colscan_kernel(int32_t *__restrict__
 
 // Pass 3: expert offsets (exclusive scan of counts), then a stable scatter: one wave walks the
 // block's tokens in order; the K experts of a token are distinct, so its K lanes bump distinct
-// LDS counters and every pair lands at offsets[e] + (pairs of e in earlier tokens).
+// LDS counters and every pair lands at offsets[e] + (pairs of e in earlier tokens). Every block
+// computes all the offsets; block 0 also writes them, and the expert tile list of bm rows when
+// `tiles` is set.
 __global__ __launch_bounds__(256) void perm_scatter_kernel(const int32_t *__restrict__ ids, int T, int K, int E,
                                                            int nb, const int32_t *__restrict__ hist,
                                                            const int32_t *__restrict__ counts,
                                                            int32_t *__restrict__ offsets,
                                                            int32_t *__restrict__ sorted_pairs,
-                                                           int32_t *__restrict__ inv)
+                                                           int32_t *__restrict__ inv, int bm,
+                                                           int32_t *__restrict__ tiles)
 {
     extern __shared__ int lds[];
     int *cnt = lds;                                   // [E]
     int *blk_ids = lds + E;                           // [PERM_TOKENS_PER_BLOCK * K]
+    int *off = blk_ids + PERM_TOKENS_PER_BLOCK * K;   // [E + 1], block 0 with a tile list only
     __shared__ int sh[16];
     const int b = blockIdx.x;
     const int per = (E + blockDim.x - 1) / blockDim.x;
@@ -501,14 +505,24 @@ __global__ __launch_bounds__(256) void perm_scatter_kernel(const int32_t *__rest
         local += counts[e];
     int total;
     int run = block_excl_scan(local, sh, &total);
+    const bool list = b == 0 && tiles;
     for (int e = e0; e < e1; e++) {
         if (b == 0)
             offsets[e] = run;
+        if (list)
+            off[e] = run;
         cnt[e] = run + hist[(int64_t)e * nb + b];
         run += counts[e];
     }
-    if (b == 0 && threadIdx.x == 0)
+    if (b == 0 && threadIdx.x == 0) {
         offsets[E] = total;
+        if (list)
+            off[E] = total;
+    }
+    if (list) {   // block-uniform: every thread of block 0 takes part
+        __syncthreads();
+        write_tiles(off, E, bm, tiles, sh);
+    }
     const int t0 = b * PERM_TOKENS_PER_BLOCK, t1 = min(T, t0 + PERM_TOKENS_PER_BLOCK);
     for (int i = threadIdx.x; i < (t1 - t0) * K; i += blockDim.x)
         blk_ids[i] = ids[(int64_t)t0 * K + i];
@@ -527,7 +541,8 @@ __global__ __launch_bounds__(256) void perm_scatter_kernel(const int32_t *__rest
 }
 
 hipError_t launch_permute(const int32_t *ids, int T, int K, int E, int32_t *hist, int32_t *counts,
-                          int32_t *offsets, int32_t *sorted_pairs, int32_t *inv, hipStream_t st)
+                          int32_t *offsets, int32_t *sorted_pairs, int32_t *inv, hipStream_t st, int bm,
+                          int32_t *tiles)
 {
     const int nb = (T + PERM_TOKENS_PER_BLOCK - 1) / PERM_TOKENS_PER_BLOCK;
     hipLaunchKernelGGL(perm_hist_kernel, dim3(nb), dim3(256), E * sizeof(int), st, ids, T, K, E, nb, hist);
@@ -537,9 +552,11 @@ hipError_t launch_permute(const int32_t *ids, int T, int K, int E, int32_t *hist
     hipLaunchKernelGGL(perm_colscan_kernel, dim3(E), dim3(256), 0, st, hist, nb, counts);
     if ((err = hipGetLastError()) != hipSuccess)
         return err;
-    const size_t lds = (E + PERM_TOKENS_PER_BLOCK * K) * sizeof(int);
+    if (tiles && bm <= 0)
+        return hipErrorInvalidValue;
+    const size_t lds = (E + PERM_TOKENS_PER_BLOCK * K + (tiles ? E + 1 : 0)) * sizeof(int);
     hipLaunchKernelGGL(perm_scatter_kernel, dim3(nb), dim3(256), lds, st, ids, T, K, E, nb, hist, counts, offsets,
-                       sorted_pairs, inv);
+                       sorted_pairs, inv, bm, tiles);
     return hipGetLastError();
 }
 

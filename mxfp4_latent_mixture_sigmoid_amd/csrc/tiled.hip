@@ -430,13 +430,17 @@ __global__ __launch_bounds__(WAVE *RG_WAVES) void ring_kernel(const GemmArgs g, 
 
     // This wave's loads: blocks wv*LOADS .. wv*LOADS+LOADS-1 of a stage. Within a stage they are one
     // base plus a fixed stride: 16 rows of A, or one row-block stride of B's current 16-step chunk.
+    // An A block (16 rows x 64 bytes) is loaded with four consecutive lanes on one row -- lane l
+    // takes row l / 4 and 16-byte chunk (l % 4) ^ (l / 16), so slot 4 r + (c ^ (r / 4)) holds chunk c
+    // of row r -- which L2 serves at ~1.6x the rate of the operand order (lane l on row l % 16); the
+    // fragment reads (lane l: row l % 16, chunk l / 16) then fall in distinct banks.
     // When the B blocks do not fill the last wave, its spare loads repeat the last block (the same
     // bytes into the same slot), so that every wave issues the same number of loads.
     const bool loads_a = wv < AW;
     const int li = loads_a ? wv : wv - AW;
     const int bfirst = li * LOADS;                       // first B block of a B wave
     const uint8_t *a_base = reinterpret_cast<const uint8_t *>(
-        g.A + (int64_t)(m0 + li * (LOADS * 16) + (lane & 15)) * g.lda + 8 * (lane >> 4));
+        g.A + (int64_t)(m0 + li * (LOADS * 16) + (lane >> 2)) * g.lda + 8 * ((lane & 3) ^ ((lane >> 4) & 3)));
     const int bnb0 = n0 / 16 + bfirst;
     auto issue = [&](int s) {                // stage min(s, nst - 1) into buffer s % RG_NBUF
         const int ss = min(s, nst - 1), buf = s % RG_NBUF;
@@ -471,9 +475,10 @@ __global__ __launch_bounds__(WAVE *RG_WAVES) void ring_kernel(const GemmArgs g, 
 #pragma unroll
         for (int j = 0; j < WNF; j++)
             bf[j] = lds[buf][AF + wn * WNF + j][lane];
+        const int rr = lane & 15, cc = lane >> 4;
 #pragma unroll
         for (int f = 0; f < WMF; f++)
-            af[f] = lds[buf][wm * WMF + f][lane];
+            af[f] = lds[buf][wm * WMF + f][rr * 4 + (cc ^ ((rr >> 2) & 3))];
     };
     // Wait until only the later stages' loads of this wave are outstanding, then a barrier makes every
     // wave's loads of this stage visible (and all waves are past the previous stage).

@@ -17,10 +17,11 @@
 namespace mxmoe {
 
 
-// LDS holds the activation chunk in matrix-core operand order: for step s and 16-row fragment mf,
-// a 1 KiB block whose 16-byte lane slots are the operand of lane l (row mf*16 + l%16, inputs
-// s*32 + 8(l/16) .. +7). Operand reads are then one sequential 1 KiB per wave (no bank conflicts),
-// and the staging thread t of each 64 writes slot t of a block (sequential as well).
+// LDS holds the activation chunk per step s and 16-row fragment mf in a 1 KiB block: slot
+// 4 r + (c ^ (r / 4)) holds 16-byte chunk c (inputs s*32 + 8c .. +7) of row mf*16 + r. The staging
+// thread t of each 64 loads the chunk of slot t (four consecutive threads on one row, which L2
+// serves faster than one thread per row) and writes slot t (sequential); the operand read of lane l
+// (row l % 16, chunk l / 16) then falls in distinct banks.
 template <int WAVES, int SK_MAX_STEPS>
 __global__ __launch_bounds__(WAVE *WAVES) void skinny_kernel(const SkinnyArgs g)
 {
@@ -56,14 +57,14 @@ __global__ __launch_bounds__(WAVE *WAVES) void skinny_kernel(const SkinnyArgs g)
     for (int u = 0; u < A_PER_THREAD; u++) {
         const int slot = threadIdx.x + u * WAVE * WAVES;        // block (slot / 64), lane slot % 64
         const int blk = slot / WAVE, sl = slot % WAVE;
-        const int st = min(blk / 4, nsteps - 1), m = (blk % 4) * 16 + (sl & 15);
-        av[u] = load16(g.A + (int64_t)min(m, g.M - 1) * g.lda + kc0 + st * BF16_STEP + 8 * (sl >> 4));
+        const int st = min(blk / 4, nsteps - 1), m = (blk % 4) * 16 + (sl >> 2);
+        av[u] = load16(g.A + (int64_t)min(m, g.M - 1) * g.lda + kc0 + st * BF16_STEP + 8 * ((sl & 3) ^ ((sl >> 4) & 3)));
     }
 #pragma unroll
     for (int u = 0; u < A_PER_THREAD; u++) {
         const int slot = threadIdx.x + u * WAVE * WAVES;
         const int blk = slot / WAVE, sl = slot % WAVE;
-        const int m = (blk % 4) * 16 + (sl & 15);
+        const int m = (blk % 4) * 16 + (sl >> 2);
         if (blk / 4 < nsteps && (blk % 4) < mt)
             lds_a[slot] = m < g.M ? av[u] : u32x4_t{0u, 0u, 0u, 0u};
     }
@@ -82,7 +83,7 @@ __global__ __launch_bounds__(WAVE *WAVES) void skinny_kernel(const SkinnyArgs g)
             u32x4_t a[4];
 #pragma unroll
             for (int mf = 0; mf < 4; mf++)
-                a[mf] = lds_a[(s * 4 + mf) * WAVE + lane];
+                a[mf] = lds_a[(s * 4 + mf) * WAVE + (lane & 15) * 4 + ((lane >> 4) ^ ((lane >> 2) & 3))];
 #pragma unroll
             for (int mf = 0; mf < 4; mf++)
                 if (mf < mt)
@@ -143,14 +144,14 @@ __global__ __launch_bounds__(WAVE *WAVES) void skinny_persist_kernel(const Skinn
         for (int u = 0; u < A_PER_THREAD; u++) {
             const int slot = threadIdx.x + u * WAVE * WAVES;
             const int blk = slot / WAVE, sl = slot % WAVE;
-            const int st = min(blk / 4, nsteps - 1), m = (blk % 4) * 16 + (sl & 15);
-            av[u] = load16(g.A + (int64_t)min(m, g.M - 1) * g.lda + kc0 + st * BF16_STEP + 8 * (sl >> 4));
+            const int st = min(blk / 4, nsteps - 1), m = (blk % 4) * 16 + (sl >> 2);
+            av[u] = load16(g.A + (int64_t)min(m, g.M - 1) * g.lda + kc0 + st * BF16_STEP + 8 * ((sl & 3) ^ ((sl >> 4) & 3)));
         }
 #pragma unroll
         for (int u = 0; u < A_PER_THREAD; u++) {
             const int slot = threadIdx.x + u * WAVE * WAVES;
             const int blk = slot / WAVE, sl = slot % WAVE;
-            const int m = (blk % 4) * 16 + (sl & 15);
+            const int m = (blk % 4) * 16 + (sl >> 2);
             if (blk / 4 < nsteps && (blk % 4) < MT)
                 lds_a[slot] = m < g.M ? av[u] : u32x4_t{0u, 0u, 0u, 0u};
         }
@@ -171,7 +172,7 @@ __global__ __launch_bounds__(WAVE *WAVES) void skinny_persist_kernel(const Skinn
                 u32x4_t a[4];
 #pragma unroll
                 for (int mf = 0; mf < 4; mf++)
-                    a[mf] = lds_a[(step * 4 + mf) * WAVE + lane];
+                    a[mf] = lds_a[(step * 4 + mf) * WAVE + (lane & 15) * 4 + ((lane >> 4) ^ ((lane >> 2) & 3))];
 #pragma unroll
                 for (int mf = 0; mf < 4; mf++)
                     if (mf < MT)

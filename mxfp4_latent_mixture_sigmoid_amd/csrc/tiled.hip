@@ -72,7 +72,8 @@ __device__ __attribute__((always_inline)) inline void tiled_tile(const GemmArgs 
     const uint8_t *Bg = g.B + (int64_t)group * g.b_stride;
 
     // ---- A staging. A stage holds TL_SUB x NMF 1 KiB blocks (sub-step s, fragment f at block
-    // s * TL_MFW + f, lane slot l = row f*16 + l%16, inputs s*32 + 8(l/16)). Thread t fills lane slot
+    // s * TL_MFW + f; slot 4 r + (c ^ (r / 4)) holds row f*16 + r, inputs s*32 + 8c .. +7, so that the
+    // loads of slots 4r .. 4r+3 -- four consecutive lanes -- share a row). Thread t fills lane slot
     // t % 64 of blocks b = wv + 4u (u < NMF), b -> (s, f) = (b / NMF, b % NMF): its fragment row
     // f = (wv + 4u) % NMF repeats with period FR = NMF / gcd(NMF, 4) in u (NMF = 2..6, 8: 1, 3, 1,
     // 5, 3, 2 distinct rows), so row pointer u % FR serves load u.
@@ -81,9 +82,9 @@ __device__ __attribute__((always_inline)) inline void tiled_tile(const GemmArgs 
 #pragma unroll
     for (int i = 0; i < FR; i++) {
         const int f = (wv + 4 * i) % NMF;
-        const int r = min(m0 + f * 16 + (lane & 15), m1 - 1);   // clamped valid row
+        const int r = min(m0 + f * 16 + (lane >> 2), m1 - 1);   // clamped valid row
         const int64_t row = g.a_index ? (int64_t)(g.a_index[r] / g.a_div) : (int64_t)r;
-        arow[i] = g.A + row * g.lda + 8 * (lane >> 4);
+        arow[i] = g.A + row * g.lda + 8 * ((lane & 3) ^ ((lane >> 4) & 3));
     }
     const int nstages = (g.K + TL_STAGE_K - 1) / TL_STAGE_K;
     auto load_a = [&](int stage, u32x4_t *v) {
@@ -227,7 +228,7 @@ __device__ __attribute__((always_inline)) inline void tiled_tile(const GemmArgs 
                         u32x4_t a[NMF];
 #pragma unroll
                         for (int f = 0; f < NMF; f++)
-                            a[f] = lds[cur][(s * TL_MFW + f) * WAVE + lane];
+                            a[f] = lds[cur][(s * TL_MFW + f) * WAVE + (lane & 15) * 4 + ((lane >> 4) ^ ((lane >> 2) & 3))];
 #pragma unroll
                         for (int nf = 0; nf < TL_NF; nf++)
 #pragma unroll

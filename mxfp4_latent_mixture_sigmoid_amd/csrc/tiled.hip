@@ -161,7 +161,7 @@ __device__ __attribute__((always_inline)) inline void tiled_tile(const GemmArgs 
 #pragma unroll
         for (int nf = 0; nf < TL_NF; nf++) {
             const int nb = min(n0 / 16 + nf, nblocks - 1);
-            b[nf] = load16_nt(Bg + bf16_block_index(nb, min(kstep, ks - 1), g.N, g.K) * BF16_BLOCK_BYTES + lane * 16);
+            b[nf] = load16(Bg + bf16_block_index(nb, min(kstep, ks - 1), g.N, g.K) * BF16_BLOCK_BYTES + lane * 16);
         }
     };
     // The stage loop is one basic block: waves past N multiply clamped (valid) B and store nothing,

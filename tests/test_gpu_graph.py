@@ -44,10 +44,10 @@ def _same(tag, r, lg, out, r2, lg2, out2, T, K):
     assert torch.equal(out[:T].view(torch.int16), out2[:T].view(torch.int16)), f"{tag}: output"
 
 
-def _check_replays(shape, T, replays=4):
-    G.log(f"[graph] {shape.name} T={T}")
+def _check_replays(shape, T, replays=4, stage1_a4=False, stage2_fp8=False):
+    G.log(f"[graph] {shape.name} T={T} a4={stage1_a4} fp8={stage2_fp8}")
     inp = make_inputs(replace(shape, T=T))
-    layer = G.make_layer(shape, inp, T_max=T)
+    layer = G.make_layer(shape, inp, T_max=T, stage1_a4=stage1_a4, stage2_fp8=stage2_fp8)
     bias = None if inp.get("router_bias") is None else G.dev(inp["router_bias"])
     xs = [G.dev(inp["x"])]
     rng = np.random.default_rng(shape.seed + 101)
@@ -90,6 +90,12 @@ def test_graph_replays_match_eager_without_latent_projections():
 
 def test_graph_replays_match_eager_decode_full_size():
     _check_replays(SHAPES["tp8_decode_t64"], 64, replays=3)
+
+
+@pytest.mark.parametrize("a4,fp8", [(True, False), (False, True), (True, True)])
+def test_graph_replays_match_eager_quantised_stages(a4, fp8):
+    # the quantisers and the scaled-instruction expert kernels inside the captured step
+    _check_replays(MID, 64, replays=3, stage1_a4=a4, stage2_fp8=fp8)
 
 
 def test_graph_rejects_profiling_and_zero_tokens():

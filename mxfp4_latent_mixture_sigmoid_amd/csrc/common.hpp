@@ -103,6 +103,16 @@ __device__ inline bf16x8_t mx_dequant8(uint32_t codes, float scale)
     return r.v;
 }
 
+// A 16-row x 64-byte operand block (one 32-input step of 16 BF16 rows) staged in LDS with four
+// consecutive lanes per row holds chunk c (16 bytes) of row r in slot 4 r + (c ^ chunk_swizzle(r)).
+// The operand read (lane l: row l % 16, chunk l / 16) then hits distinct banks in every group of 8,
+// 16 or 32 consecutive lanes: for a fixed chunk, the rows of each such group map to distinct slots
+// modulo 8, 16 and 32. (r / 4 as the XOR repeats a slot modulo 8 within eight lanes.)
+__host__ __device__ inline int chunk_swizzle(int r)
+{
+    return ((((r >> 2) ^ (r >> 3)) & 1) << 1) | (((r >> 1) ^ (r >> 3)) & 1);
+}
+
 __device__ inline bf16x8_t as_bf16x8(u32x4_t v)
 {
     union {

@@ -18,7 +18,7 @@ namespace mxmoe {
 
 
 // LDS holds the activation chunk per step s and 16-row fragment mf in a 1 KiB block: slot
-// 4 r + (c ^ (r / 4)) holds 16-byte chunk c (inputs s*32 + 8c .. +7) of row mf*16 + r. The staging
+// 4 r + (c ^ chunk_swizzle(r)) holds 16-byte chunk c (inputs s*32 + 8c .. +7) of row mf*16 + r. The staging
 // thread t of each 64 loads the chunk of slot t (four consecutive threads on one row, which L2
 // serves faster than one thread per row) and writes slot t (sequential); the operand read of lane l
 // (row l % 16, chunk l / 16) then falls in distinct banks.
@@ -58,7 +58,7 @@ __global__ __launch_bounds__(WAVE *WAVES) void skinny_kernel(const SkinnyArgs g)
         const int slot = threadIdx.x + u * WAVE * WAVES;        // block (slot / 64), lane slot % 64
         const int blk = slot / WAVE, sl = slot % WAVE;
         const int st = min(blk / 4, nsteps - 1), m = (blk % 4) * 16 + (sl >> 2);
-        av[u] = load16(g.A + (int64_t)min(m, g.M - 1) * g.lda + kc0 + st * BF16_STEP + 8 * ((sl & 3) ^ ((sl >> 4) & 3)));
+        av[u] = load16(g.A + (int64_t)min(m, g.M - 1) * g.lda + kc0 + st * BF16_STEP + 8 * ((sl & 3) ^ chunk_swizzle(sl >> 2)));
     }
 #pragma unroll
     for (int u = 0; u < A_PER_THREAD; u++) {
@@ -83,7 +83,7 @@ __global__ __launch_bounds__(WAVE *WAVES) void skinny_kernel(const SkinnyArgs g)
             u32x4_t a[4];
 #pragma unroll
             for (int mf = 0; mf < 4; mf++)
-                a[mf] = lds_a[(s * 4 + mf) * WAVE + (lane & 15) * 4 + ((lane >> 4) ^ ((lane >> 2) & 3))];
+                a[mf] = lds_a[(s * 4 + mf) * WAVE + (lane & 15) * 4 + ((lane >> 4) ^ chunk_swizzle(lane & 15))];
 #pragma unroll
             for (int mf = 0; mf < 4; mf++)
                 if (mf < mt)
@@ -145,7 +145,7 @@ __global__ __launch_bounds__(WAVE *WAVES) void skinny_persist_kernel(const Skinn
             const int slot = threadIdx.x + u * WAVE * WAVES;
             const int blk = slot / WAVE, sl = slot % WAVE;
             const int st = min(blk / 4, nsteps - 1), m = (blk % 4) * 16 + (sl >> 2);
-            av[u] = load16(g.A + (int64_t)min(m, g.M - 1) * g.lda + kc0 + st * BF16_STEP + 8 * ((sl & 3) ^ ((sl >> 4) & 3)));
+            av[u] = load16(g.A + (int64_t)min(m, g.M - 1) * g.lda + kc0 + st * BF16_STEP + 8 * ((sl & 3) ^ chunk_swizzle(sl >> 2)));
         }
 #pragma unroll
         for (int u = 0; u < A_PER_THREAD; u++) {
@@ -172,7 +172,7 @@ __global__ __launch_bounds__(WAVE *WAVES) void skinny_persist_kernel(const Skinn
                 u32x4_t a[4];
 #pragma unroll
                 for (int mf = 0; mf < 4; mf++)
-                    a[mf] = lds_a[(step * 4 + mf) * WAVE + (lane & 15) * 4 + ((lane >> 4) ^ ((lane >> 2) & 3))];
+                    a[mf] = lds_a[(step * 4 + mf) * WAVE + (lane & 15) * 4 + ((lane >> 4) ^ chunk_swizzle(lane & 15))];
 #pragma unroll
                 for (int mf = 0; mf < 4; mf++)
                     if (mf < MT)

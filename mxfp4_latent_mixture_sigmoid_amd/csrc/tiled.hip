@@ -72,7 +72,7 @@ __device__ __attribute__((always_inline)) inline void tiled_tile(const GemmArgs 
     const uint8_t *Bg = g.B + (int64_t)group * g.b_stride;
 
     // ---- A staging. A stage holds TL_SUB x NMF 1 KiB blocks (sub-step s, fragment f at block
-    // s * TL_MFW + f; slot 4 r + (c ^ (r / 4)) holds row f*16 + r, inputs s*32 + 8c .. +7, so that the
+    // s * TL_MFW + f; slot 4 r + (c ^ chunk_swizzle(r)) holds row f*16 + r, inputs s*32 + 8c .. +7, so the
     // loads of slots 4r .. 4r+3 -- four consecutive lanes -- share a row). Thread t fills lane slot
     // t % 64 of blocks b = wv + 4u (u < NMF), b -> (s, f) = (b / NMF, b % NMF): its fragment row
     // f = (wv + 4u) % NMF repeats with period FR = NMF / gcd(NMF, 4) in u (NMF = 2..6, 8: 1, 3, 1,
@@ -84,7 +84,7 @@ __device__ __attribute__((always_inline)) inline void tiled_tile(const GemmArgs 
         const int f = (wv + 4 * i) % NMF;
         const int r = min(m0 + f * 16 + (lane >> 2), m1 - 1);   // clamped valid row
         const int64_t row = g.a_index ? (int64_t)(g.a_index[r] / g.a_div) : (int64_t)r;
-        arow[i] = g.A + row * g.lda + 8 * ((lane & 3) ^ ((lane >> 4) & 3));
+        arow[i] = g.A + row * g.lda + 8 * ((lane & 3) ^ chunk_swizzle(lane >> 2));
     }
     const int nstages = (g.K + TL_STAGE_K - 1) / TL_STAGE_K;
     auto load_a = [&](int stage, u32x4_t *v) {
@@ -230,7 +230,7 @@ __device__ __attribute__((always_inline)) inline void tiled_tile(const GemmArgs 
                         u32x4_t a[NMF];
 #pragma unroll
                         for (int f = 0; f < NMF; f++)
-                            a[f] = lds[cur][(s * TL_MFW + f) * WAVE + (lane & 15) * 4 + ((lane >> 4) ^ ((lane >> 2) & 3))];
+                            a[f] = lds[cur][(s * TL_MFW + f) * WAVE + (lane & 15) * 4 + ((lane >> 4) ^ chunk_swizzle(lane & 15))];
 #pragma unroll
                         for (int nf = 0; nf < TL_NF; nf++)
 #pragma unroll
@@ -434,16 +434,17 @@ __global__ __launch_bounds__(WAVE *RG_WAVES) void ring_kernel(const GemmArgs g, 
     // This wave's loads: blocks wv*LOADS .. wv*LOADS+LOADS-1 of a stage. Within a stage they are one
     // base plus a fixed stride: 16 rows of A, or one row-block stride of B's current 16-step chunk.
     // An A block (16 rows x 64 bytes) is loaded with four consecutive lanes on one row -- lane l
-    // takes row l / 4 and 16-byte chunk (l % 4) ^ (l / 16), so slot 4 r + (c ^ (r / 4)) holds chunk c
-    // of row r -- which L2 serves at ~1.6x the rate of the operand order (lane l on row l % 16); the
-    // fragment reads (lane l: row l % 16, chunk l / 16) then fall in distinct banks.
+    // takes row r = l / 4 and 16-byte chunk (l % 4) ^ chunk_swizzle(r), so slot 4 r + (c ^
+    // chunk_swizzle(r)) holds chunk c of row r -- which L2 serves at ~1.6x the rate of the operand
+    // order (lane l on row l % 16); the fragment reads (lane l: row l % 16, chunk l / 16) then fall in
+    // distinct banks.
     // When the B blocks do not fill the last wave, its spare loads repeat the last block (the same
     // bytes into the same slot), so that every wave issues the same number of loads.
     const bool loads_a = wv < AW;
     const int li = loads_a ? wv : wv - AW;
     const int bfirst = li * LOADS;                       // first B block of a B wave
     const uint8_t *a_base = reinterpret_cast<const uint8_t *>(
-        g.A + (int64_t)(m0 + li * (LOADS * 16) + (lane >> 2)) * g.lda + 8 * ((lane & 3) ^ ((lane >> 4) & 3)));
+        g.A + (int64_t)(m0 + li * (LOADS * 16) + (lane >> 2)) * g.lda + 8 * ((lane & 3) ^ chunk_swizzle(lane >> 2)));
     const int bnb0 = n0 / 16 + bfirst;
     auto issue = [&](int s) {                // stage min(s, nst - 1) into buffer s % RG_NBUF
         const int ss = min(s, nst - 1), buf = s % RG_NBUF;
@@ -481,7 +482,7 @@ __global__ __launch_bounds__(WAVE *RG_WAVES) void ring_kernel(const GemmArgs g, 
         const int rr = lane & 15, cc = lane >> 4;
 #pragma unroll
         for (int f = 0; f < WMF; f++)
-            af[f] = lds[buf][wm * WMF + f][rr * 4 + (cc ^ ((rr >> 2) & 3))];
+            af[f] = lds[buf][wm * WMF + f][rr * 4 + (cc ^ chunk_swizzle(rr))];
     };
     // Wait until only the later stages' loads of this wave are outstanding, then a barrier makes every
     // wave's loads of this stage visible (and all waves are past the previous stage).

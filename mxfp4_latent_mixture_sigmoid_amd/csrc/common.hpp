@@ -80,11 +80,13 @@ __device__ inline int bf16_ilogb(uint32_t mag)
     return eb ? (int)eb - 127 : (31 - __builtin_clz(m)) - 133;
 }
 
-// E8M0 byte -> the float 2^(e-127) used as the conversion scale (255 -> NaN).
+// E8M0 byte -> the FP32 scale 2^(e-127) of the scaled FP4 -> BF16 conversion below, in one
+// instruction: 2^-127 (an FP32 denormal; kernels keep FP32 denormals) shifted by e, exact for
+// e = 0..254. e = 255 gives +inf, which that conversion turns into NaN for every code (checked on
+// gfx950 for all 16 codes, the same bits as a NaN scale): the E8M0 NaN.
 __device__ inline float e8m0_to_f32(uint32_t e)
 {
-    uint32_t bits = (e == 0u) ? 0x00400000u : (e == 255u ? 0x7FC00000u : (e << 23));
-    return __uint_as_float(bits);
+    return __builtin_amdgcn_ldexpf(__uint_as_float(0x00400000u), (int)e);
 }
 
 // Eight E2M1 codes (one dword, element 2i in the low nibble of byte i) times one E8M0 scale,

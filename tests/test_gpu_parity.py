@@ -80,6 +80,26 @@ def test_unpack_scale_range_bit_exact():
         assert np.array_equal(got, ref)
 
 
+def test_unpack_special_scales():
+    """E8M0 bytes 0 and 1 (products down to BF16 subnormals, 2^-128), 2 and 255 (NaN for every code of
+    the block): exact bits where the oracle's value is a number, NaN where it is NaN."""
+    shape = replace(SHAPES["tiny"], E=2, name="scales")
+    inp = make_inputs(shape)
+    rng = np.random.default_rng(2)
+    for m in ("gate", "up", "down"):
+        inp[m + "_scales"] = rng.choice(np.array([0, 1, 2, 255], np.uint8), inp[m + "_scales"].shape)
+    layer = G.make_layer(shape, inp, T_max=1)
+    for which, (c, s) in enumerate((("gate_codes", "gate_scales"), ("up_codes", "up_scales"),
+                                    ("down_codes", "down_scales"))):
+        got = G.host_bf16(layer.unpack_expert(1, which))
+        refv = O.dequant(inp[c][1], inp[s][1])
+        nan = np.isnan(refv)
+        assert nan.any() and (~nan).any()
+        gotv = G.bf16_f64(got)
+        assert np.all(np.isnan(gotv[nan])), which
+        assert np.array_equal(got[~nan], O.f64_to_bf16(refv)[~nan]), which
+
+
 @pytest.mark.parametrize("name", list(SMALL_SHAPES))
 def test_forward_parity(name):
     shape, inp, layer = _setup(name)

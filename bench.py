@@ -155,7 +155,7 @@ def log(msg: str) -> None:
 class Leg:
     """One workload on the GPU: packed layer, resident inputs, routing and output buffers."""
 
-    def __init__(self, shape, fp8: bool, a4: bool):
+    def __init__(self, shape, fp8: bool, a4: bool, shared_stream: bool = False):
         import numpy as np
         import torch
         from mxfp4_latent_mixture_sigmoid_amd import MoELayer, abi
@@ -171,7 +171,7 @@ class Leg:
         self.inp = make_inputs(shape)
         weights = {k: dev(v) for k, v in self.inp.items() if k in abi.WEIGHT_FIELDS and v is not None}
         self.layer = MoELayer(shape.H, shape.Lt, shape.E, shape.K, shape.I, shape.S, shape.Is, shape.has_latent,
-                              weights, T_max=shape.T, stage2_fp8=fp8, stage1_a4=a4)
+                              weights, T_max=shape.T, stage2_fp8=fp8, stage1_a4=a4, shared_stream=shared_stream)
         torch.cuda.synchronize()
         del weights
         self.x = dev(self.inp["x"])
@@ -314,6 +314,9 @@ def main() -> int:
     ap.add_argument("--stage1", choices=("bf16", "mxfp4"), default="bf16",
                     help="arithmetic of the experts' gate/up product: BF16 z (the layer as defined), or z "
                          "quantised to MX FP4 on the scaled FP4 x FP4 matrix-core instruction (A4W4)")
+    ap.add_argument("--shared-stream", action="store_true",
+                    help="run the shared experts' gate/up product on a second stream, concurrently with the "
+                         "routing and the routed experts, instead of inside the x-side product")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -336,10 +339,10 @@ def main() -> int:
     fp8, a4 = args.stage2 == "fp8", args.stage1 == "mxfp4"
     shape = SHAPES[args.workload]
     T = shape.T
-    main_leg = Leg(shape, fp8, a4)
+    main_leg = Leg(shape, fp8, a4, args.shared_stream)
     pre_leg = None
     if not args.no_prefill and args.prefill_workload != args.workload:
-        pre_leg = Leg(SHAPES[args.prefill_workload], fp8, a4)
+        pre_leg = Leg(SHAPES[args.prefill_workload], fp8, a4, args.shared_stream)
 
     prefill = None
     if pre_leg is not None:
@@ -446,7 +449,8 @@ def main() -> int:
         "config": {"workload": shape.name, "tokens": T, "hidden": shape.H, "latent": shape.Lt,
                    "experts": shape.E, "top_k": shape.K, "inter": shape.I, "shared_experts": shape.S,
                    "shared_inter": shape.Is, "routing": shape.routing, "active_experts": n_active,
-                   "stage1": args.stage1, "stage2": args.stage2},
+                   "stage1": args.stage1, "stage2": args.stage2,
+                   "shared": "stream" if args.shared_stream else "fused"},
         "roofline": roof,
         "cpu_baseline": cpu,
         "gpu_ms_per_step": round(gpu_ms, 5),

@@ -79,6 +79,22 @@ typedef enum { MOE_STAGE2_BF16 = 0, MOE_STAGE2_FP8 = 1 } moe_stage2;
  *   also holds the gate|up weights in the layout of gfx950's scaled MX matrix-core instruction. */
 typedef enum { MOE_STAGE1_BF16 = 0, MOE_STAGE1_MXFP4 = 1 } moe_stage1;
 
+/* Where the shared experts' gate/up product (h_s = bf16(silu(x Wg_s^T) (x Wu_s^T))) runs. The
+ * reference engine runs the shared experts on a second stream, concurrently with the routed
+ * experts (page "Kimi K3.1 Pro on AMD Instinct GPUs", section "Serving with ATOM", "What we
+ * optimized", paragraph on the MXFP4 latent MoE).
+ * MOE_SHARED_FUSED:  its columns are part of the x-side product over x (one weight stream, one launch).
+ * MOE_SHARED_STREAM: it is a product of its own on a second stream that the handle owns (created by
+ *   moe_create at the default priority, destroyed by moe_destroy). Each call forks that stream off
+ *   the caller's stream at its start (an event recorded on the caller's stream) and joins it back
+ *   before the output product (the caller's stream waits on an event recorded on the second
+ *   stream), so every call stays ordered on the caller's stream and can be captured into a HIP
+ *   graph. The outputs are bit-identical to MOE_SHARED_FUSED. The packed buffer holds the shared
+ *   gate/up rows apart from the x-side rows. Without shared experts the field has no effect. Calls
+ *   on one handle with this mode must come from one host thread at a time: they share the second
+ *   stream and its two events. */
+typedef enum { MOE_SHARED_FUSED = 0, MOE_SHARED_STREAM = 1 } moe_shared_stream;
+
 typedef struct {
     int32_t hidden;          /* H: width of x and out (multiple of 128); unused without latent  */
     int32_t latent;          /* Lt: latent width (multiple of 128)                               */
@@ -91,6 +107,7 @@ typedef struct {
     int32_t act;             /* moe_act                                                          */
     int32_t stage2;          /* moe_stage2                                                       */
     int32_t stage1;          /* moe_stage1                                                       */
+    int32_t shared_stream;   /* moe_shared_stream                                                */
 } moe_config;
 
 /* Canonical weights (device, caller-owned; only read by moe_create's packing kernels, so they
@@ -237,7 +254,8 @@ typedef enum {
     MOE_KERNEL_OUT_EPI = 10, /* few-token output partial sums                       */
     MOE_KERNEL_ROUTER_XSIDE = 11,/* router + x-side product as one (moe_route_forward) */
     MOE_KERNEL_H_QUANT = 12, /* MX FP8 quantisation of h (MOE_STAGE2_FP8)           */
-    MOE_KERNEL_Z_QUANT = 13  /* MX FP4 quantisation of z (MOE_STAGE1_MXFP4)         */
+    MOE_KERNEL_Z_QUANT = 13, /* MX FP4 quantisation of z (MOE_STAGE1_MXFP4)         */
+    MOE_KERNEL_SHARED = 14   /* shared gate/up product and its GLU (MOE_SHARED_STREAM, second stream) */
 } moe_kernel;
 
 /* Profiling hook (benchmarks, tests): after moe_profile_begin, every kernel launch of moe_route

@@ -31,13 +31,15 @@ STAGE2_BF16 = 0
 STAGE2_FP8 = 1
 STAGE1_BF16 = 0
 STAGE1_MXFP4 = 1
+SHARED_FUSED = 0
+SHARED_STREAM = 1
 
 
 class MoeConfig(ctypes.Structure):
     _fields_ = [("hidden", c_i32), ("latent", c_i32), ("n_experts", c_i32), ("top_k", c_i32),
                 ("inter", c_i32), ("n_shared", c_i32), ("shared_inter", c_i32),
                 ("has_latent_proj", c_i32), ("act", c_i32), ("stage2", c_i32),
-                ("stage1", c_i32)]
+                ("stage1", c_i32), ("shared_stream", c_i32)]
 
 
 WEIGHT_FIELDS = ("w_router", "w_down", "w_up", "gate_codes", "gate_scales", "up_codes", "up_scales",
@@ -120,10 +122,10 @@ def stream_handle(stream=None):
 
 
 def make_config(hidden, latent, n_experts, top_k, inter, n_shared, shared_inter, has_latent_proj,
-                stage2_fp8: bool = False, stage1_a4: bool = False) -> MoeConfig:
+                stage2_fp8: bool = False, stage1_a4: bool = False, shared_stream: bool = False) -> MoeConfig:
     return MoeConfig(hidden, latent, n_experts, top_k, inter, n_shared, shared_inter,
                      int(bool(has_latent_proj)), ACT_SILU_GLU, STAGE2_FP8 if stage2_fp8 else STAGE2_BF16,
-                     STAGE1_MXFP4 if stage1_a4 else STAGE1_BF16)
+                     STAGE1_MXFP4 if stage1_a4 else STAGE1_BF16, SHARED_STREAM if shared_stream else SHARED_FUSED)
 
 
 def query(cfg: MoeConfig, T_max: int):
@@ -204,7 +206,7 @@ def unpack_expert(h, e: int, which: int, out, stream=None) -> None:
 
 
 KERNELS = ("router", "topk", "permute", "xside", "tilemap", "gateup", "down", "combine", "out", "xside_epi",
-           "out_epi", "router_xside", "h_quant", "z_quant")
+           "out_epi", "router_xside", "h_quant", "z_quant", "shared")
 
 
 def profile_begin(h, max_launches: int) -> None:

@@ -25,6 +25,9 @@ struct moe_handle {
     uint8_t *packed;
     int64_t off_router, off_xside, off_rx, off_outside, off_gateup, off_down, off_down8, off_gateup4;
     int64_t gateup_stride, down_stride;   // packed bytes per expert
+    int64_t off_shared = 0;               // shared gate|up rows on their own (MOE_SHARED_STREAM)
+    hipStream_t side = nullptr;           // MOE_SHARED_STREAM: the second stream and its fork/join events
+    hipEvent_t fork = nullptr, join = nullptr;
     // profiling hook state
     bool prof = false;
     int prof_max = 0;
@@ -39,6 +42,13 @@ constexpr int64_t ALIGN = 256;
 // tiles once they average TILED_MIN_ROWS rows or more (prefill).
 constexpr int BM_STREAM = 16;
 constexpr int TILED_MIN_ROWS = 32;
+// MOE_SHARED_STREAM with shared experts: their gate|up product runs apart, on the second stream.
+bool shared_apart(const moe_config *c)
+{
+    return c->shared_stream == MOE_SHARED_STREAM && c->has_latent_proj && c->n_shared > 0;
+}
+// Shared experts whose gate|up columns are part of the x-side product.
+int64_t fused_shared(const moe_config *c) { return shared_apart(c) ? 0 : c->n_shared; }
 bool tiled_experts(const moe_config *c, int64_t T) { return T * c->top_k >= (int64_t)TILED_MIN_ROWS * c->n_experts; }
 int expert_bm(const moe_config *c, int64_t T) { return tiled_experts(c, T) ? TILED_BM : BM_STREAM; }
 constexpr int SKINNY_STEPS = 16;   // 32-wide K steps per split of the few-token router product
@@ -66,6 +76,8 @@ bool valid_config(const moe_config *c)
         return false;
     if (c->stage1 != MOE_STAGE1_BF16 && c->stage1 != MOE_STAGE1_MXFP4)
         return false;
+    if (c->shared_stream != MOE_SHARED_FUSED && c->shared_stream != MOE_SHARED_STREAM)
+        return false;
     // the FP8 down product keeps a whole 128-row tile of h (inter bytes per row) in LDS
     if (c->stage2 == MOE_STAGE2_FP8 && (c->inter > FP8_DOWN_MAX_K || c->latent % 64))
         return false;
@@ -89,7 +101,7 @@ bool valid_config(const moe_config *c)
 }
 
 struct PackedLayout {
-    int64_t router, xside, rx, outside, gateup, down, down8, gateup4, total, gateup_stride, down_stride;
+    int64_t router, xside, rx, outside, shared, gateup, down, down8, gateup4, total, gateup_stride, down_stride;
 };
 
 PackedLayout packed_layout(const moe_config *c)
@@ -98,19 +110,24 @@ PackedLayout packed_layout(const moe_config *c)
     const int64_t Hin = c->has_latent_proj ? c->hidden : c->latent;
     const int64_t E_pad = (c->n_experts + 15) / 16 * 16;
     const int64_t Lt = c->latent, H = c->hidden, S = c->n_shared, Is = c->shared_inter, I = c->inter;
+    const int64_t Sf = fused_shared(c);
     int64_t off = 0;
     L.router = off;
     off = align_up(off + bf16_packed_bytes(E_pad, Hin));
     L.xside = off;
     if (c->has_latent_proj)
-        off = align_up(off + bf16_packed_bytes(Lt + 2 * S * Is, H));
+        off = align_up(off + bf16_packed_bytes(Lt + 2 * Sf * Is, H));
     // the router and x-side rows once more as one matrix, for moe_route_forward's single product
     L.rx = off;
     if (c->has_latent_proj)
-        off = align_up(off + bf16_packed_bytes(router_rows_rx(c) + Lt + 2 * S * Is, H));
+        off = align_up(off + bf16_packed_bytes(router_rows_rx(c) + Lt + 2 * Sf * Is, H));
     L.outside = off;
     if (c->has_latent_proj)
         off = align_up(off + bf16_packed_bytes(H, Lt + S * Is));
+    // MOE_SHARED_STREAM: the shared gate|up rows (16 gate / 16 up alternating) as a matrix of their own
+    L.shared = off;
+    if (shared_apart(c))
+        off = align_up(off + bf16_packed_bytes(2 * S * Is, H));
     L.gateup_stride = mx_packed_bytes(2 * I, Lt);
     L.down_stride = mx_packed_bytes(Lt, I);
     L.gateup = off;
@@ -396,6 +413,7 @@ moe_status moe_create(const moe_config *cfg, const moe_weights *w, void *packed,
     h->off_rx = L.rx;
     h->E_rx = (int)router_rows_rx(cfg);
     h->off_outside = L.outside;
+    h->off_shared = L.shared;
     h->off_gateup = L.gateup;
     h->off_down = L.down;
     h->off_down8 = L.down8;
@@ -406,16 +424,27 @@ moe_status moe_create(const moe_config *cfg, const moe_weights *w, void *packed,
     hipStream_t st = static_cast<hipStream_t>(stream);
     const int64_t E = cfg->n_experts, Lt = cfg->latent, H = cfg->hidden, I = cfg->inter;
     const int64_t S = sh ? cfg->n_shared : 0, Is = sh ? cfg->shared_inter : 0;
+    const int64_t Sf = sh ? fused_shared(cfg) : 0;   // shared experts packed with the x-side rows
     hipError_t e = launch_pack_router(h->packed + L.router, static_cast<const uint16_t *>(w->w_router), E, h->E_pad,
                                       h->Hin, st);
     if (e == hipSuccess && lat)
         e = launch_pack_xside(h->packed + L.xside, static_cast<const uint16_t *>(w->w_down),
                               static_cast<const uint16_t *>(w->sh_gate), static_cast<const uint16_t *>(w->sh_up), Lt,
-                              H, S, Is, st);
+                              H, Sf, Is, st);
     if (e == hipSuccess && lat)
         e = launch_pack_router_xside(h->packed + L.rx, static_cast<const uint16_t *>(w->w_router), E, h->E_rx,
                                      static_cast<const uint16_t *>(w->w_down), static_cast<const uint16_t *>(w->sh_gate),
-                                     static_cast<const uint16_t *>(w->sh_up), Lt, H, S, Is, st);
+                                     static_cast<const uint16_t *>(w->sh_up), Lt, H, Sf, Is, st);
+    if (e == hipSuccess && shared_apart(cfg))
+        e = launch_pack_xside(h->packed + L.shared, nullptr, static_cast<const uint16_t *>(w->sh_gate),
+                              static_cast<const uint16_t *>(w->sh_up), 0, H, S, Is, st);
+    if (e == hipSuccess && shared_apart(cfg)) {
+        e = hipStreamCreateWithFlags(&h->side, hipStreamNonBlocking);
+        if (e == hipSuccess)
+            e = hipEventCreateWithFlags(&h->fork, hipEventDisableTiming);
+        if (e == hipSuccess)
+            e = hipEventCreateWithFlags(&h->join, hipEventDisableTiming);
+    }
     if (e == hipSuccess && lat)
         e = launch_pack_outside(h->packed + L.outside, static_cast<const uint16_t *>(w->w_up),
                                 static_cast<const uint16_t *>(w->sh_down), Lt, H, S, Is, st);
@@ -499,6 +528,12 @@ void moe_destroy(moe_handle *h)
     if (!h)
         return;
     prof_clear(h);
+    if (h->join)
+        (void)hipEventDestroy(h->join);
+    if (h->fork)
+        (void)hipEventDestroy(h->fork);
+    if (h->side)
+        (void)hipStreamDestroy(h->side);
     delete h;
 }
 
@@ -596,6 +631,41 @@ moe_status select_impl(moe_handle *h, int32_t T, const TopkArgs &ta, const moe_r
     return MOE_OK;
 }
 
+// MOE_SHARED_STREAM: h_s = bf16(silu(x Wg_s^T) (x Wu_s^T)) into columns Lt.. of [zc | h_s], on the
+// handle's second stream, forked off `caller` here; experts_impl joins it back before the output
+// product. Few tokens: split-K partials at P (the x-side product's split count and layout), summed
+// and gated by the x-side epilogue; many tokens: one product whose epilogue applies the GLU. Each
+// element is computed as by the x-side product that holds the shared columns otherwise.
+moe_status shared_impl(moe_handle *h, const void *x, int32_t T, uint16_t *Acat, int ldcat, float *P,
+                       hipStream_t caller)
+{
+    const moe_config *c = &h->cfg;
+    const int H = c->hidden, Lt = c->latent, Ns = 2 * c->n_shared * c->shared_inter;
+    if (hipEventRecord(h->fork, caller) != hipSuccess || hipStreamWaitEvent(h->side, h->fork, 0) != hipSuccess)
+        return MOE_ERR_HIP;
+    hipStream_t st = h->side;
+    if (T <= SKINNY_MAX_M) {
+        const int64_t pstride = (int64_t)(Ns / 16) * SKINNY_TILE_FLOATS;
+        SkinnyArgs g{static_cast<const uint16_t *>(x), H, T, h->packed + h->off_shared, Ns, H, P, pstride};
+        MOE_LAUNCH(MOE_KERNEL_SHARED, launch_skinny_persist(g, 8, XSIDE_GROUPS, SKINNY_XSTEPS, st));
+        XsideEpiArgs ea{P, pstride, skinny_splits(H, SKINNY_XSTEPS), T, Ns, 0, Ns, nullptr, Acat + Lt, ldcat,
+                        nullptr, c->n_experts, 0, nullptr};
+        MOE_LAUNCH(MOE_KERNEL_SHARED, launch_xside_epilogue(ea, st));
+    } else {
+        GemmArgs g{};
+        g.A = static_cast<const uint16_t *>(x);
+        g.lda = H;
+        g.B = h->packed + h->off_shared;
+        g.M = T;
+        g.N = Ns;
+        g.K = H;
+        g.split = INT_MAX;
+        g.lo = OutDesc{OUT_GLU, Acat + Lt, ldcat, 0, INT_MAX, nullptr};
+        MOE_LAUNCH(MOE_KERNEL_SHARED, (ring_preferred(g) ? launch_ring(g, st) : launch_tiled(g, false, 0, st)));
+    }
+    return hipEventRecord(h->join, st) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
 // The x-side products, which need only x: z = bf16(x W_down^T) and h_s = bf16(silu(x Wg_s^T) (x Wu_s^T)).
 // With `tiles` set (moe_forward alone) the expert tile lists are built here as well: by the few-token
 // epilogue, or by a tile-list launch.
@@ -606,17 +676,25 @@ moe_status xside_impl(moe_handle *h, const void *x, int32_t T, const moe_routing
     const bool lat = c->has_latent_proj != 0;
     const int E = c->n_experts, Lt = c->latent, H = c->hidden;
     const int S = lat ? c->n_shared : 0, Is = S ? c->shared_inter : 0;
-    const int ldcat = Lt + S * Is, Nx = Lt + 2 * S * Is;
+    const int ldcat = Lt + S * Is, Nx = Lt + 2 * (lat ? (int)fused_shared(c) : 0) * Is;   // x-side columns
     const int bm = expert_bm(c, T);
     uint16_t *Z = reinterpret_cast<uint16_t *>(ws + W.z);
     uint16_t *Acat = reinterpret_cast<uint16_t *>(ws + W.acat);
     int32_t *tl = reinterpret_cast<int32_t *>(ws + W.tiles);
+    // MOE_SHARED_STREAM: forked once the x-side product is on the stream, so that it runs beside
+    // the routed experts rather than beside that product; its partials follow the product's
+    float *ps = lat && T <= SKINNY_MAX_M ? reinterpret_cast<float *>(ws + W.partials) +
+                                               (int64_t)skinny_splits(H, SKINNY_XSTEPS) * (Nx / 16) * SKINNY_TILE_FLOATS
+                                         : nullptr;
+    moe_status e;
     if (lat && T <= SKINNY_MAX_M) {   // z and h_s from split-K partials, summed by the epilogue
         float *partials = reinterpret_cast<float *>(ws + W.partials);
         const int64_t pstride = (int64_t)(Nx / 16) * SKINNY_TILE_FLOATS;
         SkinnyArgs g{static_cast<const uint16_t *>(x), H, T, h->packed + h->off_xside, Nx, H, partials, pstride};
         MOE_LAUNCH(MOE_KERNEL_XSIDE, launch_skinny_persist(g, 8, XSIDE_GROUPS, SKINNY_XSTEPS, st));
-        XsideEpiArgs ea{partials, pstride, skinny_splits(H, SKINNY_XSTEPS), T, Nx, Lt, 2 * S * Is, Z, Acat, ldcat,
+        if (shared_apart(c) && (e = shared_impl(h, x, T, Acat, ldcat, ps, st)) != MOE_OK)
+            return e;
+        XsideEpiArgs ea{partials, pstride, skinny_splits(H, SKINNY_XSTEPS), T, Nx, Lt, Nx - Lt, Z, Acat, ldcat,
                         r->offsets, E, bm, tiles ? tl : nullptr};
         MOE_LAUNCH(MOE_KERNEL_XSIDE_EPI, launch_xside_epilogue(ea, st));
         return MOE_OK;
@@ -633,6 +711,8 @@ moe_status xside_impl(moe_handle *h, const void *x, int32_t T, const moe_routing
         g.lo = OutDesc{OUT_BF16, Z, Lt, 0, Lt, nullptr};
         g.hi = OutDesc{OUT_GLU, Acat + Lt, ldcat, Lt, INT_MAX, nullptr};
         MOE_LAUNCH(MOE_KERNEL_XSIDE, (ring_preferred(g) ? launch_ring(g, st) : launch_tiled(g, false, 0, st)));
+        if (shared_apart(c) && (e = shared_impl(h, x, T, Acat, ldcat, ps, st)) != MOE_OK)
+            return e;
     }
     if (tiles)
         MOE_LAUNCH(MOE_KERNEL_TILEMAP, launch_tilemap(r->offsets, E, bm, tl, st));
@@ -653,10 +733,16 @@ moe_status front_impl(moe_handle *h, const void *x, int32_t T, const float *logi
     const moe_config *c = &h->cfg;
     const int E = c->n_experts, K = c->top_k, Lt = c->latent, H = c->hidden;
     const int S = c->n_shared, Is = S ? c->shared_inter : 0;
-    const int ldcat = Lt + S * Is, Nx = Lt + 2 * S * Is, Erx = h->E_rx, Nrx = Erx + Nx;
+    const int ldcat = Lt + S * Is, Nx = Lt + 2 * (int)fused_shared(c) * Is, Erx = h->E_rx, Nrx = Erx + Nx;
     const int bm = expert_bm(c, T);
     uint16_t *Z = reinterpret_cast<uint16_t *>(ws + W.z);
     uint16_t *Acat = reinterpret_cast<uint16_t *>(ws + W.acat);
+    // MOE_SHARED_STREAM: forked once the combined product is on the stream (beside the top-K and the
+    // routed experts); its partials follow the combined product's
+    float *ps = T <= SKINNY_MAX_M ? reinterpret_cast<float *>(ws + W.rpartials) +
+                                        (int64_t)skinny_splits(H, SKINNY_XSTEPS) * (Nrx / 16) * SKINNY_TILE_FLOATS
+                                  : nullptr;
+    moe_status e;
     TopkArgs ta{};
     ta.T = T;
     ta.E = E;
@@ -674,6 +760,8 @@ moe_status front_impl(moe_handle *h, const void *x, int32_t T, const float *logi
         SkinnyArgs g{static_cast<const uint16_t *>(x), H, T, h->packed + h->off_rx, Nrx, H, P, pstride,
                      reinterpret_cast<uint32_t *>(ws + W.sync)};
         MOE_LAUNCH(MOE_KERNEL_ROUTER_XSIDE, launch_skinny_persist(g, 8, RX_GROUPS, SKINNY_XSTEPS, st));
+        if (shared_apart(c) && (e = shared_impl(h, x, T, Acat, ldcat, ps, st)) != MOE_OK)
+            return e;
         ta.src = P;
         ta.partials = 1;
         ta.split_stride = pstride;
@@ -682,7 +770,7 @@ moe_status front_impl(moe_handle *h, const void *x, int32_t T, const float *logi
         ta.logits_out = logits_out;
         // top-K (with the grouping and the tile lists) and the x-side epilogue in one launch
         set_grouping(ta, r, W, ws, reinterpret_cast<int32_t *>(ws + W.tiles), bm);
-        XsideEpiArgs ea{P + (int64_t)(Erx / 16) * SKINNY_TILE_FLOATS, pstride, splits, T, Nx, Lt, 2 * S * Is, Z,
+        XsideEpiArgs ea{P + (int64_t)(Erx / 16) * SKINNY_TILE_FLOATS, pstride, splits, T, Nx, Lt, Nx - Lt, Z,
                         Acat, ldcat, nullptr, E, bm, nullptr};
         MOE_LAUNCH(MOE_KERNEL_TOPK, launch_topk_xside(ta, ea, st));
         return MOE_OK;
@@ -701,6 +789,8 @@ moe_status front_impl(moe_handle *h, const void *x, int32_t T, const float *logi
     g.hi = OutDesc{OUT_BF16, Z, Lt, Erx, Erx + Lt, nullptr};
     g.top = OutDesc{OUT_GLU, Acat + Lt, ldcat, Erx + Lt, INT_MAX, nullptr};
     MOE_LAUNCH(MOE_KERNEL_ROUTER_XSIDE, (ring_preferred(g) ? launch_ring(g, st) : launch_tiled(g, false, 0, st)));
+    if (shared_apart(c) && (e = shared_impl(h, x, T, Acat, ldcat, ps, st)) != MOE_OK)
+        return e;
     ta.src = lg;
     ta.splits = 1;
     return select_impl(h, T, ta, r, W, ws, st, true);
@@ -770,6 +860,8 @@ moe_status experts_impl(moe_handle *h, const void *x, int32_t T, const moe_routi
     // zc = bf16(sum_j w_j y_j) in slot order: into the first Lt columns of [zc | h_s], or the output
     MOE_LAUNCH(MOE_KERNEL_COMBINE, launch_combine(Yb, Lt, r->inv, r->topk_w, T, K, lat ? Acat : static_cast<uint16_t *>(out),
                            lat ? ldcat : Lt, st));
+    if (shared_apart(c) && hipStreamWaitEvent(st, h->join, 0) != hipSuccess)   // h_s from the second stream
+        return MOE_ERR_HIP;
     if (lat && T <= SKINNY_MAX_M) {   // out = bf16([zc | h_s] [W_up | Wd_s]^T) from split-K partials
         float *partials = reinterpret_cast<float *>(ws + W.partials);
         const int64_t pstride = (int64_t)(H / 16) * SKINNY_TILE_FLOATS;

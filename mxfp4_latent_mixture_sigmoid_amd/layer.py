@@ -16,14 +16,16 @@ class MoELayer:
 
     ``stage2_fp8`` quantises h to MX FP8 for the down product (MOE_STAGE2_FP8); ``stage1_a4``
     quantises z to MX FP4 for the gate/up product (MOE_STAGE1_MXFP4, A4W4). Both default to the
-    BF16 layer; each adds one packed copy of the weights it changes.
+    BF16 layer; each adds one packed copy of the weights it changes. ``shared_stream`` runs the
+    shared experts' gate/up product on a second stream owned by the handle, concurrently with the
+    routing and the routed experts (MOE_SHARED_STREAM); the outputs are the same bits.
     """
 
     def __init__(self, hidden, latent, n_experts, top_k, inter, n_shared, shared_inter,
                  has_latent_proj, weights: dict, T_max: int, device="cuda", stream=None,
-                 stage2_fp8: bool = False, stage1_a4: bool = False):
+                 stage2_fp8: bool = False, stage1_a4: bool = False, shared_stream: bool = False):
         self.cfg = abi.make_config(hidden, latent, n_experts, top_k, inter, n_shared, shared_inter,
-                                   has_latent_proj, stage2_fp8, stage1_a4)
+                                   has_latent_proj, stage2_fp8, stage1_a4, shared_stream)
         self.E, self.K, self.Lt = n_experts, top_k, latent
         self.H = hidden if has_latent_proj else latent
         self.T_max = T_max

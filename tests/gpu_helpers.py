@@ -83,7 +83,8 @@ def assert_close(name: str, got, ref, bf16: bool = True) -> dict:
     return r
 
 
-def make_layer(shape, inp: dict, T_max: int, stage2_fp8: bool = False, stage1_a4: bool = False):
+def make_layer(shape, inp: dict, T_max: int, stage2_fp8: bool = False, stage1_a4: bool = False,
+               shared_stream: bool = False):
     from mxfp4_latent_mixture_sigmoid_amd import MoELayer
     w = {}
     for k in ("w_router", "w_down", "w_up", "gate_codes", "gate_scales", "up_codes", "up_scales",
@@ -91,7 +92,7 @@ def make_layer(shape, inp: dict, T_max: int, stage2_fp8: bool = False, stage1_a4
         if k in inp and inp[k] is not None:
             w[k] = dev(inp[k])
     layer = MoELayer(shape.H, shape.Lt, shape.E, shape.K, shape.I, shape.S, shape.Is, shape.has_latent,
-                     w, T_max=T_max, stage2_fp8=stage2_fp8, stage1_a4=stage1_a4)
+                     w, T_max=T_max, stage2_fp8=stage2_fp8, stage1_a4=stage1_a4, shared_stream=shared_stream)
     torch.cuda.synchronize()
     del w
     return layer

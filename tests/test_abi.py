@@ -121,6 +121,24 @@ def test_fp8_second_stage_rejects_unsupported_shapes(kw):
     assert abi.lib().moe_query(ctypes.byref(c), 64, None, None) == abi.Status.INVALID_ARG
 
 
+def test_shared_stream_sizes():
+    """MOE_SHARED_STREAM packs the shared gate/up rows once, as a matrix of their own, and leaves them
+    out of the x-side and the combined router + x-side matrices; the workspace is unchanged."""
+    T, H, S, Is = 64, 7168, 2, 384
+    pb0, wb0 = abi.query(_cfg(), T)
+    pb1, wb1 = abi.query(_cfg(shared_stream=True), T)
+    assert pb0 - pb1 == 2 * S * Is * H * 2   # one BF16 copy of the rows fewer (every region 256-B aligned here)
+    assert wb1 == wb0
+    none = dict(n_shared=0, shared_inter=0)
+    assert abi.query(_cfg(shared_stream=True, **none), T) == abi.query(_cfg(**none), T)
+
+
+def test_unknown_shared_stream_mode_is_rejected():
+    c = _cfg()
+    c.shared_stream = 2
+    assert abi.lib().moe_query(ctypes.byref(c), 64, None, None) == abi.Status.INVALID_ARG
+
+
 def test_unknown_second_stage_is_rejected():
     c = _cfg()
     c.stage2 = 2

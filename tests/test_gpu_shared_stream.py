@@ -2,8 +2,8 @@
 
 The mode only moves where h_s is computed: every output must equal the fused mode's (whose outputs
 the parity tests hold to the FP64 oracle) bit for bit -- routing arrays, logits and output, through
-moe_route_forward and through moe_route + moe_forward, on the few-token (split-K) and the
-many-token paths -- and a HIP graph captured with the fork and join must replay to the same bits."""
+moe_route_forward, moe_route + moe_forward and moe_route_forward_static, on the few-token
+(split-K) and the many-token paths -- and a HIP graph captured with the fork and join must replay to the same bits."""
 from dataclasses import replace
 
 import pytest
@@ -60,6 +60,13 @@ def _check(shape, T, graph=False):
             ref = _run(fused, shape, inp, x, T, bias, two)
             got = _run(apart, shape, inp, x, T, bias, two)
             _same(f"{shape.name} T={T} {'route+forward' if two else 'route_forward'}", ref, got, T, shape.K)
+        if T <= 64:   # the allocation-free entry point: the second stream's partials in the scratch array
+            ref = _run(fused, shape, inp, x, T, bias, False)
+            r = apart.alloc_routing(T)
+            lg = torch.empty(T, shape.E, dtype=torch.float32, device="cuda")
+            out = apart.route_forward_static(x, T, r, logit_bias=bias, logits_out=lg)
+            torch.cuda.synchronize()
+            _same(f"{shape.name} T={T} route_forward_static", ref, (r, lg, out), T, shape.K)
         if graph:
             ref = _run(fused, shape, inp, x, T, bias, False)
             rg = apart.alloc_routing(T)

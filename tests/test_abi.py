@@ -33,6 +33,18 @@ def test_exports_every_declared_function():
     assert set(names) == set(abi.SIGNATURES), "binding and header disagree"
 
 
+def test_kernel_ids_match_header():
+    """The binding's kernel names (indexed by the profiling hook's kernel ids) follow the header's
+    MOE_KERNEL_* enumeration, and its config struct has the header's fields in order."""
+    src = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "mxmoe.h")).read(), flags=re.S)
+    ids = {int(v): n.lower() for n, v in re.findall(r"\bMOE_KERNEL_([A-Z0-9_]+)\s*=\s*(\d+)", src)}
+    assert sorted(ids) == list(range(len(ids)))
+    assert tuple(ids[i] for i in range(len(ids))) == abi.KERNELS
+    body = re.search(r"typedef struct \{([^}]*)\}\s*moe_config;", src).group(1)
+    fields = re.findall(r"int32_t\s+(\w+);", body)
+    assert fields == [f for f, _ in abi.MoeConfig._fields_]
+
+
 def _cfg(**kw):
     base = dict(hidden=7168, latent=3584, n_experts=896, top_k=16, inter=384, n_shared=2,
                 shared_inter=384, has_latent_proj=1)
